@@ -1,0 +1,392 @@
+"""Pins for the CPU oracle: values and properties fixed by the pages and by
+mathematics, chosen so that a dropped term, a wrong sign, a wrong index or a
+transposed operand in the oracle fails at least one of them.  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import q8_oracle as O
+
+
+def load(golden_dir, name):
+    with open(os.path.join(golden_dir, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def f32_round(fr: Fraction) -> float:
+    """Exact rational -> nearest binary32, ties to even (normal range only).
+    Written from the IEEE 754 definition, independent of numpy."""
+    if fr == 0:
+        return 0.0
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    # fix e so that 2^e <= a < 2^(e+1)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    n = a / ulp
+    lo = math.floor(n)
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * float(lo * ulp)
+
+
+# ----------------------------------------------------------------- input decode
+def test_bf16_decode_matches_torch_widening():
+    x = torch.randn(64, 33, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16)
+    np.testing.assert_array_equal(O.to_f32(x), x.float().numpy())
+
+
+def test_fp16_decode_exact():
+    x = torch.randn(8, 8, generator=torch.Generator().manual_seed(1)).to(torch.float16)
+    np.testing.assert_array_equal(O.to_f32(x), x.float().numpy())
+
+
+# ----------------------------------------------------------- weight INT8 asym
+def test_asym_hand_worked_rows(golden_dir):
+    g = load(golden_dir, "asym_minmax_examples.json")
+    for case in g["cases"]:
+        w = np.array([case["w"]], dtype=np.float32)
+        q, s, z = O.quantize_weight_int8_asym(w)
+        assert int(z[0]) == case["zero_point"], case["name"]
+        assert q[0].tolist() == case["codes"], case["name"]
+        if "scale" in case:
+            assert s[0] == np.float32(case["scale"])
+
+
+def test_asym_scale_is_binary32_division():
+    """S = fl(fl(hi - lo) / 255) bit for bit, checked with exact rationals and
+    an independent round-to-nearest-even to binary32."""
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((64, 40)) * 0.02).astype(np.float32)
+    _, s, z = O.quantize_weight_int8_asym(w)
+    for n in range(w.shape[0]):
+        lo = min(0.0, float(w[n].min()))
+        hi = max(0.0, float(w[n].max()))
+        rng_f = f32_round(Fraction(hi) - Fraction(lo))
+        s_ref = f32_round(Fraction(rng_f) / 255)
+        assert s[n] == np.float32(s_ref)
+        ratio = f32_round(Fraction(lo) / Fraction(s_ref))
+        assert int(z[n]) == -128 - int(round(ratio))  # Python round is half-even
+
+
+def test_asym_roundtrip_within_half_step():
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal((128, 256)) * 0.02).astype(np.float32)
+    q, s, z = O.quantize_weight_int8_asym(w)
+    r = O.dequantize_weight_int8(q, s, z)
+    err = np.abs(w.astype(np.float64) - r)
+    # half a step, plus slack for the binary32 rounding of S and of w/S
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 1e-5))
+    # the extremes of each row land on the ends of the code range
+    assert np.all(q.min(axis=1) == -128) and np.all(q.max(axis=1) == 127)
+
+
+def test_asym_zero_is_exact_and_metadata_size():
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((4096, 64)) * 0.02).astype(np.float32)
+    q, s, z = O.quantize_weight_int8_asym(w)
+    # the zero-point is the code of float 0: S (Z - Z) = 0
+    q0, s0, z0 = O.quantize_weight_int8_asym(np.zeros((1, 4), np.float32))
+    assert np.all(O.dequantize_weight_int8(q0, s0, z0) == 0)
+    assert np.all(z == np.rint(z)) and np.all((z >= -128) & (z <= 127))
+    # two fp32 values per output channel: 2 x 4096 x 4 B = 32 KB
+    assert s.nbytes + z.nbytes == 32 * 1024
+
+
+def test_asym_dequant_mse_small():
+    """The Lightning Fabric page checks dequantized-vs-original MSE < 1e-3."""
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((256, 256)) * 0.02).astype(np.float32)
+    q, s, z = O.quantize_weight_int8_asym(w)
+    assert np.mean((O.dequantize_weight_int8(q, s, z) - w) ** 2) < 1e-3
+
+
+def test_asym_one_signed_row_keeps_zero():
+    w = np.array([[0.5, 1.0, 2.0]], np.float32)
+    q, s, z = O.quantize_weight_int8_asym(w)
+    assert int(z[0]) == -128 and q[0, 2] == 127
+    w = np.array([[-3.0, -1.0, -0.25]], np.float32)
+    q, s, z = O.quantize_weight_int8_asym(w)
+    assert int(z[0]) == 127 and q[0, 0] == -128
+
+
+# ----------------------------------------------------------- act INT8 sym
+def test_symmetric_page_examples_4bit(golden_dir):
+    g = load(golden_dir, "notes_absmax_examples.json")
+    row = g["per_channel_row"]
+    q, s = O.quantize_symmetric_absmax(np.array([row["x"]], np.float32), 7)
+    assert abs(float(s[0]) - row["page_scale_approx"]) < 0.005
+    assert abs(48.5 / float(s[0]) - row["page_ratio_48_5"]) < 0.005
+    assert q[0, 3] == row["page_codes"]["48.5"]
+    assert list(q[0, :3]) == [0, 0, 0]
+    for blk in g["q4k_sub_blocks"]:
+        q, s = O.quantize_symmetric_absmax(np.array([blk["x"]], np.float32), 7)
+        assert abs(float(s[0]) - blk["page_scale"]) < 0.0005
+        assert q[0].tolist() == blk["formula_codes"]
+    # two of the three printed blocks agree with the formula; the third is a misprint
+    agree = [blk["page_codes"] == blk["formula_codes"] for blk in g["q4k_sub_blocks"]]
+    assert agree == [True, True, False]
+
+
+def test_symmetric_identity_and_bounds():
+    x = np.array([[-127, 5, 0, 64, 127], [1, 2, 3, -127, 0]], np.float32)
+    q, s, rs = O.quantize_act_int8_sym(x)
+    assert np.all(s == 1.0)
+    np.testing.assert_array_equal(q, x.astype(np.int8))
+    np.testing.assert_array_equal(rs, x.sum(axis=1).astype(np.int32))
+
+
+def test_symmetric_roundtrip_and_rowsum():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((32, 300)).astype(np.float32)
+    q, s, rs = O.quantize_act_int8_sym(x)
+    err = np.abs(x.astype(np.float64) - s.astype(np.float64)[:, None] * q)
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 1e-5))
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    for m in range(x.shape[0]):
+        assert int(rs[m]) == sum(int(v) for v in q[m])
+
+
+def test_symmetric_zero_row_floors_scale():
+    q, s, rs = O.quantize_act_int8_sym(np.zeros((2, 16), np.float32))
+    assert np.all(s == np.float32(1e-8)) and np.all(q == 0) and np.all(rs == 0)
+
+
+def test_ties_round_half_to_even():
+    """torch.round in every listing on the pages rounds half to even."""
+    q, s, _ = O.quantize_act_int8_sym(np.array([[127.0, 2.5, -3.5, 0.5, -0.5, 126.5]], np.float32))
+    assert s[0] == 1.0 and q[0].tolist() == [127, 2, -4, 0, 0, 126]
+    q, s, z = O.quantize_weight_int8_asym(np.array([[-128.0, 127.0, 2.5, -7.5]], np.float32))
+    assert s[0] == 1.0 and z[0] == 0 and q[0].tolist() == [-128, 127, 2, -8]
+
+
+def test_asym_codes_use_correctly_rounded_division():
+    """Codes come from fl(w / S) (binary32 division), not w * fl(1/S): values
+    placed next to half-way points between codes separate the two."""
+    S = np.float32(3.0) / np.float32(255.0)
+    vals = [np.float32(-1.0), np.float32(2.0)]
+    for k in range(-84, 169):
+        t = np.float32((k + 0.5) * float(S))
+        for d in (-2, -1, 0, 1, 2):
+            v = np.nextafter(t, np.float32(np.inf * d)) if d else t
+            for _ in range(abs(d) - 1):
+                v = np.nextafter(v, np.float32(np.inf * d))
+            if -1.0 <= v <= 2.0:
+                vals.append(np.float32(v))
+    w = np.array([vals], np.float32)
+    q, s, z = O.quantize_weight_int8_asym(w)
+    assert s[0] == S and z[0] == -43
+    for j, v in enumerate(vals):
+        quot = f32_round(Fraction(float(v)) / Fraction(float(S)))
+        ref = max(-128, min(127, round(quot) - 43))     # Python round: half to even
+        assert q[0, j] == ref, (j, float(v))
+
+
+# ----------------------------------------------------------- INT32 GEMM + epilogue
+@pytest.mark.parametrize("M,N,K", [(5, 3, 7), (4, 4, 6), (1, 9, 33)])
+def test_int_gemm_brute_force(M, N, K):
+    rng = np.random.default_rng(10 + M)
+    a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-128, 128, (N, K)).astype(np.int8)
+    acc = O.int_gemm(a, b)
+    assert acc.shape == (M, N)
+    for m in range(M):
+        for n in range(N):
+            assert acc[m, n] == sum(int(a[m, k]) * int(b[n, k]) for k in range(K))
+
+
+def test_int_gemm_extreme_fits_int32():
+    a = np.full((1, 4096), -127, np.int8)
+    b = np.full((1, 4096), -128, np.int8)
+    assert O.int_gemm(a, b)[0, 0] == 127 * 128 * 4096
+
+
+def test_zero_point_identity_exact():
+    """Sum_k qx (qw - Z) = acc - Z Sum_k qx, with Python integers."""
+    rng = np.random.default_rng(11)
+    qx = rng.integers(-127, 128, (4, 9)).astype(np.int8)
+    qw = rng.integers(-128, 128, (6, 9)).astype(np.int8)
+    z = rng.integers(-128, 128, 6).astype(np.float32)
+    acc = O.int_gemm(qx, qw)
+    rs = qx.astype(np.int64).sum(axis=1)
+    y = O.epilogue(acc, np.ones(4, np.float32), rs, np.ones(6, np.float32), z)
+    for m in range(4):
+        for n in range(6):
+            ref = sum(int(qx[m, k]) * (int(qw[n, k]) - int(z[n])) for k in range(9))
+            assert y[m, n] == ref
+
+
+def test_linear_integer_data_is_exact_product():
+    """With integer X of row absmax 127 and integer W spanning [-128, 127] both
+    quantizers are the identity, so the layer is the plain integer product."""
+    rng = np.random.default_rng(12)
+    x = rng.integers(-126, 127, (6, 32)).astype(np.float32)
+    x[:, 0] = 127
+    w = rng.integers(-127, 127, (5, 32)).astype(np.float32)
+    w[:, 1] = -128
+    w[:, 2] = 127
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    assert np.all(ws == 1) and np.all(wz == 0)
+    y, _ = O.linear_int8(x, wq, ws, wz)
+    np.testing.assert_array_equal(y, x.astype(np.float64) @ w.astype(np.float64).T)
+
+
+def test_linear_bias_and_transpose():
+    """A transposed operand or a bias added before scaling would break this."""
+    x = np.array([[254, 0, 0, 0], [0, 127, 0, 0]], np.float32)          # S_x = 2 and 1
+    w = np.array([[-128, 127, 0, 0], [127, -128, 10, 0], [0, 0, 127, -128]], np.float32)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    b = np.array([0.5, -1.0, 2.0], np.float32)
+    y, _ = O.linear_int8(x, wq, ws, wz, bias=b)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T + b
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_linear_close_to_float_product_tiny_config():
+    """Method-level sanity on the 16x256x256 workload: the W8A8 layer is about
+    1% off the unquantized product (a dropped term or sign would be far off)."""
+    from w8a8_quantized_linear_channel_amd import inputs
+    wl = inputs.tiny_linear()
+    wq, ws, wz = O.quantize_weight_int8_asym(wl.w)
+    y, _ = O.linear_int8(wl.x, wq, ws, wz)
+    ref = O.to_f32(wl.x).astype(np.float64) @ O.to_f32(wl.w).astype(np.float64).T
+    nerr = np.abs(y - ref).max() / np.abs(ref).max()
+    assert 1e-3 < nerr < 3e-2
+
+
+# ----------------------------------------------------------- LLM.int8 decomposition
+def test_outlier_set_brute_force_and_closed_threshold():
+    rng = np.random.default_rng(13)
+    x = np.clip(rng.standard_normal((20, 50)), -3.5, 3.5).astype(np.float16)
+    x[3, 7] = 6.0          # exactly the threshold: an outlier (closed interval)
+    x[5, 11] = -40.0
+    x[0, 30] = 5.99
+    cols = O.outlier_columns(x, 6.0)
+    brute = [k for k in range(50) if max(abs(float(x[m, k])) for m in range(20)) >= 6.0]
+    assert cols.tolist() == brute == [7, 11]
+    assert O.outlier_columns(x, 0.0).size == 0
+    assert O.outlier_columns(x, -1.0).size == 0
+
+
+def test_decomp_threshold_off_equals_plain_int8():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((9, 64)).astype(np.float16)
+    w = (rng.standard_normal((12, 64)) * 0.02).astype(np.float32)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    y1, _ = O.linear_int8_decomp(x, wq, ws, wz, tau=0.0)
+    y2, _ = O.linear_int8(x, wq, ws, wz)
+    np.testing.assert_array_equal(y1, y2)
+
+
+def test_decomp_all_columns_outliers_is_fp16_gemm():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((7, 48)).astype(np.float16)
+    w = (rng.standard_normal((10, 48)) * 0.02).astype(np.float32)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    y, inter = O.linear_int8_decomp(x, wq, ws, wz, tau=1e-30)
+    assert inter["cols"].size == 48 and np.all(inter["xq"] == 0)
+    wdq16 = O.dequantize_weight_int8(wq, ws, wz).astype(np.float16).astype(np.float64)
+    ref = x.astype(np.float64) @ wdq16.T
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-3 * np.abs(ref).max())
+
+
+def test_decomp_regular_scale_excludes_outliers():
+    x = np.zeros((1, 8), np.float16)
+    x[0, :] = [1.0, -2.0, 0.5, 50.0, 0.0, 3.0, -0.25, 1.5]
+    w = np.eye(8, dtype=np.float32)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    _, inter = O.linear_int8_decomp(x, wq, ws, wz, tau=6.0)
+    assert inter["cols"].tolist() == [3]
+    assert inter["x_scale"][0] == np.float32(3.0) / np.float32(127)
+    assert inter["xq"][0, 3] == 0 and inter["xq"][0, 5] == 127
+
+
+def test_decomp_beats_plain_int8_on_outlier_workload():
+    from w8a8_quantized_linear_channel_amd import inputs
+    wl = inputs.llm_int8_outliers(M=64, K=512, N=96, n_outlier_cols=4)
+    wq, ws, wz = O.quantize_weight_int8_asym(wl.w)
+    ref = O.to_f32(wl.x).astype(np.float64) @ O.to_f32(wl.w).astype(np.float64).T
+    yd, inter = O.linear_int8_decomp(wl.x, wq, ws, wz, tau=6.0)
+    yp, _ = O.linear_int8(wl.x, wq, ws, wz)
+    assert inter["cols"].tolist() == wl.extra["outlier_cols"].tolist()
+    e_d = np.abs(yd - ref).max() / np.abs(ref).max()
+    e_p = np.abs(yp - ref).max() / np.abs(ref).max()
+    assert e_d < 0.5 * e_p
+
+
+# ----------------------------------------------------------- FP8 e4m3
+def test_e4m3_decode_points(golden_dir):
+    g = load(golden_dir, "e4m3_points.json")
+    for p in g["decode"]:
+        v = O.e4m3_decode(np.array([p["code"]]))[0]
+        assert v == p["value"] and math.copysign(1, v) == math.copysign(1, p["value"])
+    assert np.isnan(O.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+
+
+def test_e4m3_encode_points(golden_dir):
+    g = load(golden_dir, "e4m3_points.json")
+    for p in g["encode_rne"]:
+        assert int(O.e4m3_encode(np.array([p["x"]]))[0]) == p["code"], p
+
+
+def test_e4m3_exhaustive_roundtrip():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    np.testing.assert_array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)
+
+
+def test_e4m3_matches_torch_cast_on_clamped_values():
+    rng = np.random.default_rng(16)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 50,
+        rng.standard_normal(20000) * 0.01,          # subnormal territory
+        rng.uniform(-448, 448, 20000),
+    ]).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_encode(v), ref)
+
+
+def test_fp8_identity_on_grid():
+    codes = np.array([[0x7E, 0x38, 0x01, 0xB8, 0x44, 0x00]], np.uint8)     # 448, 1, 2^-9, -1, 3, 0
+    x = O.e4m3_decode(codes).astype(np.float32)
+    q, s = O.quantize_fp8_rowwise(x)
+    assert s[0] == 1.0
+    np.testing.assert_array_equal(q, codes)
+
+
+def test_fp8_scale_ub_binds():
+    x = np.array([[5000.0, 1000.0, -2500.0, 10.0]], np.float32)
+    q, s = O.quantize_fp8_rowwise(x, scale_ub=1000.0)
+    assert s[0] == np.float32(1000.0) / np.float32(448)
+    assert O.e4m3_decode(q)[0].tolist()[:3] == [448.0, 448.0, -448.0]
+    q2, s2 = O.quantize_fp8_rowwise(x, scale_ub=None)
+    assert s2[0] == np.float32(5000.0) / np.float32(448)
+
+
+def test_fp8_linear_close_to_float_product():
+    from w8a8_quantized_linear_channel_amd import inputs
+    wl = inputs.fp8_rowwise(M=32, K=512, N=64)
+    wq, ws = O.quantize_fp8_rowwise(wl.w)
+    y, _ = O.linear_fp8(wl.x, wq, ws, scale_ub=1200.0)
+    ref = O.to_f32(wl.x).astype(np.float64) @ O.to_f32(wl.w).astype(np.float64).T
+    nerr = np.abs(y - ref).max() / np.abs(ref).max()
+    assert nerr < 0.08
+
+
+def test_max_rel_err_metric():
+    ref = np.array([100.0, 1.0, -1e-6, 0.0])
+    assert O.max_rel_err(ref, ref) == 0.0
+    y = ref + np.array([1.0, 0.0, 0.0, 0.0])
+    assert abs(O.max_rel_err(y, ref) - 0.01) < 1e-12
+    y = ref + np.array([0.0, 0.0, 0.05, 0.0])            # floor = 0.1 -> 0.5
+    assert abs(O.max_rel_err(y, ref) - 0.5) < 1e-9
