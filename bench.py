@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 quantized linear layer on one MI355X.
+
+Prints ONE JSON line.  The headline (`value`) is the prefill FFN-up step
+(q8_linear, X bf16 [2048, 4096] x W int8 [14336, 4096] -> bf16): per-token
+INT8 activation quantization followed by the INT8 MFMA GEMM with its fused
+dequantization epilogue, in int8 TOPS (2*M*N*K per step).  The weights are
+quantized once before timing, as at model load.  The same line carries the
+decode q_proj step (M = 16 and M = 1, N = K = 4096) in GB/s, the LLM.int8
+decomposition and the FP8 rowwise step, each with the roofline of its
+dominant kernel, and the CPU oracle timed on a bounded sample.
+
+Timing: W untimed warmup steps, then exactly K steps between two stream
+synchronizations, timed with HIP events on the stream the kernels run on.
+Inside the timed region every launch of the dominant kernel is bracketed by
+its own event pair; their mean is the kernel's average duration.  Decode
+steps (a few microseconds each) are captured into a HIP graph over 32
+distinct weight sets (537 MB, more than the 256 MB Infinity Cache) and
+replayed, so host launch overhead and cache reuse do not enter the figure.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from w8a8_quantized_linear_channel_amd import inputs  # noqa: E402
+from w8a8_quantized_linear_channel_amd import ops as q8  # noqa: E402
+
+PEAK_INT8_TOPS = 5000.0       # dense int8 MFMA, MI355X
+PEAK_FP8_TFLOPS = 5000.0      # dense fp8 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0         # HBM3E, MI355X
+METRIC = "q8_linear int8 TOPS (prefill) + GB/s (decode) and % of MI355X roofline"
+
+
+def ev():
+    return torch.cuda.Event(enable_timing=True)
+
+
+def timed_steps(step, steps, warmup, kernel_pairs):
+    """Run warmup + `steps` steps; return (ms per step, mean ms of the
+    bracketed dominant kernel).  `step(i, pair)` must launch one step and
+    record pair[0]/pair[1] around the dominant kernel."""
+    dummy = (ev(), ev())
+    for i in range(warmup):
+        step(i, dummy)
+    torch.cuda.synchronize()
+    t0, t1 = ev(), ev()
+    t0.record()
+    for i in range(steps):
+        step(i, kernel_pairs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    kern = sum(a.elapsed_time(b) for a, b in kernel_pairs) / steps
+    return total / steps, kern
+
+
+# ------------------------------------------------------------------ prefill
+def bench_prefill(dev, steps, warmup):
+    wl = inputs.prefill_ffn_up()
+    M, K = wl.x.shape
+    N = wl.w.shape[0]
+    x = wl.x.to(dev)
+    wq, ws, wz = q8.q8_quantize_weight(wl.w.to(dev), "int8_asym")      # offline step
+    xq = torch.empty(M, K, dtype=torch.int8, device=dev)
+    xs = torch.empty(M, dtype=torch.float32, device=dev)
+    xr = torch.empty(M, dtype=torch.int32, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def step(i, pair):
+        q8.q8_quantize_act(x, "int8_sym", out=(xq, xs, xr))
+        pair[0].record()
+        q8.q8_gemm_int8(xq, xs, xr, wq, ws, wz, out_dtype=torch.bfloat16, out=y)
+        pair[1].record()
+
+    pairs = [(ev(), ev()) for _ in range(steps)]
+    ms, gemm_ms = timed_steps(step, steps, warmup, pairs)
+    ops = 2.0 * M * N * K
+    res = {
+        "ms_per_step": ms,
+        "tops": ops / (ms * 1e-3) / 1e12,
+        "gemm_us": gemm_ms * 1e3,
+        "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
+        "shape": (M, N, K),
+        "host_inputs": (wl.x, wl.w),
+    }
+    # act-quant kernel alone (HBM-bound): bytes = X bf16 in + codes out + 8 B/row
+    pairs = [(ev(), ev()) for _ in range(steps)]
+
+    def qstep(i, pair):
+        pair[0].record()
+        q8.q8_quantize_act(x, "int8_sym", out=(xq, xs, xr))
+        pair[1].record()
+
+    _, q_ms = timed_steps(qstep, steps, 2, pairs)
+    qbytes = M * K * 2 + M * K + 8 * M
+    res["act_quant_us"] = q_ms * 1e3
+    res["act_quant_gbs"] = qbytes / (q_ms * 1e-3) / 1e9
+    return res
+
+
+# ------------------------------------------------------------------ decode
+def bench_decode(dev, M, replays, copies=32):
+    wl = inputs.decode_qproj(M=16)
+    N, K = wl.w.shape
+    x = wl.x[:M].contiguous().to(dev)
+    weights = []
+    for c in range(copies):
+        w = wl.w if c == 0 else inputs.decode_weight_copy(c, N, K)
+        weights.append(q8.q8_quantize_weight(w.to(dev), "int8_asym"))
+    ys = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    wsp = torch.empty(1, dtype=torch.uint8, device=dev)
+
+    def one_pass():
+        for c in range(copies):
+            wq, wsc, wz = weights[c]
+            q8.q8_linear(x, wq, wsc, wz, out_dtype=torch.bfloat16, out=ys[c], workspace=wsp)
+
+    one_pass()                      # warm up outside capture
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            one_pass()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = ev(), ev()
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    per_call_us = t0.elapsed_time(t1) * 1e3 / (replays * copies)
+    nbytes = N * K + 8 * N + M * K * 2 + M * N * 2
+    return {
+        "M": M, "N": N, "K": K,
+        "us_per_call": per_call_us,
+        "gbs": nbytes / (per_call_us * 1e-6) / 1e9,
+        "bytes_per_call": nbytes,
+    }
+
+
+# ------------------------------------------------------------------ LLM.int8
+def bench_decomp(dev, steps, warmup):
+    wl = inputs.llm_int8_outliers()
+    M, K = wl.x.shape
+    N = wl.w.shape[0]
+    x = wl.x.to(dev)
+    wq, ws, wz = q8.q8_quantize_weight(wl.w.to(dev), "int8_asym")
+    y = torch.empty(M, N, dtype=torch.float16, device=dev)
+    wsp = torch.empty(q8.q8_workspace_bytes("decomp", M, N, K), dtype=torch.uint8, device=dev)
+
+    def step(i, pair):
+        pair[0].record()
+        q8.q8_linear_int8_decomp(x, wq, ws, wz, 6.0, out=y, workspace=wsp)
+        pair[1].record()
+
+    pairs = [(ev(), ev()) for _ in range(steps)]
+    ms, _ = timed_steps(step, steps, warmup, pairs)
+    ops = 2.0 * M * N * K
+    nbytes = N * K + 8 * N + M * K * 2 + M * N * 2
+    t_ideal = max(ops / (PEAK_INT8_TOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+    return {"M": M, "N": N, "K": K, "ms_per_step": ms, "tops": ops / (ms * 1e-3) / 1e12,
+            "roofline": {"bound": "ridge", "ideal_us": t_ideal * 1e6, "frac": t_ideal / (ms * 1e-3)}}
+
+
+# ------------------------------------------------------------------ FP8
+def bench_fp8(dev, steps, warmup):
+    wl = inputs.fp8_rowwise()
+    M, K = wl.x.shape
+    N = wl.w.shape[0]
+    x = wl.x.to(dev)
+    wq, ws, _ = q8.q8_quantize_weight(wl.w.to(dev), "fp8_e4m3")
+    xq = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    xs = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def step(i, pair):
+        q8.q8_quantize_act(x, "fp8_e4m3", scale_ub=1200.0, out=(xq, xs, None))
+        pair[0].record()
+        q8.q8_gemm_fp8(xq, xs, wq, ws, out=y)
+        pair[1].record()
+
+    pairs = [(ev(), ev()) for _ in range(steps)]
+    ms, gemm_ms = timed_steps(step, steps, warmup, pairs)
+    flops = 2.0 * M * N * K
+    return {"M": M, "N": N, "K": K, "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "gemm_us": gemm_ms * 1e3,
+            "roofline": {"bound": "mfma", "achieved": flops / (gemm_ms * 1e-3) / 1e12,
+                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}}
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline(x_host, w_host, target_s):
+    """The oracle (untuned numpy) on a bounded sample of the prefill step: the
+    first R token rows of X against the full weight matrix."""
+    from oracle import q8_oracle as O
+    wq, ws, wz = O.quantize_weight_int8_asym(w_host)        # offline, untimed
+    N, K = w_host.shape
+    rows = 4
+    t = time.perf_counter()
+    O.linear_int8(x_host[:rows], wq, ws, wz)
+    dt = time.perf_counter() - t
+    rows = int(max(4, min(x_host.shape[0], rows * target_s / max(dt, 1e-3))))
+    t = time.perf_counter()
+    O.linear_int8(x_host[:rows], wq, ws, wz)
+    dt = time.perf_counter() - t
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"first {rows} of 2048 token rows (activation quantization, exact int64 GEMM, "
+                      f"epilogue) against all {N}x{K} weights; numpy's integer matmul is single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8"], default=None,
+                    help="run one workload (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    out = {"metric": METRIC}
+    if args.only in (None, "prefill"):
+        pf = bench_prefill(dev, args.steps, args.warmup)
+        M, N, K = pf["shape"]
+        out.update({
+            "value": round(pf["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(pf["ms_per_step"], 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "data": "synthetic: seeded numpy PCG64, X ~ N(0,1) in bf16, W ~ N(0,0.02) quantized once",
+            "config": {"workload": "prefill FFN-up q8_linear (dynamic per-token int8 X, per-channel "
+                                   "asymmetric int8 W, INT32 accumulation, bf16 out)",
+                       "M": M, "N": N, "K": K, "x_dtype": "bf16", "y_dtype": "bf16"},
+            "roofline": {"bound": "mfma", "kernel": "k_gemm int8 256x256",
+                         "achieved": round(pf["gemm_tops"], 1), "peak": PEAK_INT8_TOPS,
+                         "unit": "TOP/s", "frac": round(pf["gemm_tops"] / PEAK_INT8_TOPS, 4),
+                         "traffic": None, "kernel_us": round(pf["gemm_us"], 2)},
+            "act_quant": {"us": round(pf["act_quant_us"], 2), "gbs": round(pf["act_quant_gbs"], 1),
+                          "frac_hbm": round(pf["act_quant_gbs"] / PEAK_HBM_GBS, 4)},
+        })
+    if args.only in (None, "decode"):
+        dec = {}
+        for M in (16, 1):
+            d = bench_decode(dev, M, replays=max(4, args.steps // 4))
+            dec[f"M{M}"] = {"us_per_call": round(d["us_per_call"], 3), "GB/s": round(d["gbs"], 1),
+                            "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1),
+                                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                         "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                                         "bytes_per_call": d["bytes_per_call"]}}
+        out["decode"] = {"workload": "decode q_proj q8_linear, N = K = 4096, bf16, 32 rotating weight sets",
+                         **dec}
+    if args.only in (None, "decomp"):
+        d = bench_decomp(dev, args.steps, args.warmup)
+        out["llm_int8"] = {"workload": "LLM.int8 decomposition 512x4096x4096 fp16, 6 outlier columns",
+                           "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
+                           "roofline": {k: round(v, 4) if isinstance(v, float) else v
+                                        for k, v in d["roofline"].items()}}
+    if args.only in (None, "fp8"):
+        d = bench_fp8(dev, args.steps, args.warmup)
+        out["fp8"] = {"workload": "FP8 e4m3 rowwise 4096x4096x14336 bf16, scale_ub 1200",
+                      "ms_per_step": round(d["ms_per_step"], 5), "TFLOPS": round(d["tflops"], 1),
+                      "gemm_us": round(d["gemm_us"], 2),
+                      "roofline": {k: round(v, 4) if isinstance(v, float) else v
+                                   for k, v in d["roofline"].items()}}
+    if args.only in (None, "prefill") and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(*pf["host_inputs"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

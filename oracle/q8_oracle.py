@@ -283,18 +283,32 @@ def linear_fp8(x, wq_codes, w_scale, scale_ub=1200.0, bias=None):
     return y, {"xq": xq, "x_scale": xs}
 
 
+def fp8_abs_dot(x, wq_codes, w_scale, scale_ub=1200.0) -> np.ndarray:
+    """A[m,n] = S_x[m] S_w[n] sum_k |e4m3(xq[m,k])| |e4m3(wq[n,k])| -- the scale
+    on which the rounding error of any way of summing the FP8 products lives
+    (the usual dot-product error bound is proportional to it)."""
+    xq, xs = quantize_fp8_rowwise(x, scale_ub)
+    a = np.abs(e4m3_decode(xq)) @ np.abs(e4m3_decode(wq_codes)).T
+    return a * xs.astype(np.float64)[:, None] * w_scale.astype(np.float64)[None, :]
+
+
 # --------------------------------------------------------------------------
 # Comparison metric used by the parity tests
 # --------------------------------------------------------------------------
-def max_rel_err(y, y_ref, floor_frac: float = 1e-3) -> float:
-    """max_i |y_i - yref_i| / max(|yref_i|, floor_frac * max_j |yref_j|).
+def max_rel_err(y, y_ref, floor_frac: float = 1e-3, abs_dot=None, abs_dot_frac: float = 0.0) -> float:
+    """max_i |y_i - yref_i| / max(|yref_i|, floor_frac * max_j |yref_j|,
+    abs_dot_frac * abs_dot_i).
 
-    The floor keeps outputs that cancel to almost zero from dominating a
-    relative metric; it is 0.1% of the largest reference output."""
+    The first floor keeps outputs that cancel to almost zero from dominating
+    a relative metric (0.1% of the largest reference output).  The optional
+    second floor is for products whose hardware accumulation is not exact
+    (FP8): their error scales with sum_k |x_k w_k|, not with |y|."""
     y = np.asarray(y, dtype=np.float64)
     y_ref = np.asarray(y_ref, dtype=np.float64)
     if y_ref.size == 0:
         return 0.0
     floor = floor_frac * np.abs(y_ref).max()
     den = np.maximum(np.abs(y_ref), floor if floor > 0 else 1e-30)
+    if abs_dot is not None and abs_dot_frac > 0:
+        den = np.maximum(den, abs_dot_frac * np.asarray(abs_dot, dtype=np.float64))
     return float(np.max(np.abs(y - y_ref) / den))

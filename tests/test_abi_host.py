@@ -1,0 +1,143 @@
+"""Host-side tests of the C ABI: the library loads, exports every function
+include/q8.h declares, and rejects bad arguments before any device work.
+Pointers passed here are never dereferenced (validation fails first), so
+these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w8a8_quantized_linear_channel_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libq8.so not built")
+
+P = 0x10000           # a fake 16-byte-aligned device address (never dereferenced)
+P2 = 0x20000
+MIS = 0x10004         # misaligned
+INF = float("inf")
+NAN = float("nan")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = declared_functions()
+    for f in ["q8_quantize_weight", "q8_quantize_act", "q8_linear", "q8_linear_int8_decomp",
+              "q8_linear_fp8", "q8_workspace_bytes", "q8_status_str"]:
+        assert f in names
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    h = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(h, name), name
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code, name in _lib.STATUS_NAMES.items():
+        assert L.q8_status_str(code).decode() == name
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    ws = lambda op, M, N, K: L.q8_workspace_bytes(op, M, N, K)  # noqa: E731
+    # decode: the activation quantization is fused, no workspace
+    for M in (1, 2, 4, 8, 16):
+        assert ws(_lib.Q8_OP_LINEAR, M, 4096, 4096) == 0
+    # GEMM path: codes + scale + row sum, each 256-byte aligned
+    assert ws(_lib.Q8_OP_LINEAR, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192
+    assert ws(_lib.Q8_OP_FP8, 4096, 4096, 14336) == 4096 * 14336 + 16384
+    d = ws(_lib.Q8_OP_DECOMP, 512, 4096, 4096)
+    assert d >= 512 * 4096 + 2 * 2048 + 8 * 4096 * 4 + 4096 + 4096 * 4 + 4
+    # invalid shapes give 0
+    assert ws(_lib.Q8_OP_LINEAR, 0, 16, 16) == 0
+    assert ws(_lib.Q8_OP_LINEAR, 16, 16, 24) == 0
+
+
+def test_quantize_weight_validation():
+    L = _lib.lib()
+    f = L.q8_quantize_weight
+    E = _lib
+    assert f(E.Q8_INT8_SYM, P, E.Q8_F32, 4, 16, P, P, P, None) == 4        # BAD_FORMAT
+    assert f(E.Q8_INT8_ASYM, P, 7, 4, 16, P, P, P, None) == 3              # BAD_DTYPE
+    assert f(E.Q8_INT8_ASYM, P, E.Q8_F32, 0, 16, P, P, P, None) == 2       # BAD_SHAPE
+    assert f(E.Q8_INT8_ASYM, P, E.Q8_F32, 4, 24, P, P, P, None) == 2       # K % 16
+    assert f(E.Q8_INT8_ASYM, P, E.Q8_F32, 4, 65536 + 16, P, P, P, None) == 2
+    assert f(E.Q8_INT8_ASYM, None, E.Q8_F32, 4, 16, P, P, P, None) == 1    # NULL
+    assert f(E.Q8_INT8_ASYM, P, E.Q8_F32, 4, 16, P, P, None, None) == 1    # zero-point required
+    assert f(E.Q8_FP8_E4M3, P, E.Q8_F32, 4, 16, P, P, P, None) == 5        # zp must be NULL
+    assert f(E.Q8_INT8_ASYM, MIS, E.Q8_F32, 4, 16, P, P, P, None) == 6     # ALIGN
+
+
+def test_quantize_act_validation():
+    f = _lib.lib().q8_quantize_act
+    E = _lib
+    assert f(E.Q8_INT8_ASYM, P, E.Q8_BF16, 4, 16, INF, P, P, P, None) == 4
+    assert f(E.Q8_INT8_SYM, P, 9, 4, 16, INF, P, P, P, None) == 3
+    assert f(E.Q8_INT8_SYM, P, E.Q8_BF16, -1, 16, INF, P, P, P, None) == 2
+    assert f(E.Q8_INT8_SYM, P, E.Q8_BF16, 4, 16, INF, None, P, P, None) == 1
+    assert f(E.Q8_FP8_E4M3, P, E.Q8_BF16, 4, 16, NAN, P, P, None, None) == 5
+    assert f(E.Q8_FP8_E4M3, P, E.Q8_BF16, 4, 16, 0.0, P, P, None, None) == 5
+    assert f(E.Q8_FP8_E4M3, P, E.Q8_BF16, 4, 16, -3.0, P, P, None, None) == 5
+    assert f(E.Q8_FP8_E4M3, P, E.Q8_BF16, 4, 16, 1200.0, P, P, P, None) == 5   # no row sum for fp8
+    assert f(E.Q8_INT8_SYM, P, E.Q8_BF16, 4, 16, INF, P, P, MIS, None) == 6
+
+
+def test_linear_validation():
+    f = _lib.lib().q8_linear
+    E = _lib
+    ok = dict(x=P, xd=E.Q8_BF16, M=64, K=64, wq=P, ws=P, wz=P, N=64, b=None, y=P, yd=E.Q8_BF16,
+              w=P2, wb=1 << 20, acc=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["xd"], a["M"], a["K"], a["wq"], a["ws"], a["wz"], a["N"], a["b"], a["y"],
+                 a["yd"], a["w"], a["wb"], a["acc"], None)
+
+    assert call(xd=5) == 3
+    assert call(yd=-1) == 3
+    assert call(N=0) == 2
+    assert call(K=100) == 2
+    assert call(wz=None) == 1
+    assert call(y=None) == 1
+    assert call(w=None) == 7                   # workspace needed for M > 16
+    assert call(wb=100) == 7
+    assert call(b=MIS) == 6
+    assert call(acc=MIS) == 6
+    # decode needs no workspace: with none given, the next check (alignment) decides
+    assert call(M=8, w=None, wb=0, y=MIS) == 6
+
+
+def test_decomp_and_fp8_validation():
+    E = _lib
+    f = _lib.lib().q8_linear_int8_decomp
+    assert f(P, 64, 64, P, P, P, 64, NAN, None, P, P2, 1 << 24, None, None, None, None) == 5
+    assert f(P, 64, 64, P, P, P, 64, 6.0, None, P, None, 0, None, None, None, None) == 7
+    assert f(P, 64, 64, P, P, P, 64, 6.0, None, P, P2, 1 << 24, MIS, None, None, None) == 6
+    assert f(P, 64, 40, P, P, P, 64, 6.0, None, P, P2, 1 << 24, None, None, None, None) == 2
+    g = _lib.lib().q8_linear_fp8
+    assert g(P, 64, 64, P, P, 64, NAN, None, P, P2, 1 << 24, None) == 5
+    assert g(P, 64, 64, P, P, 64, 1200.0, None, P, P2, 10, None) == 7
+    assert g(None, 64, 64, P, P, 64, 1200.0, None, P, P2, 1 << 24, None) == 1
+
+
+def test_valid_arguments_without_a_device_report_device_error():
+    """With every argument valid, the call reaches the device check, which
+    fails cleanly when there is no GPU (the CPU test host).  Never run where a
+    GPU is visible: the fake pointers would then reach a kernel."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; the no-device path is checked on CPU hosts only")
+    E = _lib
+    st = _lib.lib().q8_quantize_weight(E.Q8_INT8_ASYM, P, E.Q8_F32, 4, 16, P, P, P, None)
+    assert st == 8

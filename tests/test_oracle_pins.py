@@ -390,3 +390,19 @@ def test_max_rel_err_metric():
     assert abs(O.max_rel_err(y, ref) - 0.01) < 1e-12
     y = ref + np.array([0.0, 0.0, 0.05, 0.0])            # floor = 0.1 -> 0.5
     assert abs(O.max_rel_err(y, ref) - 0.5) < 1e-9
+
+
+def test_fp8_abs_dot_bounds_the_output():
+    """|y| <= A elementwise (triangle inequality), with equality for
+    same-signed operands; the accumulation floor used for FP8 rests on it."""
+    from w8a8_quantized_linear_channel_amd import inputs
+    wl = inputs.fp8_rowwise(M=16, K=256, N=32)
+    wq, ws = O.quantize_fp8_rowwise(wl.w)
+    y, _ = O.linear_fp8(wl.x, wq, ws, 1200.0)
+    a = O.fp8_abs_dot(wl.x, wq, ws, 1200.0)
+    assert np.all(np.abs(y) <= a * (1 + 1e-12))
+    xp = np.abs(O.to_f32(wl.x))
+    wp = np.abs(O.to_f32(wl.w))
+    wq2, ws2 = O.quantize_fp8_rowwise(wp)
+    y2, _ = O.linear_fp8(xp, wq2, ws2, 1200.0)
+    np.testing.assert_allclose(y2, O.fp8_abs_dot(xp, wq2, ws2, 1200.0), rtol=1e-12)

@@ -1,0 +1,403 @@
+// C ABI of libq8: argument validation, workspace carving and kernel dispatch.
+// Every check that needs no device runs first, so argument errors are
+// reported before any HIP call (and can be exercised on a machine without a
+// GPU); then the device of the stream is checked once per device and cached.
+#include "q8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "q8_kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;          // keeps acc - Z*rowsum inside int32 (|.| <= 32512 K)
+constexpr int64_t kMaxRows = (1LL << 31) - 1;
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int d) { return d == Q8_F32 || d == Q8_F16 || d == Q8_BF16; }
+
+q8_status check_mk(int64_t M, int64_t K) {
+  if (M < 1 || K < 1 || M > kMaxRows) return Q8_ERR_BAD_SHAPE;
+  if (K % 16 != 0 || K > kMaxK) return Q8_ERR_BAD_SHAPE;
+  return Q8_OK;
+}
+
+q8_status check_mnk(int64_t M, int64_t N, int64_t K) {
+  q8_status s = check_mk(M, K);
+  if (s != Q8_OK) return s;
+  if (N < 1 || N > kMaxRows) return Q8_ERR_BAD_SHAPE;
+  // tile count of the smallest GEMM tile must fit an int grid
+  if (((M + 63) / 64) * ((N + 63) / 64) > kMaxRows) return Q8_ERR_BAD_SHAPE;
+  return Q8_OK;
+}
+
+// Bump allocator over the caller's workspace; every piece 256-byte aligned.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + kAlign - 1) / kAlign * kAlign;
+    return o;
+  }
+};
+
+struct LinearWs { size_t xq, xs, rs, total; };
+LinearWs linear_ws(int64_t M, int64_t K) {
+  LinearWs w{0, 0, 0, 0};
+  if (M <= q8::kGemvMaxM) return w;     // decode path: quantization is fused, no scratch
+  Carve c;
+  w.xq = c.take((size_t)M * K);
+  w.xs = c.take((size_t)M * 4);
+  w.rs = c.take((size_t)M * 4);
+  w.total = c.off;
+  return w;
+}
+
+struct DecompWs { size_t xq, xs, rs, partial, flags, idx, cnt, total; };
+DecompWs decomp_ws(int64_t M, int64_t K) {
+  Carve c;
+  DecompWs w;
+  const int64_t parts = (M + q8::kColmaxRows - 1) / q8::kColmaxRows;
+  w.xq = c.take((size_t)M * K);
+  w.xs = c.take((size_t)M * 4);
+  w.rs = c.take((size_t)M * 4);
+  w.partial = c.take((size_t)parts * K * 4);
+  w.flags = c.take((size_t)K);
+  w.idx = c.take((size_t)K * 4);
+  w.cnt = c.take(4);
+  w.total = c.off;
+  return w;
+}
+
+struct Fp8Ws { size_t xq, xs, total; };
+Fp8Ws fp8_ws(int64_t M, int64_t K) {
+  Carve c;
+  Fp8Ws w;
+  w.xq = c.take((size_t)M * K);
+  w.xs = c.take((size_t)M * 4);
+  w.total = c.off;
+  return w;
+}
+
+// ---- device check: gfx950 only, cached per device
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+q8_status device_of(hipStream_t st, int* dev) {
+  if (st != nullptr) {
+    if (hipStreamGetDevice(st, dev) != hipSuccess) return Q8_ERR_DEVICE;
+  } else if (hipGetDevice(dev) != hipSuccess) {
+    return Q8_ERR_DEVICE;
+  }
+  return (*dev >= 0 && *dev < kMaxDevices) ? Q8_OK : Q8_ERR_DEVICE;
+}
+
+q8_status check_device(hipStream_t st) {
+  int dev = -1;
+  q8_status s = device_of(st, &dev);
+  if (s != Q8_OK) {
+    (void)hipGetLastError();   // do not leave a sticky error for the caller
+    return s;
+  }
+  int state = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return Q8_ERR_DEVICE;
+    }
+    state = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? Q8_OK : Q8_ERR_DEVICE;
+}
+
+// Optional (Q8_DEBUG_VALIDATE=1): every pointer must be device memory of the
+// stream's device.
+bool debug_validate() {
+  static const bool on = [] {
+    const char* e = std::getenv("Q8_DEBUG_VALIDATE");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+q8_status check_ptrs(hipStream_t st, std::initializer_list<const void*> ptrs) {
+  if (!debug_validate()) return Q8_OK;
+  int dev = -1;
+  if (device_of(st, &dev) != Q8_OK) return Q8_ERR_DEVICE;
+  for (const void* p : ptrs) {
+    if (p == nullptr) continue;
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+      (void)hipGetLastError();
+      return Q8_ERR_BAD_ARG;
+    }
+    if (a.type != hipMemoryTypeDevice || a.device != dev) return Q8_ERR_BAD_ARG;
+  }
+  return Q8_OK;
+}
+
+q8_status launched(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNCH; }
+
+#define Q8_TRY(expr)                 \
+  do {                               \
+    const q8_status s_ = (expr);     \
+    if (s_ != Q8_OK) return s_;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* q8_status_str(q8_status s) {
+  switch (s) {
+    case Q8_OK: return "Q8_OK";
+    case Q8_ERR_NULL_PTR: return "Q8_ERR_NULL_PTR";
+    case Q8_ERR_BAD_SHAPE: return "Q8_ERR_BAD_SHAPE";
+    case Q8_ERR_BAD_DTYPE: return "Q8_ERR_BAD_DTYPE";
+    case Q8_ERR_BAD_FORMAT: return "Q8_ERR_BAD_FORMAT";
+    case Q8_ERR_BAD_ARG: return "Q8_ERR_BAD_ARG";
+    case Q8_ERR_ALIGN: return "Q8_ERR_ALIGN";
+    case Q8_ERR_WORKSPACE: return "Q8_ERR_WORKSPACE";
+    case Q8_ERR_DEVICE: return "Q8_ERR_DEVICE";
+    case Q8_ERR_LAUNCH: return "Q8_ERR_LAUNCH";
+  }
+  return "Q8_ERR_UNKNOWN";
+}
+
+size_t q8_workspace_bytes(q8_op op, int64_t M, int64_t N, int64_t K) {
+  if (check_mnk(M, N, K) != Q8_OK) return 0;
+  switch (op) {
+    case Q8_OP_LINEAR: return linear_ws(M, K).total;
+    case Q8_OP_DECOMP: return decomp_ws(M, K).total;
+    case Q8_OP_FP8: return fp8_ws(M, K).total;
+  }
+  return 0;
+}
+
+q8_status q8_quantize_weight(q8_format fmt, const void* w, q8_dtype w_dtype, int64_t N, int64_t K,
+                             void* wq, float* w_scale, float* w_zp, void* stream) {
+  if (fmt != Q8_INT8_ASYM && fmt != Q8_FP8_E4M3) return Q8_ERR_BAD_FORMAT;
+  if (!valid_dtype(w_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mk(N, K));
+  if (!w || !wq || !w_scale) return Q8_ERR_NULL_PTR;
+  if (fmt == Q8_INT8_ASYM && !w_zp) return Q8_ERR_NULL_PTR;
+  if (fmt == Q8_FP8_E4M3 && w_zp) return Q8_ERR_BAD_ARG;
+  if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale) || (w_zp && !aligned16(w_zp)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {w, wq, w_scale, w_zp}));
+  if (fmt == Q8_INT8_ASYM)
+    return launched(q8::launch_quant_weight_i8(w, w_dtype, N, K, static_cast<int8_t*>(wq), w_scale,
+                                               w_zp, st));
+  return launched(q8::launch_quant_rows_fp8(w, w_dtype, N, K, INFINITY, static_cast<uint8_t*>(wq),
+                                            w_scale, st));
+}
+
+q8_status q8_quantize_act(q8_format fmt, const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
+                          float scale_ub, void* xq, float* x_scale, int32_t* x_rowsum, void* stream) {
+  if (fmt != Q8_INT8_SYM && fmt != Q8_FP8_E4M3) return Q8_ERR_BAD_FORMAT;
+  if (!valid_dtype(x_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mk(M, K));
+  if (!x || !xq || !x_scale) return Q8_ERR_NULL_PTR;
+  if (fmt == Q8_FP8_E4M3) {
+    if (x_rowsum) return Q8_ERR_BAD_ARG;
+    if (std::isnan(scale_ub) || scale_ub <= 0.0f) return Q8_ERR_BAD_ARG;
+  }
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale) || (x_rowsum && !aligned16(x_rowsum)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, xq, x_scale, x_rowsum}));
+  if (fmt == Q8_INT8_SYM)
+    return launched(q8::launch_quant_act_i8(x, x_dtype, M, K, nullptr, static_cast<int8_t*>(xq),
+                                            x_scale, x_rowsum, st));
+  return launched(q8::launch_quant_rows_fp8(x, x_dtype, M, K, scale_ub, static_cast<uint8_t*>(xq),
+                                            x_scale, st));
+}
+
+q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const int8_t* wq,
+                    const float* w_scale, const float* w_zp, int64_t N, const float* bias, void* y,
+                    q8_dtype y_dtype, void* workspace, size_t workspace_bytes, int32_t* acc_out,
+                    void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mnk(M, N, K));
+  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  const LinearWs ws = linear_ws(M, K);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (acc_out && !aligned16(acc_out)) ||
+      (ws.total > 0 && !aligned16(workspace)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace, acc_out}));
+
+  if (M <= q8::kGemvMaxM)
+    return launched(q8::launch_gemv_i8(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype,
+                                       acc_out, st));
+
+  char* base = static_cast<char*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
+  float* xs = reinterpret_cast<float*>(base + ws.xs);
+  int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
+  Q8_TRY(launched(q8::launch_quant_act_i8(x, x_dtype, M, K, nullptr, xq, xs, rs, st)));
+  q8::GemmArgs g{};
+  g.a = reinterpret_cast<const uint8_t*>(xq);
+  g.b = reinterpret_cast<const uint8_t*>(wq);
+  g.a_scale = xs;
+  g.a_rowsum = rs;
+  g.b_scale = w_scale;
+  g.b_zp = w_zp;
+  g.bias = bias;
+  g.y = y;
+  g.acc_out = acc_out;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launched(q8::launch_gemm(q8::GEMM_INT8, g, y_dtype, st));
+}
+
+q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_t* wq,
+                                const float* w_scale, const float* w_zp, int64_t N, float threshold,
+                                const float* bias, void* y, void* workspace, size_t workspace_bytes,
+                                int32_t* outlier_idx, int32_t* n_outliers, int32_t* acc_out,
+                                void* stream) {
+  Q8_TRY(check_mnk(M, N, K));
+  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (std::isnan(threshold)) return Q8_ERR_BAD_ARG;
+  const DecompWs ws = decomp_ws(M, K);
+  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
+      !aligned16(workspace) || (bias && !aligned16(bias)) || (acc_out && !aligned16(acc_out)) ||
+      (outlier_idx && !aligned16(outlier_idx)) || (n_outliers && !aligned16(n_outliers)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace, outlier_idx, n_outliers, acc_out}));
+
+  char* base = static_cast<char*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
+  float* xs = reinterpret_cast<float*>(base + ws.xs);
+  int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
+  float* partial = reinterpret_cast<float*>(base + ws.partial);
+  uint8_t* flags = reinterpret_cast<uint8_t*>(base + ws.flags);
+  int32_t* idx = reinterpret_cast<int32_t*>(base + ws.idx);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + ws.cnt);
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+
+  Q8_TRY(launched(q8::launch_outlier_detect(xh, M, K, threshold, partial, flags, idx, cnt, outlier_idx,
+                                            n_outliers, st)));
+  Q8_TRY(launched(q8::launch_quant_act_i8(x, Q8_F16, M, K, flags, xq, xs, rs, st)));
+  q8::GemmArgs g{};
+  g.a = reinterpret_cast<const uint8_t*>(xq);
+  g.b = reinterpret_cast<const uint8_t*>(wq);
+  g.a_scale = xs;
+  g.a_rowsum = rs;
+  g.b_scale = w_scale;
+  g.b_zp = w_zp;
+  g.bias = bias;
+  g.y = y;
+  g.acc_out = acc_out;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.x_f16 = xh;
+  g.out_idx = idx;
+  g.out_cnt = cnt;
+  return launched(q8::launch_gemm(q8::GEMM_INT8_DECOMP, g, Q8_F16, st));
+}
+
+q8_status q8_linear_fp8(const void* x, int64_t M, int64_t K, const uint8_t* wq, const float* w_scale,
+                        int64_t N, float scale_ub, const float* bias, void* y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Q8_TRY(check_mnk(M, N, K));
+  if (!x || !wq || !w_scale || !y) return Q8_ERR_NULL_PTR;
+  if (std::isnan(scale_ub) || scale_ub <= 0.0f) return Q8_ERR_BAD_ARG;
+  const Fp8Ws ws = fp8_ws(M, K);
+  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) || !aligned16(workspace) ||
+      (bias && !aligned16(bias)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, wq, w_scale, bias, y, workspace}));
+
+  char* base = static_cast<char*>(workspace);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + ws.xq);
+  float* xs = reinterpret_cast<float*>(base + ws.xs);
+  Q8_TRY(launched(q8::launch_quant_rows_fp8(x, Q8_BF16, M, K, scale_ub, xq, xs, st)));
+  q8::GemmArgs g{};
+  g.a = xq;
+  g.b = wq;
+  g.a_scale = xs;
+  g.b_scale = w_scale;
+  g.bias = bias;
+  g.y = y;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launched(q8::launch_gemm(q8::GEMM_FP8, g, Q8_BF16, st));
+}
+
+q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                       int64_t K, const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N,
+                       const float* bias, void* y, q8_dtype y_dtype, int32_t* acc_out, void* stream) {
+  if (!valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mnk(M, N, K));
+  if (!xq || !x_scale || !x_rowsum || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(x_rowsum) || !aligned16(wq) ||
+      !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) || (bias && !aligned16(bias)) ||
+      (acc_out && !aligned16(acc_out)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {xq, x_scale, x_rowsum, wq, w_scale, w_zp, bias, y, acc_out}));
+  q8::GemmArgs g{};
+  g.a = reinterpret_cast<const uint8_t*>(xq);
+  g.b = reinterpret_cast<const uint8_t*>(wq);
+  g.a_scale = x_scale;
+  g.a_rowsum = x_rowsum;
+  g.b_scale = w_scale;
+  g.b_zp = w_zp;
+  g.bias = bias;
+  g.y = y;
+  g.acc_out = acc_out;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launched(q8::launch_gemm(q8::GEMM_INT8, g, y_dtype, st));
+}
+
+q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,
+                      const float* w_scale, int64_t N, const float* bias, void* y, void* stream) {
+  Q8_TRY(check_mnk(M, N, K));
+  if (!xq || !x_scale || !wq || !w_scale || !y) return Q8_ERR_NULL_PTR;
+  if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+      (bias && !aligned16(bias)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {xq, x_scale, wq, w_scale, bias, y}));
+  q8::GemmArgs g{};
+  g.a = xq;
+  g.b = wq;
+  g.a_scale = x_scale;
+  g.b_scale = w_scale;
+  g.bias = bias;
+  g.y = y;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launched(q8::launch_gemm(q8::GEMM_FP8, g, Q8_BF16, st));
+}
+
+}  // extern "C"

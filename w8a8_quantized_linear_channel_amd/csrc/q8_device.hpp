@@ -1,0 +1,154 @@
+// Device-side helpers shared by the libq8 kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Element types of X / W / Y, matching q8_dtype.
+enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+constexpr float kEps = 1e-8f;        // floor of every scale
+constexpr float kFp8Max = 448.0f;    // largest finite OCP e4m3fn value
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Decode one 16-byte chunk of a row into floats: 4 for fp32, 8 for fp16/bf16.
+template <int DT> struct Chunk;
+template <> struct Chunk<DT_F32> {
+  static constexpr int kElems = 4;
+  __device__ __forceinline__ static void decode(const v4i& c, float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __int_as_float(c[i]);
+  }
+};
+template <> struct Chunk<DT_F16> {
+  static constexpr int kElems = 8;
+  __device__ __forceinline__ static void decode(const v4i& c, float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t u = (uint32_t)c[i];
+      v[2 * i] = f16_bits_to_f32(u & 0xffffu);
+      v[2 * i + 1] = f16_bits_to_f32(u >> 16);
+    }
+  }
+};
+template <> struct Chunk<DT_BF16> {
+  static constexpr int kElems = 8;
+  __device__ __forceinline__ static void decode(const v4i& c, float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t u = (uint32_t)c[i];
+      v[2 * i] = __uint_as_float(u << 16);
+      v[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+    }
+  }
+};
+
+// fp32 -> bf16 / fp16 with round-to-nearest-even (hardware conversions).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int DT> __device__ __forceinline__ void store_out(void* y, int64_t i, float v);
+template <> __device__ __forceinline__ void store_out<DT_F32>(void* y, int64_t i, float v) {
+  ((float*)y)[i] = v;
+}
+template <> __device__ __forceinline__ void store_out<DT_F16>(void* y, int64_t i, float v) {
+  ((uint16_t*)y)[i] = f32_to_f16(v);
+}
+template <> __device__ __forceinline__ void store_out<DT_BF16>(void* y, int64_t i, float v) {
+  ((uint16_t*)y)[i] = f32_to_bf16(v);
+}
+
+// Wave64 reductions (butterfly over all 64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Block-wide reductions for blocks of NW waves; `red` is LDS of >= NW slots.
+// Every thread gets the result.
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+template <int NW>
+__device__ __forceinline__ float block_min(float v, float* red) {
+  v = wave_min(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = fminf(r, red[i]);
+  return r;
+}
+template <int NW>
+__device__ __forceinline__ int block_sum(int v, int* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) r += red[i];
+  return r;
+}
+
+// Symmetric int8 code: clamp(rne(x / s), -127, 127) with IEEE division.
+__device__ __forceinline__ int code_sym_i8(float x, float s) {
+  float q = __builtin_rintf(x / s);
+  q = fminf(fmaxf(q, -127.0f), 127.0f);
+  return (int)q;
+}
+
+// Four e4m3fn codes (ties to even) of values already clamped to [-448, 448],
+// packed little-endian into one word.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
+  return (uint32_t)p;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+}  // namespace q8

@@ -1,0 +1,50 @@
+// Internal launchers of the libq8 kernels (host side, not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+// Quantizers (quant.hip); dt / ydt use the q8_dtype numbering.
+hipError_t launch_quant_weight_i8(const void* w, int dt, int64_t N, int64_t K, int8_t* wq,
+                                  float* w_scale, float* w_zp, hipStream_t st);
+hipError_t launch_quant_rows_fp8(const void* x, int dt, int64_t R, int64_t K, float bound,
+                                 uint8_t* xq, float* x_scale, hipStream_t st);
+hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, const uint8_t* colflag,
+                               int8_t* xq, float* x_scale, int32_t* x_rowsum, hipStream_t st);
+
+// Operands and epilogue inputs of the MFMA GEMM (gemm.hip).
+struct GemmArgs {
+  const uint8_t* a;         // [M, K] activation codes (int8 or e4m3 bytes)
+  const uint8_t* b;         // [N, K] weight codes
+  const float* a_scale;     // [M]
+  const int32_t* a_rowsum;  // [M], int8 paths
+  const float* b_scale;     // [N]
+  const float* b_zp;        // [N], int8 paths
+  const float* bias;        // [N] or null
+  void* y;                  // [M, N] of ydt
+  int32_t* acc_out;         // [M, N] or null (int8 paths)
+  int64_t M, N, K;
+  // LLM.int8 outlier flow
+  const uint16_t* x_f16;    // [M, K] fp16 activations
+  const int32_t* out_idx;   // ascending outlier columns
+  const int32_t* out_cnt;   // [1] number of outlier columns (device)
+};
+
+enum GemmKind : int { GEMM_INT8 = 0, GEMM_INT8_DECOMP = 1, GEMM_FP8 = 2 };
+
+hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, int ydt, hipStream_t st);
+
+// Decode-shaped int8 linear, M <= 16, activation quantization fused (gemv.hip).
+hipError_t launch_gemv_i8(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq,
+                          const float* w_scale, const float* w_zp, int64_t N, const float* bias,
+                          void* y, int ydt, int32_t* acc_out, hipStream_t st);
+constexpr int64_t kGemvMaxM = 16;
+
+// LLM.int8 outlier detection (decomp.hip).  partial: [ceil(M/64), K] floats.
+hipError_t launch_outlier_detect(const uint16_t* x_f16, int64_t M, int64_t K, float threshold,
+                                 float* partial, uint8_t* flags, int32_t* idx, int32_t* cnt,
+                                 int32_t* user_idx, int32_t* user_cnt, hipStream_t st);
+constexpr int64_t kColmaxRows = 64;
+
+}  // namespace q8

@@ -1,0 +1,225 @@
+"""Thin torch binding of the libq8 C ABI, one Python function per C call and
+with the same name.  It checks tensor devices/dtypes/shapes, allocates
+outputs and the workspace with torch, passes raw device pointers and the
+current HIP stream, and turns a non-OK status into an exception.  All
+arithmetic happens in the HIP kernels."""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.Q8_F32, torch.float16: _lib.Q8_F16, torch.bfloat16: _lib.Q8_BF16}
+_FMT = {"int8_asym": _lib.Q8_INT8_ASYM, "int8_sym": _lib.Q8_INT8_SYM, "fp8_e4m3": _lib.Q8_FP8_E4M3}
+_OP = {"linear": _lib.Q8_OP_LINEAR, "decomp": _lib.Q8_OP_DECOMP, "fp8": _lib.Q8_OP_FP8}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, dev=None) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def q8_workspace_bytes(op: str, M: int, N: int, K: int) -> int:
+    return int(_lib.lib().q8_workspace_bytes(_OP[op], M, N, K))
+
+
+def _workspace(op: str, M: int, N: int, K: int, dev) -> torch.Tensor:
+    n = q8_workspace_bytes(op, M, N, K)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+
+
+def q8_quantize_weight(w: torch.Tensor, fmt: str = "int8_asym"):
+    """Per-output-channel weight quantization.  Returns (wq, scale, zero_point);
+    zero_point is None for "fp8_e4m3" (codes are returned as uint8)."""
+    _need(w, "w")
+    if w.dim() != 2 or w.dtype not in _DT:
+        raise ValueError("w must be 2-D float32/float16/bfloat16")
+    N, K = w.shape
+    dev = w.device
+    if fmt == "int8_asym":
+        wq = torch.empty(N, K, dtype=torch.int8, device=dev)
+        zp = torch.empty(N, dtype=torch.float32, device=dev)
+    elif fmt == "fp8_e4m3":
+        wq = torch.empty(N, K, dtype=torch.uint8, device=dev)
+        zp = None
+    else:
+        raise ValueError(f"unsupported weight format {fmt}")
+    scale = torch.empty(N, dtype=torch.float32, device=dev)
+    st = _lib.lib().q8_quantize_weight(_FMT[fmt], _ptr(w), _DT[w.dtype], N, K, _ptr(wq), _ptr(scale),
+                                       _ptr(zp), _stream(dev))
+    _lib.check("q8_quantize_weight", st)
+    return wq, scale, zp
+
+
+def q8_quantize_act(x: torch.Tensor, fmt: str = "int8_sym", scale_ub: float = math.inf,
+                    rowsum: bool = True, out=None):
+    """Dynamic per-token quantization.  Returns (xq, scale, rowsum or None);
+    `out` may supply those three tensors preallocated."""
+    _need(x, "x")
+    if x.dim() != 2 or x.dtype not in _DT:
+        raise ValueError("x must be 2-D float32/float16/bfloat16")
+    M, K = x.shape
+    dev = x.device
+    if fmt not in ("int8_sym", "fp8_e4m3"):
+        raise ValueError(f"unsupported activation format {fmt}")
+    code_dt = torch.int8 if fmt == "int8_sym" else torch.uint8
+    if out is not None:
+        xq, scale, rs = out
+        _need(xq, "xq", code_dt, (M, K), dev)
+        _need(scale, "scale", torch.float32, (M,), dev)
+        if rs is not None:
+            _need(rs, "rowsum", torch.int32, (M,), dev)
+    else:
+        xq = torch.empty(M, K, dtype=code_dt, device=dev)
+        scale = torch.empty(M, dtype=torch.float32, device=dev)
+        rs = torch.empty(M, dtype=torch.int32, device=dev) if (rowsum and fmt == "int8_sym") else None
+    st = _lib.lib().q8_quantize_act(_FMT[fmt], _ptr(x), _DT[x.dtype], M, K, float(scale_ub), _ptr(xq),
+                                    _ptr(scale), _ptr(rs), _stream(dev))
+    _lib.check("q8_quantize_act", st)
+    return xq, scale, rs
+
+
+def q8_linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, w_zp: torch.Tensor,
+              bias: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+              acc_out: bool = False, workspace: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None):
+    """W8A8 linear.  Returns y (and the INT32 accumulator if acc_out)."""
+    _need(x, "x")
+    dev = x.device
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(wq, "wq", torch.int8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    _need(w_zp, "w_zp", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    out_dtype = out_dtype or x.dtype
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=dev)
+    _need(y, "y", out_dtype, (M, N), dev)
+    acc = torch.empty(M, N, dtype=torch.int32, device=dev) if acc_out else None
+    ws = workspace if workspace is not None else _workspace("linear", M, N, K, dev)
+    st = _lib.lib().q8_linear(_ptr(x), _DT[x.dtype], M, K, _ptr(wq), _ptr(w_scale), _ptr(w_zp), N,
+                              _ptr(bias), _ptr(y), _DT[out_dtype], _ptr(ws), ws.numel(), _ptr(acc),
+                              _stream(dev))
+    _lib.check("q8_linear", st)
+    return (y, acc) if acc_out else y
+
+
+def q8_linear_int8_decomp(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                          w_zp: torch.Tensor, threshold: float = 6.0,
+                          bias: Optional[torch.Tensor] = None, return_outliers: bool = False,
+                          acc_out: bool = False, workspace: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None):
+    """LLM.int8() decomposition.  Returns y, plus (outlier_idx, n_outliers)
+    device tensors if return_outliers, plus the int8-path accumulator if acc_out."""
+    _need(x, "x", torch.float16)
+    dev = x.device
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(wq, "wq", torch.int8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    _need(w_zp, "w_zp", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    y = out if out is not None else torch.empty(M, N, dtype=torch.float16, device=dev)
+    _need(y, "y", torch.float16, (M, N), dev)
+    idx = torch.empty(K, dtype=torch.int32, device=dev) if return_outliers else None
+    cnt = torch.empty(1, dtype=torch.int32, device=dev) if return_outliers else None
+    acc = torch.empty(M, N, dtype=torch.int32, device=dev) if acc_out else None
+    ws = workspace if workspace is not None else _workspace("decomp", M, N, K, dev)
+    st = _lib.lib().q8_linear_int8_decomp(_ptr(x), M, K, _ptr(wq), _ptr(w_scale), _ptr(w_zp), N,
+                                          float(threshold), _ptr(bias), _ptr(y), _ptr(ws), ws.numel(),
+                                          _ptr(idx), _ptr(cnt), _ptr(acc), _stream(dev))
+    _lib.check("q8_linear_int8_decomp", st)
+    res = [y]
+    if return_outliers:
+        res += [idx, cnt]
+    if acc_out:
+        res.append(acc)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def q8_linear_fp8(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                  scale_ub: float = 1200.0, bias: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """FP8 e4m3 W8A8 rowwise linear (bf16 in, bf16 out)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(wq, "wq", torch.uint8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (M, N), dev)
+    ws = workspace if workspace is not None else _workspace("fp8", M, N, K, dev)
+    st = _lib.lib().q8_linear_fp8(_ptr(x), M, K, _ptr(wq), _ptr(w_scale), N, float(scale_ub), _ptr(bias),
+                                  _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check("q8_linear_fp8", st)
+    return y
+
+
+def q8_gemm_int8(xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor, wq: torch.Tensor,
+                 w_scale: torch.Tensor, w_zp: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                 out_dtype: torch.dtype = torch.bfloat16, acc_out: bool = False,
+                 out: Optional[torch.Tensor] = None):
+    """INT8 GEMM + dequantization epilogue on pre-quantized activations."""
+    _need(xq, "xq", torch.int8)
+    dev = xq.device
+    M, K = xq.shape
+    N = wq.shape[0]
+    _need(x_scale, "x_scale", torch.float32, (M,), dev)
+    _need(x_rowsum, "x_rowsum", torch.int32, (M,), dev)
+    _need(wq, "wq", torch.int8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    _need(w_zp, "w_zp", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=dev)
+    _need(y, "y", out_dtype, (M, N), dev)
+    acc = torch.empty(M, N, dtype=torch.int32, device=dev) if acc_out else None
+    st = _lib.lib().q8_gemm_int8(_ptr(xq), _ptr(x_scale), _ptr(x_rowsum), M, K, _ptr(wq), _ptr(w_scale),
+                                 _ptr(w_zp), N, _ptr(bias), _ptr(y), _DT[out_dtype], _ptr(acc),
+                                 _stream(dev))
+    _lib.check("q8_gemm_int8", st)
+    return (y, acc) if acc_out else y
+
+
+def q8_gemm_fp8(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Rowwise FP8 GEMM on e4m3 codes (bf16 out)."""
+    _need(xq, "xq", torch.uint8)
+    dev = xq.device
+    M, K = xq.shape
+    N = wq.shape[0]
+    _need(x_scale, "x_scale", torch.float32, (M,), dev)
+    _need(wq, "wq", torch.uint8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (M, N), dev)
+    st = _lib.lib().q8_gemm_fp8(_ptr(xq), _ptr(x_scale), M, K, _ptr(wq), _ptr(w_scale), N, _ptr(bias),
+                                _ptr(y), _stream(dev))
+    _lib.check("q8_gemm_fp8", st)
+    return y
