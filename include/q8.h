@@ -26,8 +26,10 @@
  * - Every argument is checked on the host BEFORE anything is enqueued.  On a
  *   non-Q8_OK status nothing has been written.  Q8_ERR_LAUNCH reports a
  *   failed kernel launch (hipGetLastError) after validation passed.
- * - Preconditions checked for every call: M, N, K >= 1; K % 16 == 0; all
- *   pointers 16-byte aligned; the device running `stream` is gfx950.
+ * - Preconditions checked for every call: M, N, K >= 1; K % 16 == 0;
+ *   K <= 65536 (keeps the zero-point-corrected INT32 sums in range); every
+ *   matrix (X, W, Y) has fewer than 2^31 elements; all pointers 16-byte
+ *   aligned; the device running `stream` is gfx950.
  *   Inputs must be finite: NaN/Inf inputs give unspecified codes and outputs.
  * - Floating point follows IEEE binary32 with round-to-nearest-even; scales
  *   are computed with correctly rounded division, codes with x / S (not

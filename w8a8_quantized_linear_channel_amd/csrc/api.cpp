@@ -32,8 +32,8 @@ q8_status check_mnk(int64_t M, int64_t N, int64_t K) {
   q8_status s = check_mk(M, K);
   if (s != Q8_OK) return s;
   if (N < 1 || N > kMaxRows) return Q8_ERR_BAD_SHAPE;
-  // tile count of the smallest GEMM tile must fit an int grid
-  if (((M + 63) / 64) * ((N + 63) / 64) > kMaxRows) return Q8_ERR_BAD_SHAPE;
+  // the GEMM indexes its operands and output with 32-bit offsets
+  if (M * K > kMaxRows || N * K > kMaxRows || M * N > kMaxRows) return Q8_ERR_BAD_SHAPE;
   return Q8_OK;
 }
 

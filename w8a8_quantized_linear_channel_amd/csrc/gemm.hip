@@ -9,23 +9,37 @@
 //   GEMM_INT8_DECOMP  as GEMM_INT8, then the LLM.int8 outlier flow is added
 //                     with v_mfma_f32_32x32x16_f16 on top of the dequantized
 //                     accumulator: y += X[:, O] . fp16(S_b (Wq[:, O] - Z_b))^T
-//   GEMM_FP8          v_mfma_f32_16x16x128_f8f6f4 on e4m3 codes, fp32
+//   GEMM_FP8          v_mfma_f32_32x32x64_f8f6f4 on e4m3 codes, fp32
 //                     accumulation, y = S_a[m] S_b[n] acc (+ bias)
 //
 // Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile; each wave
-// owns (BM/2) x (BN/2) built from MFMA fragments (32 x 32 int8, 16 x 16 fp8).  K advances 128 bytes per
-// stage.  Stages are double buffered in LDS: while the MFMAs consume stage k,
-// the next stage's global loads are in flight in registers.  The 16-byte
-// chunks of each 128-byte LDS row are XOR-swizzled by (row & 7), so the
-// fragment reads (rows 0..7 of one chunk column in one LDS cycle) hit 8
-// distinct bank groups.  Workgroups are renumbered so that consecutive tiles
-// land on the same XCD (the dispatcher deals workgroups round-robin over the 8
-// XCDs) and, within an XCD, 4 tile-rows share each weight tile in L2.
+// owns (BM/2) x (BN/2) built from 32 x 32 MFMA fragments.  K advances 128
+// bytes per stage.  Stages are double buffered in LDS and filled by
+// global_load_lds_dwordx4 (global -> LDS without registers): while the MFMAs
+// consume one buffer the next stage streams into the other.  Within a stage
+// the B fragments of k-step s+1 are read from LDS while the MFMAs of k-step s
+// run, and each A fragment is re-read right after its last use.
+//
+// LDS layout: row-major 128-byte rows (one row of the tile, one stage of K),
+// the 16-byte chunk c of row r stored at chunk position c ^ (r & 7).  A
+// fragment read has rows 0..7 of one logical chunk in one LDS cycle, and the
+// XOR puts them in 8 distinct bank groups.  The DMA writes 64 consecutive
+// 16-byte slots per wave instruction, so the swizzle is applied on the global
+// side: each lane fetches the chunk that belongs at its fixed slot.
+//
+// Workgroups are renumbered so consecutive tiles land on the same XCD (the
+// dispatcher deals workgroups round-robin over the 8 XCDs) and, within an
+// XCD, 4 tile-rows share each weight tile in L2.
+//
+// Indices are 32-bit: the host guarantees M*K, N*K and M*N are below 2^31.
 #include "q8_device.hpp"
 #include "q8_kernels.hpp"
 
 namespace q8 {
 namespace {
+
+typedef __attribute__((address_space(1))) void* gptr_t;   // global (DMA source)
+typedef __attribute__((address_space(3))) void* lptr_t;   // LDS (DMA destination)
 
 constexpr int kBK = 128;            // bytes of K per stage
 constexpr int kThreads = 256;       // 4 waves
@@ -34,51 +48,49 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
 
-// One MFMA shape: operand fragment loads from the swizzled LDS stage, the
-// instruction, and where output register r of a lane lands in the fragment.
+// One MFMA shape.  A fragment row is (base multiple of 32) + lane % 32, so
+// (row & 7) == (lane & 7) and the swizzled byte offset of the lane's operand
+// inside its LDS row is lane_off(lane) XOR a per-k-step constant.
 // A and B fragments use the same lane -> k mapping, so each instruction sums
 // over exactly the k bytes of its step whatever order the hardware uses.
 struct MmaI8 {                       // v_mfma_i32_32x32x32_i8
-  static constexpr int F = 32, KSTEP = 32, NR = 16;
+  static constexpr int KSTEP = 32, NR = 16;
   using Op = v4i;
   using Acc = v16i;
-  // lane l: row l % 32, 16-byte chunk l / 32 of the 32-byte k-step
-  __device__ static Op load(const uint8_t* S, int row, int ks, int lane) {
-    return *(const v4i*)(S + swz(row, ks * 2 + (lane >> 5)));
+  // lane l: 16-byte logical chunk 2*ks + l/32 of its row
+  __device__ static int lane_off(int lane) { return ((lane >> 5) ^ (lane & 7)) << 4; }
+  __device__ static Op load(const uint8_t* row, int off, int ks) {
+    return *(const v4i*)(row + (off ^ (ks << 5)));
   }
   __device__ static Acc mma(const Op& a, const Op& b, const Acc& c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
-  __device__ static int op_row(int lane) { return lane & 31; }
-  __device__ static int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-  __device__ static int out_col(int lane) { return lane & 31; }
 };
-struct MmaF8 {                       // v_mfma_f32_16x16x128_f8f6f4, both operands e4m3
-  static constexpr int F = 16, KSTEP = 128, NR = 4;
+struct MmaF8 {                       // v_mfma_f32_32x32x64_f8f6f4, both operands e4m3
+  static constexpr int KSTEP = 64, NR = 16;
   using Op = v8i;
-  using Acc = v4f;
-  // lane l: row l % 16, 32-byte chunk l / 16 of the 128-byte k-step
-  __device__ static Op load(const uint8_t* S, int row, int ks, int lane) {
-    const int c = 2 * (lane >> 4);
-    const v4i lo = *(const v4i*)(S + swz(row, c));
-    const v4i hi = *(const v4i*)(S + swz(row, c + 1));
+  using Acc = v16f;
+  // lane l: logical chunks 4*ks + 2*(l/32) + {0, 1} of its row
+  __device__ static int lane_off(int lane) { return ((2 * (lane >> 5)) ^ (lane & 7)) << 4; }
+  __device__ static Op load(const uint8_t* row, int off, int ks) {
+    const v4i lo = *(const v4i*)(row + (off ^ (ks << 6)));
+    const v4i hi = *(const v4i*)(row + ((off ^ 16) ^ (ks << 6)));
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ static Acc mma(const Op& a, const Op& b, const Acc& c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
-  __device__ static int op_row(int lane) { return lane & 15; }
-  __device__ static int out_row(int r, int lane) { return 4 * (lane >> 4) + r; }
-  __device__ static int out_col(int lane) { return lane & 15; }
 };
+// 32 x 32 output fragment layout (all 32x32 MFMAs): register r of lane l is
+// row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-template <int BM, int BN, class MM>
+template <int BM, int BN>
 struct Tile {
   static constexpr int TM = BM / 2, TN = BN / 2;            // wave tile
-  static constexpr int FM = TM / MM::F, FN = TN / MM::F;    // fragments per wave
-  static constexpr int ALOADS = BM * (kBK / 16) / kThreads;
+  static constexpr int FM = TM / 32, FN = TN / 32;          // 32x32 fragments per wave
+  static constexpr int ALOADS = BM * (kBK / 16) / kThreads;   // 16-byte chunks per thread
   static constexpr int BLOADS = BN * (kBK / 16) / kThreads;
-  static constexpr int STAGE = (BM + BN) * kBK;             // bytes per LDS stage
   static_assert(ALOADS >= 1 && BLOADS >= 1 && FM >= 1 && FN >= 1, "tile too small");
 };
 
@@ -102,53 +114,77 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int& tm, int& tn) 
 template <int BM, int BN, int KIND, int YDT>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   using MM = typename std::conditional<KIND == GEMM_FP8, MmaF8, MmaI8>::type;
-  using TL = Tile<BM, BN, MM>;
+  using TL = Tile<BM, BN>;
   using Acc = typename MM::Acc;
   constexpr int NR = MM::NR;
+  constexpr int KS = kBK / MM::KSTEP;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::STAGE];
+  // two LDS buffers as distinct objects, so the compiler can tell the buffer
+  // the DMA is filling from the one the fragment reads come from
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[BM * kBK], sb0[BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[BM * kBK], sb1[BN * kBK];
 
-  const int64_t M = g.M, N = g.N, K = g.K;
-  const int ntm = (int)((M + BM - 1) / BM), ntn = (int)((N + BN - 1) / BN);
+  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(ntm, ntn, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- global -> register -> LDS loader (16 bytes per thread per load)
-  v4i ra[TL::ALOADS], rb[TL::BLOADS];
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * kBK;
+  // ---- DMA loader.  One wave instruction fills 1 KB = 8 LDS rows; lane l
+  // lands at row l/8, physical chunk l%8, which holds logical chunk
+  // (l%8) ^ (row%8).  Rows past M (or N) re-read the last row: they only feed
+  // outputs that are never stored.
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ (lrow & 7);
+  uint32_t aoff[TL::ALOADS], boff[TL::BLOADS];
+#pragma unroll
+  for (int j = 0; j < TL::ALOADS; ++j) {
+    int gm = m0 + (j * (kThreads / 64) + wave) * 8 + lrow;
+    gm = gm < M ? gm : M - 1;
+    aoff[j] = (uint32_t)(gm * K + lchunk * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < TL::BLOADS; ++j) {
+    int gn = n0 + (j * (kThreads / 64) + wave) * 8 + lrow;
+    gn = gn < N ? gn : N - 1;
+    boff[j] = (uint32_t)(gn * K + lchunk * 16);
+  }
+  auto dma = [&](uint8_t* sa, uint8_t* sb, int k0) {
+    const uint8_t* abase = g.a + k0;
+    const uint8_t* bbase = g.b + k0;
+#pragma unroll
+    for (int j = 0; j < TL::ALOADS; ++j)
+      __builtin_amdgcn_global_load_lds((gptr_t)(abase + aoff[j]),
+                                       (lptr_t)(sa + (j * (kThreads / 64) + wave) * 8 * kBK), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < TL::BLOADS; ++j)
+      __builtin_amdgcn_global_load_lds((gptr_t)(bbase + boff[j]),
+                                       (lptr_t)(sb + (j * (kThreads / 64) + wave) * 8 * kBK), 16, 0, 0);
+  };
+  // Register loader for a last stage that K does not fill: chunks past K are
+  // zero so they add nothing to the dot products.
+  auto tail = [&](uint8_t* sa, uint8_t* sb, int k0) {
 #pragma unroll
     for (int j = 0; j < TL::ALOADS; ++j) {
       const int i = tid + j * kThreads, row = i >> 3, c = i & 7;
-      const int64_t gm = m0 + row, gk = k0 + c * 16;
-      ra[j] = (gm < M && gk < K) ? *(const v4i*)(g.a + gm * K + gk) : v4i{0, 0, 0, 0};
+      const int gm = (m0 + row) < M ? (m0 + row) : M - 1;
+      const int gk = k0 + c * 16;
+      *(v4i*)(sa + swz(row, c)) = gk < K ? *(const v4i*)(g.a + gm * K + gk) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < TL::BLOADS; ++j) {
       const int i = tid + j * kThreads, row = i >> 3, c = i & 7;
-      const int64_t gn = n0 + row, gk = k0 + c * 16;
-      rb[j] = (gn < N && gk < K) ? *(const v4i*)(g.b + gn * K + gk) : v4i{0, 0, 0, 0};
+      const int gn = (n0 + row) < N ? (n0 + row) : N - 1;
+      const int gk = k0 + c * 16;
+      *(v4i*)(sb + swz(row, c)) = gk < K ? *(const v4i*)(g.b + gn * K + gk) : v4i{0, 0, 0, 0};
     }
   };
-  auto sstore = [&](int buf) {
-    uint8_t* As = smem + buf * TL::STAGE;
-    uint8_t* Bs = As + BM * kBK;
-#pragma unroll
-    for (int j = 0; j < TL::ALOADS; ++j) {
-      const int i = tid + j * kThreads;
-      *(v4i*)(As + swz(i >> 3, i & 7)) = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < TL::BLOADS; ++j) {
-      const int i = tid + j * kThreads;
-      *(v4i*)(Bs + swz(i >> 3, i & 7)) = rb[j];
-    }
-  };
+  const int nfull = K / kBK;                 // stages filled by DMA
+  const bool ragged = (K % kBK) != 0;        // one more, partial stage at the end
 
   Acc acc[TL::FM][TL::FN];
 #pragma unroll
@@ -156,103 +192,137 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TL::FN; ++j) acc[i][j] = Acc{};
 
-  const int orow = MM::op_row(lane);
-  auto compute = [&](int buf) {
-    const uint8_t* As = smem + buf * TL::STAGE;
-    const uint8_t* Bs = As + BM * kBK;
+  // Byte offset of this lane's operand row in the A / B stage, and of its
+  // chunk inside the row.
+  const int arow = (wm * TL::TM + (lane & 31)) * kBK;
+  const int brow = (wn * TL::TN + (lane & 31)) * kBK;
+  const int loff = MM::lane_off(lane);
+  // B fragments are double buffered across k-steps; each A fragment is
+  // re-read for the next k-step right after its last MFMA of this one.
+  auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
+    const uint8_t* ar = As + arow;
+    const uint8_t* br = Bs + brow;
+    typename MM::Op af[TL::FM], bf[2][TL::FN];
 #pragma unroll
-    for (int ks = 0; ks < kBK / MM::KSTEP; ++ks) {
-      typename MM::Op af[TL::FM], bf[TL::FN];
+    for (int i = 0; i < TL::FM; ++i) af[i] = MM::load(ar + i * 32 * kBK, loff, 0);
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i) af[i] = MM::load(As, wm * TL::TM + i * MM::F + orow, ks, lane);
+    for (int j = 0; j < TL::FN; ++j) bf[0][j] = MM::load(br + j * 32 * kBK, loff, 0);
 #pragma unroll
-      for (int j = 0; j < TL::FN; ++j) bf[j] = MM::load(Bs, wn * TL::TN + j * MM::F + orow, ks, lane);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
+        for (int j = 0; j < TL::FN; ++j) bf[cur ^ 1][j] = MM::load(br + j * 32 * kBK, loff, ks + 1);
+      }
 #pragma unroll
-        for (int j = 0; j < TL::FN; ++j) acc[i][j] = MM::mma(af[i], bf[j], acc[i][j]);
+      for (int i = 0; i < TL::FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) acc[i][j] = MM::mma(af[i], bf[cur][j], acc[i][j]);
+        if (ks + 1 < KS) af[i] = MM::load(ar + i * 32 * kBK, loff, ks + 1);
+      }
     }
   };
+  auto stage_done = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA has landed
+    __syncthreads();                                   // ... and every other wave's
+  };
 
-  // ---- main loop: one barrier per stage
-  const int nk = (int)((K + kBK - 1) / kBK);
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    compute(kt & 1);
-    if (more) sstore((kt + 1) & 1);
-    __syncthreads();
+  // ---- main loop over the full stages, two per trip (buffer 0, buffer 1).
+  // Stage s lives in buffer s & 1.  On entry to a trip buffer 0 holds stage
+  // kt; the loop has a single exit so the accumulators stay in place.
+  int kt = 0;
+  if (nfull > 0) {
+    dma(sa0, sb0, 0);
+    stage_done();
+  }
+  for (; kt + 2 <= nfull; kt += 2) {
+    dma(sa1, sb1, (kt + 1) * kBK);
+    compute(sa0, sb0);
+    stage_done();
+    if (kt + 2 < nfull) dma(sa0, sb0, (kt + 2) * kBK);
+    compute(sa1, sb1);
+    stage_done();
+  }
+  if (kt < nfull) compute(sa0, sb0);   // odd number of full stages: the last is in buffer 0
+  // ---- the partial last stage, through registers (its buffer is free: it
+  // was last read two stages ago)
+  if (ragged) {
+    uint8_t* ta = (nfull & 1) ? sa1 : sa0;
+    uint8_t* tb = (nfull & 1) ? sb1 : sb0;
+    tail(ta, tb, nfull * kBK);
+    stage_done();
+    compute(ta, tb);
   }
 
-  // ---- epilogue: register r of fragment (i, j) is output
-  // (mw + i*F + out_row(r), nw + j*F + out_col)
-  const int64_t mw = m0 + wm * TL::TM, nw = n0 + wn * TL::TN;
-  const int ocol = MM::out_col(lane);
-  if constexpr (KIND == GEMM_FP8) {
+  // ---- epilogue.  Register r of fragment (i, j) is output
+  // (mw + i*32 + out_row(r), nw + j*32 + lane%32).  Row factors are loaded
+  // once per fragment row, column factors once per fragment.
+  const int mw = m0 + wm * TL::TM, nw = n0 + wn * TL::TN;
+  const int ocol = lane & 31;
+  const bool full = (m0 + BM <= M) && (n0 + BN <= N);
+  if constexpr (KIND == GEMM_FP8 || KIND == GEMM_INT8) {
 #pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-      const int64_t n = nw + j * MM::F + ocol;
-      if (n >= N) continue;
-      const float sb = g.b_scale[n];
-      const float bb = g.bias ? g.bias[n] : 0.0f;
+    for (int i = 0; i < TL::FM; ++i) {
+      float sx[NR];
+      int rs[NR];
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
+      for (int r = 0; r < NR; ++r) {
+        const int m = mw + i * 32 + out_row(r, lane);
+        const int mc = m < M ? m : M - 1;
+        sx[r] = g.a_scale[mc];
+        if constexpr (KIND == GEMM_INT8) rs[r] = g.a_rowsum[mc];
+      }
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int64_t m = mw + i * MM::F + MM::out_row(r, lane);
-          if (m < M) store_out<YDT>(g.y, m * N + n, acc[i][j][r] * (g.a_scale[m] * sb) + bb);
-        }
-    }
-  } else if constexpr (KIND == GEMM_INT8) {
-    // zero-point correction in int32, then fp32 scaling, stored at once
-#pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-      const int64_t n = nw + j * MM::F + ocol;
-      if (n >= N) continue;
-      const float sb = g.b_scale[n];
-      const int zb = (int)g.b_zp[n];
-      const float bb = g.bias ? g.bias[n] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
+      for (int j = 0; j < TL::FN; ++j) {
+        const int n = nw + j * 32 + ocol;
+        const int nc = n < N ? n : N - 1;
+        const float sb = g.b_scale[nc];
+        const float bb = g.bias ? g.bias[nc] : 0.0f;
+        int zb = 0;
+        if constexpr (KIND == GEMM_INT8) zb = (int)g.b_zp[nc];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          const int64_t m = mw + i * MM::F + MM::out_row(r, lane);
-          if (m < M) {
+          const int m = mw + i * 32 + out_row(r, lane);
+          if (!full && (m >= M || n >= N)) continue;
+          const int o = m * N + n;
+          float v;
+          if constexpr (KIND == GEMM_INT8) {
             const int a = acc[i][j][r];
-            if (g.acc_out) g.acc_out[m * N + n] = a;
-            const int c = a - zb * g.a_rowsum[m];
-            store_out<YDT>(g.y, m * N + n, (g.a_scale[m] * sb) * (float)c + bb);
+            if (g.acc_out) g.acc_out[o] = a;
+            v = (sx[r] * sb) * (float)(a - zb * rs[r]) + bb;
+          } else {
+            v = acc[i][j][r] * (sx[r] * sb) + bb;
           }
+          store_out<YDT>(g.y, o, v);
         }
+      }
     }
   } else {
     // LLM.int8: dequantize the int8 part in place (the fp32 value replaces
     // the int32 in the same registers), then add the outlier flow with
-    // v_mfma_f32_32x32x16_f16 whose accumulator input is that value.  Its
-    // output layout is the 32 x 32 layout of the int8 instruction.
+    // v_mfma_f32_32x32x16_f16 whose accumulator input is that value (its
+    // output layout is the same 32 x 32 layout).
 #pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-      const int64_t n = nw + j * MM::F + ocol;
-      const bool nok = n < N;
-      const float sb = nok ? g.b_scale[n] : 0.0f;
-      const int zb = nok ? (int)g.b_zp[n] : 0;
+    for (int i = 0; i < TL::FM; ++i) {
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
+      for (int j = 0; j < TL::FN; ++j) {
+        const int n = nw + j * 32 + ocol;
+        const int nc = n < N ? n : N - 1;
+        const float sb = g.b_scale[nc];
+        const int zb = (int)g.b_zp[nc];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          const int64_t m = mw + i * MM::F + MM::out_row(r, lane);
-          const bool ok = nok && m < M;
+          const int m = mw + i * 32 + out_row(r, lane);
+          const int mc = m < M ? m : M - 1;
           const int a = acc[i][j][r];
-          if (ok && g.acc_out) g.acc_out[m * N + n] = a;
-          const int c = a - zb * (ok ? g.a_rowsum[m] : 0);
-          acc[i][j][r] = __float_as_int((ok ? g.a_scale[m] * sb : 0.0f) * (float)c);
+          if (g.acc_out && m < M && n < N) g.acc_out[m * N + n] = a;
+          acc[i][j][r] = __float_as_int((g.a_scale[mc] * sb) * (float)(a - zb * g.a_rowsum[mc]));
         }
+      }
     }
     const int cnt = *g.out_cnt;
     const int kg = lane >> 5;                          // 8-column group of the 16-column step
+    const int orow = lane & 31;
     for (int kc = 0; kc < cnt; kc += 16) {
       int col[8];
 #pragma unroll
@@ -263,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
       v8h xo[TL::FM], wo[TL::FN];
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i) {
-        const int64_t m = mw + i * MM::F + orow;
+        const int m = mw + i * 32 + orow;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           xo[i][e] = (col[e] >= 0 && m < M) ? __builtin_bit_cast(_Float16, g.x_f16[m * K + col[e]])
@@ -271,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
       }
 #pragma unroll
       for (int j = 0; j < TL::FN; ++j) {
-        const int64_t n = nw + j * MM::F + orow;
+        const int n = nw + j * 32 + orow;
         const bool nok = n < N;
         const float sb = nok ? g.b_scale[n] : 0.0f;
         const float zb = nok ? g.b_zp[n] : 0.0f;
@@ -293,14 +363,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
     }
 #pragma unroll
     for (int j = 0; j < TL::FN; ++j) {
-      const int64_t n = nw + j * MM::F + ocol;
+      const int n = nw + j * 32 + ocol;
       if (n >= N) continue;
       const float bb = g.bias ? g.bias[n] : 0.0f;
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          const int64_t m = mw + i * MM::F + MM::out_row(r, lane);
+          const int m = mw + i * 32 + out_row(r, lane);
           if (m < M) store_out<YDT>(g.y, m * N + n, __int_as_float(acc[i][j][r]) + bb);
         }
     }
