@@ -13,19 +13,21 @@
 //                     accumulation, y = S_a[m] S_b[n] acc (+ bias)
 //
 // Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile; each wave
-// owns (BM/2) x (BN/2) built from 32 x 32 MFMA fragments.  K advances 128
-// bytes per stage.  Stages are double buffered in LDS and filled by
-// global_load_lds_dwordx4 (global -> LDS without registers): while the MFMAs
-// consume one buffer the next stage streams into the other.  Within a stage
-// the B fragments of k-step s+1 are read from LDS while the MFMAs of k-step s
-// run, and each A fragment is re-read right after its last use.
+// owns (BM/2) x (BN/2) built from 32 x 32 MFMA fragments.  K advances 64
+// bytes per stage.  Four LDS buffers hold four stages, filled by
+// global_load_lds_dwordx4 (global -> LDS without registers) three stages
+// ahead of the MFMAs, so a stage's loads have three stages of compute to
+// arrive.  Within a stage the B fragments of k-step s+1 are read from LDS while
+// the MFMAs of k-step s run, and each A fragment is re-read right after its
+// last use.
 //
-// LDS layout: row-major 128-byte rows (one row of the tile, one stage of K),
-// the 16-byte chunk c of row r stored at chunk position c ^ (r & 7).  A
-// fragment read has rows 0..7 of one logical chunk in one LDS cycle, and the
-// XOR puts them in 8 distinct bank groups.  The DMA writes 64 consecutive
-// 16-byte slots per wave instruction, so the swizzle is applied on the global
-// side: each lane fetches the chunk that belongs at its fixed slot.
+// LDS layout: row-major 64-byte rows (one row of the tile, one stage of K),
+// the 16-byte chunk c of row r stored at chunk position c ^ ((r >> 1) & 3).
+// A fragment read has rows 0..7 of one logical chunk in one LDS cycle; even
+// and odd rows fall in different halves of the banks and the XOR spreads the
+// four row pairs over the four bank groups of each half.  The DMA writes 64
+// consecutive 16-byte slots per wave instruction, so the swizzle is applied
+// on the global side: each lane fetches the chunk that belongs at its slot.
 //
 // Workgroups are renumbered so consecutive tiles land on the same XCD (the
 // dispatcher deals workgroups round-robin over the 8 XCDs) and, within an
@@ -41,16 +43,17 @@ namespace {
 typedef __attribute__((address_space(1))) void* gptr_t;   // global (DMA source)
 typedef __attribute__((address_space(3))) void* lptr_t;   // LDS (DMA destination)
 
-constexpr int kBK = 128;            // bytes of K per stage
+constexpr int kBK = 64;             // bytes of K per stage
+constexpr int kStages = 4;          // LDS buffers (prefetch distance kStages - 1)
 constexpr int kThreads = 256;       // 4 waves
 constexpr int kGroupM = 4;          // tile-rows per L2 group
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
 // One MFMA shape.  A fragment row is (base multiple of 32) + lane % 32, so
-// (row & 7) == (lane & 7) and the swizzled byte offset of the lane's operand
-// inside its LDS row is lane_off(lane) XOR a per-k-step constant.
+// ((row >> 1) & 3) == ((lane >> 1) & 3) and the swizzled byte offset of the
+// lane's operand inside its LDS row is lane_off(lane) XOR a per-k-step constant.
 // A and B fragments use the same lane -> k mapping, so each instruction sums
 // over exactly the k bytes of its step whatever order the hardware uses.
 struct MmaI8 {                       // v_mfma_i32_32x32x32_i8
@@ -58,7 +61,7 @@ struct MmaI8 {                       // v_mfma_i32_32x32x32_i8
   using Op = v4i;
   using Acc = v16i;
   // lane l: 16-byte logical chunk 2*ks + l/32 of its row
-  __device__ static int lane_off(int lane) { return ((lane >> 5) ^ (lane & 7)) << 4; }
+  __device__ static int lane_off(int lane) { return ((lane >> 5) ^ ((lane >> 1) & 3)) << 4; }
   __device__ static Op load(const uint8_t* row, int off, int ks) {
     return *(const v4i*)(row + (off ^ (ks << 5)));
   }
@@ -71,7 +74,7 @@ struct MmaF8 {                       // v_mfma_f32_32x32x64_f8f6f4, both operand
   using Op = v8i;
   using Acc = v16f;
   // lane l: logical chunks 4*ks + 2*(l/32) + {0, 1} of its row
-  __device__ static int lane_off(int lane) { return ((2 * (lane >> 5)) ^ (lane & 7)) << 4; }
+  __device__ static int lane_off(int lane) { return ((2 * (lane >> 5)) ^ ((lane >> 1) & 3)) << 4; }
   __device__ static Op load(const uint8_t* row, int off, int ks) {
     const v4i lo = *(const v4i*)(row + (off ^ (ks << 6)));
     const v4i hi = *(const v4i*)(row + ((off ^ 16) ^ (ks << 6)));
@@ -91,6 +94,7 @@ struct Tile {
   static constexpr int FM = TM / 32, FN = TN / 32;          // 32x32 fragments per wave
   static constexpr int ALOADS = BM * (kBK / 16) / kThreads;   // 16-byte chunks per thread
   static constexpr int BLOADS = BN * (kBK / 16) / kThreads;
+  static constexpr int LOADS = ALOADS + BLOADS;               // DMA instructions per wave per stage
   static_assert(ALOADS >= 1 && BLOADS >= 1 && FM >= 1 && FN >= 1, "tile too small");
 };
 
@@ -119,10 +123,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   constexpr int NR = MM::NR;
   constexpr int KS = kBK / MM::KSTEP;
 
-  // two LDS buffers as distinct objects, so the compiler can tell the buffer
+  // the LDS buffers as distinct objects, so the compiler can tell the buffers
   // the DMA is filling from the one the fragment reads come from
   __shared__ __attribute__((aligned(16))) uint8_t sa0[BM * kBK], sb0[BN * kBK];
   __shared__ __attribute__((aligned(16))) uint8_t sa1[BM * kBK], sb1[BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sa2[BM * kBK], sb2[BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t sa3[BM * kBK], sb3[BN * kBK];
 
   const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
@@ -134,22 +140,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- DMA loader.  One wave instruction fills 1 KB = 8 LDS rows; lane l
-  // lands at row l/8, physical chunk l%8, which holds logical chunk
-  // (l%8) ^ (row%8).  Rows past M (or N) re-read the last row: they only feed
-  // outputs that are never stored.
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ (lrow & 7);
+  // ---- DMA loader.  One wave instruction fills 1 KB = 16 LDS rows; lane l
+  // lands at row l/4, physical chunk l%4, which holds logical chunk
+  // (l%4) ^ ((row >> 1) & 3).  Rows past M (or N) re-read the last row: they
+  // only feed outputs that are never stored.
+  constexpr int kRowsPerDma = 64 * 16 / kBK;     // 16
+  const int lrow = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
   uint32_t aoff[TL::ALOADS], boff[TL::BLOADS];
 #pragma unroll
   for (int j = 0; j < TL::ALOADS; ++j) {
-    int gm = m0 + (j * (kThreads / 64) + wave) * 8 + lrow;
+    int gm = m0 + (j * (kThreads / 64) + wave) * kRowsPerDma + lrow;
     gm = gm < M ? gm : M - 1;
     aoff[j] = (uint32_t)(gm * K + lchunk * 16);
   }
 #pragma unroll
   for (int j = 0; j < TL::BLOADS; ++j) {
-    int gn = n0 + (j * (kThreads / 64) + wave) * 8 + lrow;
+    int gn = n0 + (j * (kThreads / 64) + wave) * kRowsPerDma + lrow;
     gn = gn < N ? gn : N - 1;
     boff[j] = (uint32_t)(gn * K + lchunk * 16);
   }
@@ -159,25 +166,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TL::ALOADS; ++j)
       __builtin_amdgcn_global_load_lds((gptr_t)(abase + aoff[j]),
-                                       (lptr_t)(sa + (j * (kThreads / 64) + wave) * 8 * kBK), 16, 0, 0);
+                                       (lptr_t)(sa + (j * (kThreads / 64) + wave) * kRowsPerDma * kBK), 16,
+                                       0, 0);
 #pragma unroll
     for (int j = 0; j < TL::BLOADS; ++j)
       __builtin_amdgcn_global_load_lds((gptr_t)(bbase + boff[j]),
-                                       (lptr_t)(sb + (j * (kThreads / 64) + wave) * 8 * kBK), 16, 0, 0);
+                                       (lptr_t)(sb + (j * (kThreads / 64) + wave) * kRowsPerDma * kBK), 16,
+                                       0, 0);
   };
   // Register loader for a last stage that K does not fill: chunks past K are
   // zero so they add nothing to the dot products.
   auto tail = [&](uint8_t* sa, uint8_t* sb, int k0) {
 #pragma unroll
     for (int j = 0; j < TL::ALOADS; ++j) {
-      const int i = tid + j * kThreads, row = i >> 3, c = i & 7;
+      const int i = tid + j * kThreads, row = i >> 2, c = i & 3;
       const int gm = (m0 + row) < M ? (m0 + row) : M - 1;
       const int gk = k0 + c * 16;
       *(v4i*)(sa + swz(row, c)) = gk < K ? *(const v4i*)(g.a + gm * K + gk) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < TL::BLOADS; ++j) {
-      const int i = tid + j * kThreads, row = i >> 3, c = i & 7;
+      const int i = tid + j * kThreads, row = i >> 2, c = i & 3;
       const int gn = (n0 + row) < N ? (n0 + row) : N - 1;
       const int gk = k0 + c * 16;
       *(v4i*)(sb + swz(row, c)) = gk < K ? *(const v4i*)(g.b + gn * K + gk) : v4i{0, 0, 0, 0};
@@ -222,35 +231,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
       }
     }
   };
-  auto stage_done = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's DMA has landed
-    __syncthreads();                                   // ... and every other wave's
+  // ---- main loop.  Stage s lives in buffer s % 4 and is requested three
+  // stages ahead.  Before computing stage s a wave waits until at most the
+  // DMA of stages s+1, s+2 is outstanding (its own loads retire in order),
+  // then the barrier makes every wave's copy of stage s visible and proves
+  // that stage s-1's buffer, refilled next with stage s+3, has been read.
+  auto wait_stage = [&](int s) {
+    const int later = (nfull - 1 - s) < 2 ? (nfull - 1 - s) : 2;   // stages issued after s
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * TL::LOADS) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TL::LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   };
-
-  // ---- main loop over the full stages, two per trip (buffer 0, buffer 1).
-  // Stage s lives in buffer s & 1.  On entry to a trip buffer 0 holds stage
-  // kt; the loop has a single exit so the accumulators stay in place.
+  auto stage = [&](int s, const uint8_t* ca, const uint8_t* cb, uint8_t* na, uint8_t* nb) {
+    wait_stage(s);
+    if (s + 3 < nfull) dma(na, nb, (s + 3) * kBK);
+    compute(ca, cb);
+  };
+  if (nfull > 0) dma(sa0, sb0, 0);
+  if (nfull > 1) dma(sa1, sb1, kBK);
+  if (nfull > 2) dma(sa2, sb2, 2 * kBK);
   int kt = 0;
-  if (nfull > 0) {
-    dma(sa0, sb0, 0);
-    stage_done();
+  for (; kt + 4 <= nfull; kt += 4) {          // single exit: the accumulators stay in place
+    stage(kt, sa0, sb0, sa3, sb3);
+    stage(kt + 1, sa1, sb1, sa0, sb0);
+    stage(kt + 2, sa2, sb2, sa1, sb1);
+    stage(kt + 3, sa3, sb3, sa2, sb2);
   }
-  for (; kt + 2 <= nfull; kt += 2) {
-    dma(sa1, sb1, (kt + 1) * kBK);
-    compute(sa0, sb0);
-    stage_done();
-    if (kt + 2 < nfull) dma(sa0, sb0, (kt + 2) * kBK);
-    compute(sa1, sb1);
-    stage_done();
-  }
-  if (kt < nfull) compute(sa0, sb0);   // odd number of full stages: the last is in buffer 0
-  // ---- the partial last stage, through registers (its buffer is free: it
-  // was last read two stages ago)
+  if (kt < nfull) stage(kt, sa0, sb0, sa3, sb3);
+  if (kt + 1 < nfull) stage(kt + 1, sa1, sb1, sa0, sb0);
+  if (kt + 2 < nfull) stage(kt + 2, sa2, sb2, sa1, sb1);
+  // ---- the partial last stage, through registers, in buffer nfull % 4 (last
+  // read by stage nfull - 4, long finished)
   if (ragged) {
-    uint8_t* ta = (nfull & 1) ? sa1 : sa0;
-    uint8_t* tb = (nfull & 1) ? sb1 : sb0;
+    const int b = nfull & 3;
+    uint8_t* ta = b == 0 ? sa0 : b == 1 ? sa1 : b == 2 ? sa2 : sa3;
+    uint8_t* tb = b == 0 ? sb0 : b == 1 ? sb1 : b == 2 ? sb2 : sb3;
+    __syncthreads();                          // every wave is past stage nfull - 4
     tail(ta, tb, nfull * kBK);
-    stage_done();
+    __syncthreads();
     compute(ta, tb);
   }
 

@@ -12,7 +12,10 @@
 //     take each row's absmax, and write the int8 codes of the segment to LDS
 //     together with the per-row code sum.
 // Loads of one wave retire in order, so giving the weight stream and the
-// activation reads to different waves is what lets them overlap.
+// activation reads to different waves is what lets them overlap; the weight
+// loads are unconditional (clamped addresses) so nothing makes a streamer wait
+// for them before the MFMAs.  Code positions past K and rows past M are zero
+// in LDS, so whatever the clamped weight loads bring there adds nothing.
 // The four streamers' partial INT32 tiles are summed through LDS and one wave
 // applies the epilogue y = S_x S_w (acc - Z_w sum_k q_x) (+ bias).
 #include "q8_device.hpp"
@@ -37,6 +40,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
                                                          int32_t* __restrict__ acc_out) {
   constexpr int E = Chunk<DT>::kElems;
   constexpr int esz = (DT == DT_F32) ? 4 : 2;
+  constexpr int CPL = kSeg / E / 64;    // chunks per lane for one row-segment
   __shared__ __attribute__((aligned(16))) int8_t xs[kRows * kXStride];
   __shared__ float sx[kRows];
   __shared__ int rsum[kRows];
@@ -47,38 +51,97 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   const int64_t n0 = (int64_t)blockIdx.x * kRows;
   const char* xb = (const char*)x;
 
-  // ---- streamers: put every weight load of a K segment in flight at once
+  // ---- streamers: every weight load of a K segment in flight at once
   v4i wv[kStepsPerWave];
+  const int64_t wrow = (n0 + lr < N ? n0 + lr : N - 1) * K;
   auto issue = [&](int64_t k0) {
     const int seg = (int)((K - k0) < kSeg ? (K - k0) : kSeg);
-    const int64_t n = n0 + lr;
 #pragma unroll
     for (int j = 0; j < kStepsPerWave; ++j) {
-      const int kk = (wave + j * kStreamers) * 64 + lg * 16;
-      wv[j] = (kk < seg && n < N) ? *(const v4i*)(wq + n * K + k0 + kk) : v4i{0, 0, 0, 0};
+      int kk = (wave + j * kStreamers) * 64 + lg * 16;
+      kk = kk < seg ? kk : seg - 16;
+      wv[j] = *(const v4i*)(wq + wrow + k0 + kk);
     }
   };
 
+  // ---- quantizers: one row-segment of X is CPL chunks per lane
+  auto load_seg = [&](int m, int64_t k0, int seg, v4i* ch) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      ch[j] = c < seg / E ? *(const v4i*)(xb + ((int64_t)m * K + k0 + (int64_t)c * E) * esz)
+                          : v4i{0, 0, 0, 0};
+    }
+  };
+  auto seg_absmax = [&](const v4i* ch) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      float v[E];
+      Chunk<DT>::decode(ch[j], v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+    return amax;
+  };
+  // codes of one row-segment into LDS; returns this lane's code sum.  For
+  // 16-bit inputs the quotient comes from two FMAs on RN(1/s) (same codes as
+  // the division for a scale taken from the row absmax).
+  auto seg_codes = [&](int m, int seg, const v4i* ch, float s, float r) {
+    int qsum = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c < seg / E) {
+        float v[E];
+        Chunk<DT>::decode(ch[j], v);
+        uint32_t words[E / 4];
+#pragma unroll
+        for (int gq = 0; gq < E / 4; ++gq) {
+          uint32_t b[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float xv = v[4 * gq + e];
+            b[e] = rne_int8_bits(DT == DT_F32 ? xv / s : quot_fma(xv, s, r));
+          }
+          words[gq] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
+          qsum = sum_i8x4(words[gq], qsum);
+        }
+        if constexpr (E == 8) {
+          *(v2i*)(xs + m * kXStride + c * E) = v2i{(int)words[0], (int)words[1]};
+        } else {
+          *(uint32_t*)(xs + m * kXStride + c * E) = words[0];
+        }
+      }
+    }
+    return qsum;
+  };
+
+  const int qw = wave - kStreamers;
+  const bool one_seg = K <= kSeg;
+  v4i cur[CPL];
   if (wave < kStreamers) {
     issue(0);
   } else {
-    // ---- quantizers: per-row absmax over the whole row, then the scale
-    const int qw = wave - kStreamers;
-    for (int m = qw; m < kRows; m += kQuantizers) {
-      float amax = 0.0f;
-      if (m < M) {
-        const int64_t nch = K / E;
-        for (int64_t c = lane; c < nch; c += 64) {
-          float v[E];
-          Chunk<DT>::decode(*(const v4i*)(xb + ((int64_t)m * K + c * E) * esz), v);
-#pragma unroll
-          for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    // rows M..15 of the code buffer stay zero for every segment
+    for (int i = qw * 64 + lane; i < (kRows - M) * (kSeg / 16); i += kQuantizers * 64) {
+      const int m = M + i / (kSeg / 16), c = i % (kSeg / 16);
+      *(v4i*)(xs + m * kXStride + c * 16) = v4i{0, 0, 0, 0};
+    }
+    if (!one_seg) {
+      // per-row absmax over every segment of the row
+      for (int m = qw; m < M; m += kQuantizers) {
+        float amax = 0.0f;
+        for (int64_t k0 = 0; k0 < K; k0 += kSeg) {
+          const int seg = (int)((K - k0) < kSeg ? (K - k0) : kSeg);
+          load_seg(m, k0, seg, cur);
+          amax = fmaxf(amax, seg_absmax(cur));
         }
         amax = wave_max(amax);
+        float s = amax / 127.0f;
+        s = s < kEps ? kEps : s;
+        if (lane == 0) { sx[m] = s; rsum[m] = 0; }
       }
-      float s = amax / 127.0f;
-      s = s < kEps ? kEps : s;
-      if (lane == 0) { sx[m] = s; rsum[m] = 0; }
     }
   }
 
@@ -87,50 +150,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     const int seg = (int)((K - k0) < kSeg ? (K - k0) : kSeg);
     __syncthreads();   // the previous segment's codes have been consumed
     if (wave >= kStreamers) {
-      // ---- quantizers: codes of this segment into LDS, row sums
-      const int qw = wave - kStreamers;
-      for (int m = qw; m < kRows; m += kQuantizers) {
-        int qsum = 0;
-        const float s = sx[m];
-        for (int c = lane; c < seg / E; c += 64) {
-          float v[E];
-          if (m < M) {
-            Chunk<DT>::decode(*(const v4i*)(xb + ((int64_t)m * K + k0 + (int64_t)c * E) * esz), v);
-          } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e) v[e] = 0.0f;
-          }
-          uint32_t words[E / 4];
-#pragma unroll
-          for (int gq = 0; gq < E / 4; ++gq) {
-            int q[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              q[e] = code_sym_i8(v[4 * gq + e], s);
-              qsum += q[e];
-            }
-            words[gq] = pack4_i8(q[0], q[1], q[2], q[3]);
-          }
-          if constexpr (E == 8) {
-            *(v2i*)(xs + m * kXStride + c * E) = v2i{(int)words[0], (int)words[1]};
-          } else {
-            *(uint32_t*)(xs + m * kXStride + c * E) = words[0];
-          }
+      // a partial segment: code positions past K are zero
+      if (seg < kSeg) {
+        for (int m = qw; m < M; m += kQuantizers)
+          for (int b = seg + lane * 16; b < kSeg; b += 64 * 16) *(v4i*)(xs + m * kXStride + b) = v4i{0, 0, 0, 0};
+      }
+      // rows of this wave, the next row's loads in flight while one is coded
+      v4i nxt[CPL];
+      if (qw < M) load_seg(qw, k0, seg, cur);
+      for (int m = qw; m < M; m += kQuantizers) {
+        if (m + kQuantizers < M) load_seg(m + kQuantizers, k0, seg, nxt);
+        float s;
+        if (one_seg) {
+          const float amax = wave_max(seg_absmax(cur));
+          s = amax / 127.0f;
+          s = s < kEps ? kEps : s;
+        } else {
+          s = sx[m];
         }
-        qsum = wave_sum(qsum);
-        if (lane == 0) rsum[m] += qsum;
+        const float r = 1.0f / s;
+        const int qsum = wave_sum(seg_codes(m, seg, cur, s, r));
+        if (lane == 0) {
+          if (one_seg) { sx[m] = s; rsum[m] = qsum; }
+          else rsum[m] += qsum;
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) cur[j] = nxt[j];
       }
     }
     __syncthreads();   // the codes of this segment are in LDS
     if (wave < kStreamers) {
-      const int nsteps = (seg + 63) / 64;
 #pragma unroll
       for (int j = 0; j < kStepsPerWave; ++j) {
         const int st = wave + j * kStreamers;
-        if (st < nsteps) {
-          const v4i xv = *(const v4i*)(xs + lr * kXStride + st * 64 + lg * 16);
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[j], xv, acc, 0, 0, 0);
-        }
+        const v4i xv = *(const v4i*)(xs + lr * kXStride + st * 64 + lg * 16);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[j], xv, acc, 0, 0, 0);
       }
       if (k0 + kSeg < K) issue(k0 + kSeg);
     }

@@ -131,6 +131,37 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
   return r;
 }
 
+// The quotient x / s rounded to binary32, from r = RN(1/s) with two FMAs
+// (y0 = x r, e = x - s y0 exactly, y1 = y0 + e r).  Used for 16-bit inputs with
+// a scale derived from the row absmax: over that whole domain the int8 and
+// e4m3 codes taken from y1 equal those of the correctly rounded quotient
+// (verified exhaustively on the host for every bf16 / fp16 x and absmax).
+__device__ __forceinline__ float quot_fma(float x, float s, float r) {
+#pragma clang fp contract(off)
+  const float y0 = x * r;
+  const float e = __builtin_fmaf(-s, y0, x);
+  return __builtin_fmaf(e, r, y0);
+}
+
+// Round-to-nearest-even to an integer by adding 1.5 * 2^23: for |y| < 2^22 the
+// low byte of the sum's bit pattern is rne(y) as a two's-complement int8.
+__device__ __forceinline__ uint32_t rne_int8_bits(float y) {
+#pragma clang fp contract(off)
+  return __float_as_uint(y + 12582912.0f);
+}
+
+// Low bytes of four words, packed little-endian into one word (v_perm_b32).
+__device__ __forceinline__ uint32_t pack_lo_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Sum of the four signed bytes of a packed word, added to acc (v_dot4_i32_i8).
+__device__ __forceinline__ int sum_i8x4(uint32_t packed, int acc) {
+  return __builtin_amdgcn_sdot4((int)packed, 0x01010101, acc, false);
+}
+
 // Symmetric int8 code: clamp(rne(x / s), -127, 127) with IEEE division.
 __device__ __forceinline__ int code_sym_i8(float x, float s) {
   float q = __builtin_rintf(x / s);

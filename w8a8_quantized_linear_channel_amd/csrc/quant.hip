@@ -2,11 +2,16 @@
 // and per-token activations (INT8 symmetric with the code row-sum, FP8 e4m3
 // with the activation-scale upper bound).
 //
-// One 256-thread workgroup per row.  Each thread reads 16-byte chunks
-// (coalesced across the workgroup), keeps up to kCache chunks in registers
-// so the row is read from HBM once, reduces min/max/absmax with wave
-// shuffles + LDS, then emits codes from the registers.  HBM-bound: per row it
-// moves K*sizeof(in) bytes in and K bytes (+ 8 B of metadata) out.
+// Weights (offline, once per model): one 256-thread workgroup per row, IEEE
+// division for every code.  Activations (every forward, HBM-bound): one wave
+// per row, four rows per 256-thread workgroup, no workgroup barriers; each
+// lane keeps its 16-byte chunks of the row in registers so the row is read
+// from HBM once, the absmax is a wave reduction, and the codes are emitted
+// from the registers.  For 16-bit inputs the quotient x / S comes from two
+// FMAs on RN(1/S) (same codes as the division over that whole input domain),
+// the integer rounding from adding 1.5 * 2^23, the byte packing from v_perm
+// and the code row sum from v_dot4.  Per row: K * sizeof(in) bytes in, K
+// bytes + 8 bytes of metadata out.
 #include "q8_device.hpp"
 #include "q8_kernels.hpp"
 
@@ -104,82 +109,100 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight_i8(const void* __rest
   if (tid == 0) { w_scale[n] = s; w_zp[n] = z; }
 }
 
+// ---------------------------------------------------------------- one wave per row
+constexpr int kRowsPerBlock = kThreads / 64;
+
+// Chunk loads for a row handled by one wave: lane l owns chunks l, l+64, ...
+// of which the first CACHE stay in registers.
+template <int DT, int CACHE>
+struct WaveRow {
+  static constexpr int E = Chunk<DT>::kElems;
+  v4i cache[CACHE];
+  template <class F>
+  __device__ __forceinline__ void load(const void* base, int64_t row, int nch, int lane, F&& each) {
+#pragma unroll
+    for (int j = 0; j < CACHE; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nch) {
+        cache[j] = load_chunk<DT>(base, row, c);
+        each(cache[j], c);
+      }
+    }
+    for (int c = lane + 64 * CACHE; c < nch; c += 64) each(load_chunk<DT>(base, row, c), c);
+  }
+  template <class F>
+  __device__ __forceinline__ void replay(const void* base, int64_t row, int nch, int lane, F&& each) {
+#pragma unroll
+    for (int j = 0; j < CACHE; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nch) each(cache[j], c);
+    }
+    for (int c = lane + 64 * CACHE; c < nch; c += 64) each(load_chunk<DT>(base, row, c), c);
+  }
+};
+
 // ---------------------------------------------------------------- rows -> FP8 e4m3 (weights and activations)
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_quant_rows_fp8(const void* __restrict__ x, int64_t K,
+// bound: activation scale upper bound on the row absmax (+inf for none).
+template <int DT, int CACHE>
+__global__ __launch_bounds__(kThreads) void k_quant_rows_fp8(const void* __restrict__ x, int64_t R, int64_t K,
                                                              float bound, uint8_t* __restrict__ xq,
                                                              float* __restrict__ x_scale) {
   constexpr int E = Chunk<DT>::kElems;
-  __shared__ float red[kWaves];
-  const int64_t m = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (m >= R) return;                                  // whole wave
   const int nch = (int)(K / E);
   const int64_t row = m * K;
-
-  v4i cache[kCache];
+  WaveRow<DT, CACHE> wr;
   float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kCache; ++j) {
-    const int c = tid + j * kThreads;
-    if (c < nch) {
-      cache[j] = load_chunk<DT>(x, row, c);
-      float v[E];
-      Chunk<DT>::decode(cache[j], v);
-#pragma unroll
-      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    }
-  }
-  for (int c = tid + kCache * kThreads; c < nch; c += kThreads) {
+  wr.load(x, row, nch, lane, [&](const v4i& ch, int) {
     float v[E];
-    Chunk<DT>::decode(load_chunk<DT>(x, row, c), v);
+    Chunk<DT>::decode(ch, v);
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  }
-  amax = block_max<kWaves>(amax, red);
-  amax = fminf(amax, bound);            // bound = +inf when there is none
-  float s = amax / kFp8Max;
+  });
+  amax = wave_max(amax);
+  const float a = fminf(amax, bound);
+  float s = a / kFp8Max;
   s = s < kEps ? kEps : s;
-
-  auto emit = [&](const v4i& ch, int c) {
+  const float r = 1.0f / s;
+  // the two-FMA quotient is used where the scale comes from a 16-bit row absmax
+  const bool fast = (DT != DT_F32) && (amax <= bound);
+  wr.replay(x, row, nch, lane, [&](const v4i& ch, int c) {
     float v[E];
     Chunk<DT>::decode(ch, v);
     uint32_t words[E / 4];
 #pragma unroll
     for (int g = 0; g < E / 4; ++g) {
-      float r[4];
+      float q[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = fminf(fmaxf(v[4 * g + e] / s, -kFp8Max), kFp8Max);
-      words[g] = pack4_e4m3(r[0], r[1], r[2], r[3]);
+      for (int e = 0; e < 4; ++e) {
+        const float xv = v[4 * g + e];
+        const float y = fast ? __builtin_copysignf(quot_fma(xv, s, r), xv) : xv / s;
+        q[e] = fminf(fmaxf(y, -kFp8Max), kFp8Max);
+      }
+      words[g] = pack4_e4m3(q[0], q[1], q[2], q[3]);
     }
     store_codes<E>(xq, row + (int64_t)c * E, words);
-  };
-#pragma unroll
-  for (int j = 0; j < kCache; ++j) {
-    const int c = tid + j * kThreads;
-    if (c < nch) emit(cache[j], c);
-  }
-  for (int c = tid + kCache * kThreads; c < nch; c += kThreads) emit(load_chunk<DT>(x, row, c), c);
-
-  if (tid == 0) x_scale[m] = s;
+  });
+  if (lane == 0) x_scale[m] = s;
 }
 
 // ---------------------------------------------------------------- activations, INT8 sym (+ row sum)
 // colflag (nullable, [K] bytes): nonzero marks a column whose values are
 // treated as 0 (the outlier columns of the mixed-precision decomposition).
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_quant_act_i8(const void* __restrict__ x, int64_t K,
+template <int DT, int CACHE>
+__global__ __launch_bounds__(kThreads) void k_quant_act_i8(const void* __restrict__ x, int64_t M, int64_t K,
                                                            const uint8_t* __restrict__ colflag,
                                                            int8_t* __restrict__ xq,
                                                            float* __restrict__ x_scale,
                                                            int32_t* __restrict__ x_rowsum) {
   constexpr int E = Chunk<DT>::kElems;
-  __shared__ float red[kWaves];
-  __shared__ int redi[kWaves];
-  const int64_t m = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (m >= M) return;                                  // whole wave
   const int nch = (int)(K / E);
   const int64_t row = m * K;
-
   auto decode_masked = [&](const v4i& ch, int c, float* v) {
     Chunk<DT>::decode(ch, v);
     if (colflag != nullptr) {
@@ -189,56 +212,41 @@ __global__ __launch_bounds__(kThreads) void k_quant_act_i8(const void* __restric
         if (f[e]) v[e] = 0.0f;
     }
   };
-
-  v4i cache[kCache];
+  WaveRow<DT, CACHE> wr;
   float amax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kCache; ++j) {
-    const int c = tid + j * kThreads;
-    if (c < nch) {
-      cache[j] = load_chunk<DT>(x, row, c);
-      float v[E];
-      decode_masked(cache[j], c, v);
-#pragma unroll
-      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    }
-  }
-  for (int c = tid + kCache * kThreads; c < nch; c += kThreads) {
+  wr.load(x, row, nch, lane, [&](const v4i& ch, int c) {
     float v[E];
-    decode_masked(load_chunk<DT>(x, row, c), c, v);
+    decode_masked(ch, c, v);
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  }
-  amax = block_max<kWaves>(amax, red);
+  });
+  amax = wave_max(amax);
   float s = amax / 127.0f;
   s = s < kEps ? kEps : s;
-
+  const float r = 1.0f / s;
   int qsum = 0;
-  auto emit = [&](const v4i& ch, int c) {
+  // |x / s| <= 127 (s = absmax/127 rounded, or the 1e-8 floor), so the codes
+  // need no clamp and the 1.5 * 2^23 rounding applies.
+  wr.replay(x, row, nch, lane, [&](const v4i& ch, int c) {
     float v[E];
     decode_masked(ch, c, v);
     uint32_t words[E / 4];
 #pragma unroll
     for (int g = 0; g < E / 4; ++g) {
-      int q[4];
+      uint32_t b[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        q[e] = code_sym_i8(v[4 * g + e], s);
-        qsum += q[e];
+        const float xv = v[4 * g + e];
+        const float y = (DT == DT_F32) ? xv / s : quot_fma(xv, s, r);
+        b[e] = rne_int8_bits(y);
       }
-      words[g] = pack4_i8(q[0], q[1], q[2], q[3]);
+      words[g] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
+      qsum = sum_i8x4(words[g], qsum);
     }
     store_codes<E>(xq, row + (int64_t)c * E, words);
-  };
-#pragma unroll
-  for (int j = 0; j < kCache; ++j) {
-    const int c = tid + j * kThreads;
-    if (c < nch) emit(cache[j], c);
-  }
-  for (int c = tid + kCache * kThreads; c < nch; c += kThreads) emit(load_chunk<DT>(x, row, c), c);
-
-  qsum = block_sum<kWaves>(qsum, redi);
-  if (tid == 0) {
+  });
+  qsum = wave_sum(qsum);
+  if (lane == 0) {
     x_scale[m] = s;
     if (x_rowsum) x_rowsum[m] = qsum;
   }
@@ -259,22 +267,44 @@ hipError_t launch_quant_weight_i8(const void* w, int dt, int64_t N, int64_t K, i
 
 hipError_t launch_quant_rows_fp8(const void* x, int dt, int64_t R, int64_t K, float bound,
                                  uint8_t* xq, float* x_scale, hipStream_t st) {
-  dim3 grid((unsigned)R), block(kThreads);
+  dim3 grid((unsigned)((R + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
+  const int64_t per_lane = K / (dt == DT_F32 ? 4 : 8) / 64;
+  const bool big = per_lane > 8;
   switch (dt) {
-    case DT_F32: k_quant_rows_fp8<DT_F32><<<grid, block, 0, st>>>(x, K, bound, xq, x_scale); break;
-    case DT_F16: k_quant_rows_fp8<DT_F16><<<grid, block, 0, st>>>(x, K, bound, xq, x_scale); break;
-    default: k_quant_rows_fp8<DT_BF16><<<grid, block, 0, st>>>(x, K, bound, xq, x_scale); break;
+    case DT_F32:
+      if (big) k_quant_rows_fp8<DT_F32, 32><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
+      else k_quant_rows_fp8<DT_F32, 8><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
+      break;
+    case DT_F16:
+      if (big) k_quant_rows_fp8<DT_F16, 32><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
+      else k_quant_rows_fp8<DT_F16, 8><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
+      break;
+    default:
+      if (big) k_quant_rows_fp8<DT_BF16, 32><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
+      else k_quant_rows_fp8<DT_BF16, 8><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
+      break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, const uint8_t* colflag,
                                int8_t* xq, float* x_scale, int32_t* x_rowsum, hipStream_t st) {
-  dim3 grid((unsigned)M), block(kThreads);
+  dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
+  const int64_t per_lane = K / (dt == DT_F32 ? 4 : 8) / 64;
+  const bool big = per_lane > 8;
   switch (dt) {
-    case DT_F32: k_quant_act_i8<DT_F32><<<grid, block, 0, st>>>(x, K, colflag, xq, x_scale, x_rowsum); break;
-    case DT_F16: k_quant_act_i8<DT_F16><<<grid, block, 0, st>>>(x, K, colflag, xq, x_scale, x_rowsum); break;
-    default: k_quant_act_i8<DT_BF16><<<grid, block, 0, st>>>(x, K, colflag, xq, x_scale, x_rowsum); break;
+    case DT_F32:
+      if (big) k_quant_act_i8<DT_F32, 32><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
+      else k_quant_act_i8<DT_F32, 8><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
+      break;
+    case DT_F16:
+      if (big) k_quant_act_i8<DT_F16, 32><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
+      else k_quant_act_i8<DT_F16, 8><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
+      break;
+    default:
+      if (big) k_quant_act_i8<DT_BF16, 32><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
+      else k_quant_act_i8<DT_BF16, 8><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
+      break;
   }
   return hipGetLastError();
 }
