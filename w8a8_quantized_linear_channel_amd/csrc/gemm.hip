@@ -17,15 +17,18 @@
 // bytes per stage.  Four LDS buffers hold four stages, filled by
 // global_load_lds_dwordx4 (global -> LDS without registers) three stages
 // ahead of the MFMAs, so a stage's loads have three stages of compute to
-// arrive.  Within a stage the B fragments of k-step s+1 are read from LDS while
-// the MFMAs of k-step s run, and each A fragment is re-read right after its
-// last use.
+// arrive.  Fragments are double buffered in registers: the LDS reads of the
+// next k-step (across a stage boundary: of the next stage, right after its
+// barrier) are issued before the MFMAs of the current one.
 //
 // LDS layout: row-major 64-byte rows (one row of the tile, one stage of K),
-// the 16-byte chunk c of row r stored at chunk position c ^ ((r >> 1) & 3).
-// A fragment read has rows 0..7 of one logical chunk in one LDS cycle; even
-// and odd rows fall in different halves of the banks and the XOR spreads the
-// four row pairs over the four bank groups of each half.  The DMA writes 64
+// the 16-byte chunk c of row r stored at chunk position c ^ ((r >> 2) & 3).
+// gfx950's LDS serves a ds_read_b128 16 lanes per cycle over 64 four-byte
+// banks (256 bytes), i.e. four 64-byte rows: a fragment read has rows 0..15
+// of one logical chunk in one cycle, rows r, r+4, r+8, r+12 share a bank
+// quarter, and the XOR gives those four rows four different 16-byte slots of
+// it.  (The bank-conflict counter reads half of all LDS cycles with the
+// 32-bank pattern c ^ ((r >> 1) & 3), and none with this one.)  The DMA writes 64
 // consecutive 16-byte slots per wave instruction, so the swizzle is applied
 // on the global side: each lane fetches the chunk that belongs at its slot.
 //
@@ -40,19 +43,40 @@
 namespace q8 {
 namespace {
 
-typedef __attribute__((address_space(1))) void* gptr_t;   // global (DMA source)
-typedef __attribute__((address_space(3))) void* lptr_t;   // LDS (DMA destination)
+typedef __attribute__((address_space(3))) void* lptr_t;   // LDS
+
+// global_load_lds_dwordx4: 64 lanes x 16 bytes from gbase + voff (per lane)
+// into 1 KB of LDS at `lds` (lane l at lds + 16 l), counted by vmcnt.  Issued
+// as inline asm on purpose: the compiler's own wait insertion cannot tell the
+// buffer a DMA fills from the buffer the fragment reads come from and would
+// put a vmcnt(0) before every LDS read, draining the prefetch each stage.
+// The kernel therefore waits for the DMA itself (s_waitcnt vmcnt + barrier).
+// M0 carries the LDS address; nothing else in these kernels uses M0, and the
+// s_nop covers the M0-write -> LDS-DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 constexpr int kBK = 64;             // bytes of K per stage
 constexpr int kStages = 4;          // LDS buffers (prefetch distance kStages - 1)
 constexpr int kThreads = 256;       // 4 waves
 constexpr int kGroupM = 4;          // tile-rows per L2 group
 constexpr int kXcds = 8;
+// s_waitcnt immediate for lgkmcnt(0) alone on gfx9: vmcnt 63 (bits 3:0 and
+// 15:14), expcnt 7 (bits 6:4), lgkmcnt 0 (bits 11:8)
+constexpr int kLgkmcnt0 = 0xC07F;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 3)) << 4); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 // One MFMA shape.  A fragment row is (base multiple of 32) + lane % 32, so
-// ((row >> 1) & 3) == ((lane >> 1) & 3) and the swizzled byte offset of the
+// ((row >> 2) & 3) == ((lane >> 2) & 3) and the swizzled byte offset of the
 // lane's operand inside its LDS row is lane_off(lane) XOR a per-k-step constant.
 // A and B fragments use the same lane -> k mapping, so each instruction sums
 // over exactly the k bytes of its step whatever order the hardware uses.
@@ -61,7 +85,7 @@ struct MmaI8 {                       // v_mfma_i32_32x32x32_i8
   using Op = v4i;
   using Acc = v16i;
   // lane l: 16-byte logical chunk 2*ks + l/32 of its row
-  __device__ static int lane_off(int lane) { return ((lane >> 5) ^ ((lane >> 1) & 3)) << 4; }
+  __device__ static int lane_off(int lane) { return ((lane >> 5) ^ ((lane >> 2) & 3)) << 4; }
   __device__ static Op load(const uint8_t* row, int off, int ks) {
     return *(const v4i*)(row + (off ^ (ks << 5)));
   }
@@ -74,7 +98,7 @@ struct MmaF8 {                       // v_mfma_f32_32x32x64_f8f6f4, both operand
   using Op = v8i;
   using Acc = v16f;
   // lane l: logical chunks 4*ks + 2*(l/32) + {0, 1} of its row
-  __device__ static int lane_off(int lane) { return ((2 * (lane >> 5)) ^ ((lane >> 1) & 3)) << 4; }
+  __device__ static int lane_off(int lane) { return ((2 * (lane >> 5)) ^ ((lane >> 2) & 3)) << 4; }
   __device__ static Op load(const uint8_t* row, int off, int ks) {
     const v4i lo = *(const v4i*)(row + (off ^ (ks << 6)));
     const v4i hi = *(const v4i*)(row + ((off ^ 16) ^ (ks << 6)));
@@ -123,12 +147,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   constexpr int NR = MM::NR;
   constexpr int KS = kBK / MM::KSTEP;
 
-  // the LDS buffers as distinct objects, so the compiler can tell the buffers
-  // the DMA is filling from the one the fragment reads come from
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[BM * kBK], sb0[BN * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[BM * kBK], sb1[BN * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t sa2[BM * kBK], sb2[BN * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t sa3[BM * kBK], sb3[BN * kBK];
+  // one LDS arena: four stages of A and B tiles in the main loop, then the
+  // epilogue's factor arrays and output staging
+  constexpr int kStageBytes = (BM + BN) * kBK;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+  uint8_t* const sa0 = smem;
+  uint8_t* const sb0 = smem + BM * kBK;
+  uint8_t* const sa1 = smem + kStageBytes;
+  uint8_t* const sb1 = sa1 + BM * kBK;
+  uint8_t* const sa2 = smem + 2 * kStageBytes;
+  uint8_t* const sb2 = sa2 + BM * kBK;
+  uint8_t* const sa3 = smem + 3 * kStageBytes;
+  uint8_t* const sb3 = sa3 + BM * kBK;
 
   const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
@@ -142,11 +172,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
 
   // ---- DMA loader.  One wave instruction fills 1 KB = 16 LDS rows; lane l
   // lands at row l/4, physical chunk l%4, which holds logical chunk
-  // (l%4) ^ ((row >> 1) & 3).  Rows past M (or N) re-read the last row: they
+  // (l%4) ^ ((row >> 2) & 3).  Rows past M (or N) re-read the last row: they
   // only feed outputs that are never stored.
   constexpr int kRowsPerDma = 64 * 16 / kBK;     // 16
   const int lrow = lane >> 2;
-  const int lchunk = (lane & 3) ^ ((lrow >> 1) & 3);
+  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
   uint32_t aoff[TL::ALOADS], boff[TL::BLOADS];
 #pragma unroll
   for (int j = 0; j < TL::ALOADS; ++j) {
@@ -160,19 +190,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
     gn = gn < N ? gn : N - 1;
     boff[j] = (uint32_t)(gn * K + lchunk * 16);
   }
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
   auto dma = [&](uint8_t* sa, uint8_t* sb, int k0) {
     const uint8_t* abase = g.a + k0;
     const uint8_t* bbase = g.b + k0;
 #pragma unroll
     for (int j = 0; j < TL::ALOADS; ++j)
-      __builtin_amdgcn_global_load_lds((gptr_t)(abase + aoff[j]),
-                                       (lptr_t)(sa + (j * (kThreads / 64) + wave) * kRowsPerDma * kBK), 16,
-                                       0, 0);
+      dma16(abase, aoff[j], sa + (j * (kThreads / 64) + swave) * kRowsPerDma * kBK);
 #pragma unroll
     for (int j = 0; j < TL::BLOADS; ++j)
-      __builtin_amdgcn_global_load_lds((gptr_t)(bbase + boff[j]),
-                                       (lptr_t)(sb + (j * (kThreads / 64) + wave) * kRowsPerDma * kBK), 16,
-                                       0, 0);
+      dma16(bbase, boff[j], sb + (j * (kThreads / 64) + swave) * kRowsPerDma * kBK);
+  };
+  // DMA instruction k (0 .. LOADS-1) of a stage: A rows first, then B rows
+  auto dma_one = [&](int k, uint8_t* sa, uint8_t* sb, int k0) {
+    if (k < TL::ALOADS)
+      dma16(g.a + k0, aoff[k], sa + (k * (kThreads / 64) + swave) * kRowsPerDma * kBK);
+    else
+      dma16(g.b + k0, boff[k - TL::ALOADS], sb + ((k - TL::ALOADS) * (kThreads / 64) + swave) * kRowsPerDma * kBK);
   };
   // Register loader for a last stage that K does not fill: chunks past K are
   // zero so they add nothing to the dot products.
@@ -206,142 +240,192 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   const int arow = (wm * TL::TM + (lane & 31)) * kBK;
   const int brow = (wn * TL::TN + (lane & 31)) * kBK;
   const int loff = MM::lane_off(lane);
-  // B fragments are double buffered across k-steps; each A fragment is
-  // re-read for the next k-step right after its last MFMA of this one.
-  auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
-    const uint8_t* ar = As + arow;
-    const uint8_t* br = Bs + brow;
-    typename MM::Op af[TL::FM], bf[2][TL::FN];
+  // Fragments live in two register sets: while the MFMAs of one k-step run,
+  // the LDS reads of the next k-step (or, across a stage boundary, of the
+  // next stage's first k-step) go to the other set.
+  typename MM::Op fa[2][TL::FM], fb[2][TL::FN];
+  auto load_frag = [&](auto SET, int f, const uint8_t* As, const uint8_t* Bs, int ks) {
+    constexpr int st = decltype(SET)::value;
+    if (f < TL::FM) fa[st][f] = MM::load(As + arow + f * 32 * kBK, loff, ks);
+    else fb[st][f - TL::FM] = MM::load(Bs + brow + (f - TL::FM) * 32 * kBK, loff, ks);
+  };
+  auto load_frags = [&](auto SET, const uint8_t* As, const uint8_t* Bs, int ks) {
 #pragma unroll
-    for (int i = 0; i < TL::FM; ++i) af[i] = MM::load(ar + i * 32 * kBK, loff, 0);
+    for (int f = 0; f < TL::FM + TL::FN; ++f) load_frag(SET, f, As, Bs, ks);
+  };
+  auto mfmas = [&](auto SET) {
+    constexpr int st = decltype(SET)::value;
 #pragma unroll
-    for (int j = 0; j < TL::FN; ++j) bf[0][j] = MM::load(br + j * 32 * kBK, loff, 0);
+    for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < KS) {
+      for (int j = 0; j < TL::FN; ++j) acc[i][j] = MM::mma(fb[st][j], fa[st][i], acc[i][j]);
+  };
+  // One k-step's MFMAs on register set CUR with other work spread between
+  // them, in this order (sched_barrier pins it): after MFMA t come the LDS
+  // reads of fragments [t*F/NM, (t+1)*F/NM) into set NXT (if pf) and DMA
+  // instructions [t*L/NM, (t+1)*L/NM) of a later stage (if dm).  Issued in a
+  // burst, the DMA instructions stall the wave on the vector-memory queue
+  // while the MFMA pipe runs dry; spread out, each waits behind an MFMA.
+  // pf and dm are compile-time constants in the steady-state loop; in the
+  // last stages only these slots, never the MFMAs, are conditional.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  auto step = [&](auto CUR, auto NXT, bool pf, bool dm, const uint8_t* xa, const uint8_t* xb, int xks,
+                  uint8_t* da, uint8_t* db, int dk0) {
+    constexpr int cs = decltype(CUR)::value;
+    constexpr int NM = TL::FM * TL::FN, NF = TL::FM + TL::FN, NL = TL::LOADS;
 #pragma unroll
-        for (int j = 0; j < TL::FN; ++j) bf[cur ^ 1][j] = MM::load(br + j * 32 * kBK, loff, ks + 1);
+    for (int t = 0; t < NM; ++t) {
+      const int i = t / TL::FN, j = t % TL::FN;
+      acc[i][j] = MM::mma(fb[cs][j], fa[cs][i], acc[i][j]);
+      if (pf) {
+#pragma unroll
+        for (int f = (t * NF + NM - 1) / NM; f < ((t + 1) * NF + NM - 1) / NM; ++f) load_frag(NXT, f, xa, xb, xks);
       }
+      if (dm) {
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TL::FN; ++j) acc[i][j] = MM::mma(af[i], bf[cur][j], acc[i][j]);
-        if (ks + 1 < KS) af[i] = MM::load(ar + i * 32 * kBK, loff, ks + 1);
+        for (int k = (t * NL + NM - 1) / NM; k < ((t + 1) * NL + NM - 1) / NM; ++k) dma_one(k, da, db, dk0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // ---- main loop.  Stage s lives in buffer s % 4 and is requested three
-  // stages ahead.  Before computing stage s a wave waits until at most the
-  // DMA of stages s+1, s+2 is outstanding (its own loads retire in order),
-  // then the barrier makes every wave's copy of stage s visible and proves
-  // that stage s-1's buffer, refilled next with stage s+3, has been read.
-  auto wait_stage = [&](int s) {
-    const int later = (nfull - 1 - s) < 2 ? (nfull - 1 - s) : 2;   // stages issued after s
+  // ---- main loop.  Stage s lives in buffer s % 4; its DMA is issued during
+  // stage s-4's last k-step.  Before stage s+1's fragments are read, each wave
+  // waits until at most the DMA of stages s+2, s+3 is outstanding (its own
+  // loads retire in order) and has finished its own LDS reads of stage s;
+  // the barrier then makes every wave's copy of stage s+1 visible and proves
+  // that buffer s % 4 is free for the DMA of stage s+4.
+  auto wait_stage = [&](int s, bool steady) {
+    const int later = steady || (nfull - 1 - s) >= 2 ? 2 : nfull - 1 - s;   // stages issued after s
     if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * TL::LOADS) : "memory");
     else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TL::LOADS) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // A bare s_barrier: __syncthreads() adds a workgroup release fence, which
+    // waits for every LDS write in flight, the DMA of later stages included.
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
-  auto stage = [&](int s, const uint8_t* ca, const uint8_t* cb, uint8_t* na, uint8_t* nb) {
-    wait_stage(s);
-    if (s + 3 < nfull) dma(na, nb, (s + 3) * kBK);
-    compute(ca, cb);
+  // One stage whose first k-step's fragments are in register set P.  STEADY:
+  // the next stage exists and so does stage s+4 (no run-time tests).
+  auto stage = [&](auto PC, auto STEADY, int s, uint8_t* ca, uint8_t* cb, const uint8_t* xa,
+                   const uint8_t* xb) {
+    constexpr int P = decltype(PC)::value;
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      if ((P + ks) & 1) step(S1{}, S0{}, true, false, ca, cb, ks + 1, ca, cb, 0);
+      else step(S0{}, S1{}, true, false, ca, cb, ks + 1, ca, cb, 0);
+    }
+    constexpr int last = (P + KS - 1) & 1;
+    using CUR = std::integral_constant<int, last>;
+    using NXT = std::integral_constant<int, last ^ 1>;
+    // This wave's LDS reads of stage s are complete (issued a k-step ago).
+    // As an s_waitcnt the compiler sees, it also tells the compiler's own
+    // wait insertion that nothing is pending past this point.
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+    const bool nxt = decltype(STEADY)::value || s + 1 < nfull;
+    const bool ahead = decltype(STEADY)::value || s + 4 < nfull;
+    if (nxt) wait_stage(s + 1, decltype(STEADY)::value);
+    step(CUR{}, NXT{}, nxt, ahead, xa, xb, 0, ca, cb, (s + 4) * kBK);
   };
+  constexpr int P1 = KS & 1, P2 = (2 * KS) & 1, P3 = (3 * KS) & 1;
+  using C1 = std::integral_constant<int, P1>;
+  using C2 = std::integral_constant<int, P2>;
+  using C3 = std::integral_constant<int, P3>;
   if (nfull > 0) dma(sa0, sb0, 0);
   if (nfull > 1) dma(sa1, sb1, kBK);
   if (nfull > 2) dma(sa2, sb2, 2 * kBK);
-  int kt = 0;
-  for (; kt + 4 <= nfull; kt += 4) {          // single exit: the accumulators stay in place
-    stage(kt, sa0, sb0, sa3, sb3);
-    stage(kt + 1, sa1, sb1, sa0, sb0);
-    stage(kt + 2, sa2, sb2, sa1, sb1);
-    stage(kt + 3, sa3, sb3, sa2, sb2);
+  if (nfull > 0) {
+    wait_stage(0, false);
+    if (nfull > 3) dma(sa3, sb3, 3 * kBK);
+    load_frags(S0{}, sa0, sb0, 0);
   }
-  if (kt < nfull) stage(kt, sa0, sb0, sa3, sb3);
-  if (kt + 1 < nfull) stage(kt + 1, sa1, sb1, sa0, sb0);
-  if (kt + 2 < nfull) stage(kt + 2, sa2, sb2, sa1, sb1);
+  int kt = 0;
+  // steady state: stages kt .. kt+3 all have a stage four ahead
+  for (; kt + 8 <= nfull; kt += 4) {          // single exit: the accumulators stay in place
+    stage(S0{}, T{}, kt, sa0, sb0, sa1, sb1);
+    stage(C1{}, T{}, kt + 1, sa1, sb1, sa2, sb2);
+    stage(C2{}, T{}, kt + 2, sa2, sb2, sa3, sb3);
+    stage(C3{}, T{}, kt + 3, sa3, sb3, sa0, sb0);
+  }
+  // the last (up to 7) stages
+  if (kt + 4 <= nfull) {
+    stage(S0{}, F{}, kt, sa0, sb0, sa1, sb1);
+    stage(C1{}, F{}, kt + 1, sa1, sb1, sa2, sb2);
+    stage(C2{}, F{}, kt + 2, sa2, sb2, sa3, sb3);
+    stage(C3{}, F{}, kt + 3, sa3, sb3, sa0, sb0);
+    kt += 4;
+  }
+  if (kt < nfull) stage(S0{}, F{}, kt, sa0, sb0, sa1, sb1);
+  if (kt + 1 < nfull) stage(C1{}, F{}, kt + 1, sa1, sb1, sa2, sb2);
+  if (kt + 2 < nfull) stage(C2{}, F{}, kt + 2, sa2, sb2, sa3, sb3);
   // ---- the partial last stage, through registers, in buffer nfull % 4 (last
   // read by stage nfull - 4, long finished)
   if (ragged) {
     const int b = nfull & 3;
     uint8_t* ta = b == 0 ? sa0 : b == 1 ? sa1 : b == 2 ? sa2 : sa3;
     uint8_t* tb = b == 0 ? sb0 : b == 1 ? sb1 : b == 2 ? sb2 : sb3;
-    __syncthreads();                          // every wave is past stage nfull - 4
+    __syncthreads();
     tail(ta, tb, nfull * kBK);
     __syncthreads();
-    compute(ta, tb);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      load_frags(S0{}, ta, tb, ks);
+      mfmas(S0{});
+    }
   }
 
-  // ---- epilogue.  Register r of fragment (i, j) is output
-  // (mw + i*32 + out_row(r), nw + j*32 + lane%32).  Row factors are loaded
-  // once per fragment row, column factors once per fragment.
-  const int mw = m0 + wm * TL::TM, nw = n0 + wn * TL::TN;
-  const int ocol = lane & 31;
-  const bool full = (m0 + BM <= M) && (n0 + BN <= N);
-  if constexpr (KIND == GEMM_FP8 || KIND == GEMM_INT8) {
-#pragma unroll
-    for (int i = 0; i < TL::FM; ++i) {
-      float sx[NR];
-      int rs[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int m = mw + i * 32 + out_row(r, lane);
-        const int mc = m < M ? m : M - 1;
-        sx[r] = g.a_scale[mc];
-        if constexpr (KIND == GEMM_INT8) rs[r] = g.a_rowsum[mc];
-      }
-#pragma unroll
-      for (int j = 0; j < TL::FN; ++j) {
-        const int n = nw + j * 32 + ocol;
-        const int nc = n < N ? n : N - 1;
-        const float sb = g.b_scale[nc];
-        const float bb = g.bias ? g.bias[nc] : 0.0f;
-        int zb = 0;
-        if constexpr (KIND == GEMM_INT8) zb = (int)g.b_zp[nc];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int m = mw + i * 32 + out_row(r, lane);
-          if (!full && (m >= M || n >= N)) continue;
-          const int o = m * N + n;
-          float v;
-          if constexpr (KIND == GEMM_INT8) {
-            const int a = acc[i][j][r];
-            if (g.acc_out) g.acc_out[o] = a;
-            v = (sx[r] * sb) * (float)(a - zb * rs[r]) + bb;
-          } else {
-            v = acc[i][j][r] * (sx[r] * sb) + bb;
-          }
-          store_out<YDT>(g.y, o, v);
-        }
-      }
-    }
-  } else {
+  // ---- epilogue.  The weight fragment is the MFMA's first operand, so
+  // fragment (i, j) holds D[n][m]: register r of lane l is output
+  // m = mw + i*32 + l%32, n = nw + j*32 + out_row(r, l); registers 4q..4q+3
+  // are four consecutive n of one m.  Factors go through LDS once; each
+  // wave then converts one 32-row slab at a time into a padded LDS staging
+  // tile (four values per 8-byte write) and stores it back row-contiguous.
+  const int mw = wm * TL::TM, nw = wn * TL::TN;        // wave offsets inside the tile
+  const int lm = lane & 31, lh = lane >> 5;
+  constexpr int kFacBytes = ((2 * BM + 3 * BN) * 4 + 15) / 16 * 16;
+  float* const f_sx = (float*)smem;                     // [BM]
+  int* const f_rs = (int*)(f_sx + BM);                  // [BM]
+  float* const f_sb = (float*)(f_rs + BM);              // [BN]
+  int* const f_zi = (int*)(f_sb + BN);                  // [BN] zero points (exact integers)
+  float* const f_bb = (float*)(f_zi + BN);              // [BN]
+  __syncthreads();                                      // the main loop's LDS reads are done
+  if (tid < BM) {
+    const int m = m0 + tid < M ? m0 + tid : M - 1;
+    f_sx[tid] = g.a_scale[m];
+    if constexpr (KIND != GEMM_FP8) f_rs[tid] = g.a_rowsum[m];
+  }
+  if (tid < BN) {
+    const int n = n0 + tid < N ? n0 + tid : N - 1;
+    f_sb[tid] = g.b_scale[n];
+    f_zi[tid] = KIND != GEMM_FP8 ? (int)g.b_zp[n] : 0;
+    f_bb[tid] = g.bias ? g.bias[n] : 0.0f;
+  }
+  __syncthreads();
+
+  if constexpr (KIND == GEMM_INT8_DECOMP) {
     // LLM.int8: dequantize the int8 part in place (the fp32 value replaces
     // the int32 in the same registers), then add the outlier flow with
-    // v_mfma_f32_32x32x16_f16 whose accumulator input is that value (its
-    // output layout is the same 32 x 32 layout).
+    // v_mfma_f32_32x32x16_f16 (same 32 x 32 output layout, weights first)
+    // whose accumulator input is that value.
 #pragma unroll
     for (int i = 0; i < TL::FM; ++i) {
+      const int ml = mw + i * 32 + lm, m = m0 + ml;
+      const float sx = f_sx[ml];
+      const int rs = f_rs[ml];
 #pragma unroll
-      for (int j = 0; j < TL::FN; ++j) {
-        const int n = nw + j * 32 + ocol;
-        const int nc = n < N ? n : N - 1;
-        const float sb = g.b_scale[nc];
-        const int zb = (int)g.b_zp[nc];
+      for (int j = 0; j < TL::FN; ++j)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          const int m = mw + i * 32 + out_row(r, lane);
-          const int mc = m < M ? m : M - 1;
+          const int nl = nw + j * 32 + out_row(r, lane), n = n0 + nl;
           const int a = acc[i][j][r];
           if (g.acc_out && m < M && n < N) g.acc_out[m * N + n] = a;
-          acc[i][j][r] = __float_as_int((g.a_scale[mc] * sb) * (float)(a - zb * g.a_rowsum[mc]));
+          acc[i][j][r] = __float_as_int((sx * f_sb[nl]) * (float)(a - f_zi[nl] * rs));
         }
-      }
     }
     const int cnt = *g.out_cnt;
     const int kg = lane >> 5;                          // 8-column group of the 16-column step
-    const int orow = lane & 31;
     for (int kc = 0; kc < cnt; kc += 16) {
       int col[8];
 #pragma unroll
@@ -352,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
       v8h xo[TL::FM], wo[TL::FN];
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i) {
-        const int m = mw + i * 32 + orow;
+        const int m = m0 + mw + i * 32 + lm;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           xo[i][e] = (col[e] >= 0 && m < M) ? __builtin_bit_cast(_Float16, g.x_f16[m * K + col[e]])
@@ -360,10 +444,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
       }
 #pragma unroll
       for (int j = 0; j < TL::FN; ++j) {
-        const int n = nw + j * 32 + orow;
+        const int nl = nw + j * 32 + lm, n = n0 + nl;
         const bool nok = n < N;
-        const float sb = nok ? g.b_scale[n] : 0.0f;
-        const float zb = nok ? g.b_zp[n] : 0.0f;
+        const float sb = f_sb[nl], zb = (float)f_zi[nl];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float wv = 0.0f;
@@ -376,34 +459,124 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TL::FN; ++j) {
           v16f c = __builtin_bit_cast(v16f, acc[i][j]);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(xo[i], wo[j], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[j], xo[i], c, 0, 0, 0);
           acc[i][j] = __builtin_bit_cast(v16i, c);
         }
     }
+  }
+
+  // Slab i of the wave (32 rows m, TN columns n) through the wave's LDS
+  // staging tile, row pitch TN*ES + 8 bytes (the pad spreads the 32 rows of
+  // one 8-byte write over all banks), then row-contiguous 8-byte stores to
+  // dst ([M, N] of ES-byte elements).  words(j, q) gives the four values
+  // n = nw + j*32 + 8q + 4*(lane/32) + 0..3 of row m = mw + i*32 + lane%32 as
+  // ES-byte elements packed into 32-bit words.
+  auto emit = [&](auto ESC, int i, auto&& words, uint8_t* dst) {
+    constexpr int ES = decltype(ESC)::value;
+    constexpr int kPitch = TL::TN * ES + 8;
+    constexpr int kChunks = TL::TN * ES / 8;             // 8-byte chunks per staged row
+    // each wave owns a fixed region sized for the widest pitch, so regions
+    // of different waves never overlap whatever each one is staging
+    constexpr int kWaveStage = 32 * (TL::TN * 4 + 8);
+    static_assert(kPitch * 32 <= kWaveStage, "staging pitch");
+    static_assert(kFacBytes + 4 * kWaveStage <= kStages * kStageBytes, "epilogue staging does not fit");
+    uint8_t* const stg = smem + kFacBytes + wave * kWaveStage;
 #pragma unroll
-    for (int j = 0; j < TL::FN; ++j) {
-      const int n = nw + j * 32 + ocol;
-      if (n >= N) continue;
-      const float bb = g.bias ? g.bias[n] : 0.0f;
+    for (int j = 0; j < TL::FN; ++j)
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
+      for (int q = 0; q < NR / 4; ++q) {
+        const int cl = j * 32 + 8 * q + 4 * lh;
+        const v4i w = words(j, q);
+        uint8_t* p = stg + lm * kPitch + cl * ES;
+        *(v2i*)p = v2i{w[0], w[1]};
+        if constexpr (ES == 4) *(v2i*)(p + 8) = v2i{w[2], w[3]};
+      }
+    const int mrow0 = m0 + mw + i * 32, ncol0 = n0 + nw;
+    if (((N * ES) & 7) == 0) {
+      // rows start 8-byte aligned, and a chunk (4 or 2 elements starting at a
+      // multiple of its length) is either wholly inside N or wholly outside
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int m = mw + i * 32 + out_row(r, lane);
-          if (m < M) store_out<YDT>(g.y, m * N + n, __int_as_float(acc[i][j][r]) + bb);
-        }
+      for (int t = 0; t < 32 * kChunks / 64; ++t) {
+        const int id = t * 64 + lane, row = id / kChunks, ch = id % kChunks;
+        const int m = mrow0 + row, n = ncol0 + ch * (8 / ES);
+        const v2i d = *(const v2i*)(stg + row * kPitch + ch * 8);
+        if (m < M && n < N) *(v2i*)(dst + (size_t)(uint32_t)(m * N + n) * ES) = d;
+      }
+    } else {
+      for (int id = lane; id < 32 * TL::TN; id += 64) {
+        const int row = id / TL::TN, c = id % TL::TN;
+        const int m = mrow0 + row, n = ncol0 + c;
+        if (m >= M || n >= N) continue;
+        const size_t o = (size_t)(uint32_t)(m * N + n) * ES;
+        if constexpr (ES == 4) *(int*)(dst + o) = *(const int*)(stg + row * kPitch + c * 4);
+        else *(uint16_t*)(dst + o) = *(const uint16_t*)(stg + row * kPitch + c * 2);
+      }
     }
+    // LDS accesses of one wave complete in order, so the next slab may reuse
+    // the staging tile right away.
+  };
+  using E2 = std::integral_constant<int, 2>;
+  using E4 = std::integral_constant<int, 4>;
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) {
+    if constexpr (KIND == GEMM_INT8) {
+      if (g.acc_out)
+        emit(E4{}, i, [&](int j, int q) {
+          return v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }, (uint8_t*)g.acc_out);
+    }
+    const int ml = mw + i * 32 + lm;
+    const float sx = f_sx[ml];
+    int rs = 0;
+    if constexpr (KIND == GEMM_INT8) rs = f_rs[ml];
+    auto words = [&](int j, int q) {
+      const int nl = nw + j * 32 + 8 * q + 4 * lh;
+      const v4f sb = *(const v4f*)(f_sb + nl);
+      const v4f bb = *(const v4f*)(f_bb + nl);
+      float v[4];
+      if constexpr (KIND == GEMM_INT8) {
+        const v4i zb = *(const v4i*)(f_zi + nl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (sx * sb[e]) * (float)(acc[i][j][4 * q + e] - zb[e] * rs) + bb[e];
+      } else if constexpr (KIND == GEMM_FP8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * (sx * sb[e]) + bb[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __int_as_float(acc[i][j][4 * q + e]) + bb[e];
+      }
+      if constexpr (YDT == DT_F32) {
+        return v4i{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
+      } else {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = YDT == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
+        return v4i{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16)), 0, 0};
+      }
+    };
+    if constexpr (YDT == DT_F32) emit(E4{}, i, words, (uint8_t*)g.y);
+    else emit(E2{}, i, words, (uint8_t*)g.y);
   }
 }
 
+// Output types: int8 GEMM f32 / f16 / bf16; the outlier flow f16 (the
+// decomposition's output is fp16); fp8 bf16.
 template <int BM, int BN, int KIND>
 hipError_t launch_tiles(const GemmArgs& g, int ydt, hipStream_t st) {
   const int64_t ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   dim3 grid((unsigned)(ntm * ntn)), block(kThreads);
-  switch (ydt) {
-    case DT_F32: k_gemm<BM, BN, KIND, DT_F32><<<grid, block, 0, st>>>(g); break;
-    case DT_F16: k_gemm<BM, BN, KIND, DT_F16><<<grid, block, 0, st>>>(g); break;
-    default: k_gemm<BM, BN, KIND, DT_BF16><<<grid, block, 0, st>>>(g); break;
+  if constexpr (KIND == GEMM_INT8) {
+    switch (ydt) {
+      case DT_F32: k_gemm<BM, BN, KIND, DT_F32><<<grid, block, 0, st>>>(g); break;
+      case DT_F16: k_gemm<BM, BN, KIND, DT_F16><<<grid, block, 0, st>>>(g); break;
+      default: k_gemm<BM, BN, KIND, DT_BF16><<<grid, block, 0, st>>>(g); break;
+    }
+  } else if constexpr (KIND == GEMM_INT8_DECOMP) {
+    if (ydt != DT_F16) return hipErrorInvalidValue;
+    k_gemm<BM, BN, KIND, DT_F16><<<grid, block, 0, st>>>(g);
+  } else {
+    if (ydt != DT_BF16) return hipErrorInvalidValue;
+    k_gemm<BM, BN, KIND, DT_BF16><<<grid, block, 0, st>>>(g);
   }
   return hipGetLastError();
 }
