@@ -57,8 +57,9 @@ def test_workspace_sizes():
     # GEMM path: codes + scale + row sum, each 256-byte aligned
     assert ws(_lib.Q8_OP_LINEAR, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192
     assert ws(_lib.Q8_OP_FP8, 4096, 4096, 14336) == 4096 * 14336 + 16384
+    # decomposition: codes, scale, row sum, column flags, outlier list, count
     d = ws(_lib.Q8_OP_DECOMP, 512, 4096, 4096)
-    assert d >= 512 * 4096 + 2 * 2048 + 8 * 4096 * 4 + 4096 + 4096 * 4 + 4
+    assert d == 512 * 4096 + 2048 + 2048 + 4096 + 4096 * 4 + 256
     # invalid shapes give 0
     assert ws(_lib.Q8_OP_LINEAR, 0, 16, 16) == 0
     assert ws(_lib.Q8_OP_LINEAR, 16, 16, 24) == 0

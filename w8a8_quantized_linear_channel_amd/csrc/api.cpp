@@ -59,15 +59,13 @@ LinearWs linear_ws(int64_t M, int64_t K) {
   return w;
 }
 
-struct DecompWs { size_t xq, xs, rs, partial, flags, idx, cnt, total; };
+struct DecompWs { size_t xq, xs, rs, flags, idx, cnt, total; };
 DecompWs decomp_ws(int64_t M, int64_t K) {
   Carve c;
   DecompWs w;
-  const int64_t parts = (M + q8::kColmaxRows - 1) / q8::kColmaxRows;
   w.xq = c.take((size_t)M * K);
   w.xs = c.take((size_t)M * 4);
   w.rs = c.take((size_t)M * 4);
-  w.partial = c.take((size_t)parts * K * 4);
   w.flags = c.take((size_t)K);
   w.idx = c.take((size_t)K * 4);
   w.cnt = c.take(4);
@@ -218,7 +216,7 @@ q8_status q8_quantize_act(q8_format fmt, const void* x, q8_dtype x_dtype, int64_
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, xq, x_scale, x_rowsum}));
   if (fmt == Q8_INT8_SYM)
-    return launched(q8::launch_quant_act_i8(x, x_dtype, M, K, nullptr, static_cast<int8_t*>(xq),
+    return launched(q8::launch_quant_act_i8(x, x_dtype, M, K, static_cast<int8_t*>(xq),
                                             x_scale, x_rowsum, st));
   return launched(q8::launch_quant_rows_fp8(x, x_dtype, M, K, scale_ub, static_cast<uint8_t*>(xq),
                                             x_scale, st));
@@ -249,7 +247,7 @@ q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const
   int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
   float* xs = reinterpret_cast<float*>(base + ws.xs);
   int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
-  Q8_TRY(launched(q8::launch_quant_act_i8(x, x_dtype, M, K, nullptr, xq, xs, rs, st)));
+  Q8_TRY(launched(q8::launch_quant_act_i8(x, x_dtype, M, K, xq, xs, rs, st)));
   q8::GemmArgs g{};
   g.a = reinterpret_cast<const uint8_t*>(xq);
   g.b = reinterpret_cast<const uint8_t*>(wq);
@@ -288,15 +286,16 @@ q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_
   int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
   float* xs = reinterpret_cast<float*>(base + ws.xs);
   int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
-  float* partial = reinterpret_cast<float*>(base + ws.partial);
   uint8_t* flags = reinterpret_cast<uint8_t*>(base + ws.flags);
   int32_t* idx = reinterpret_cast<int32_t*>(base + ws.idx);
   int32_t* cnt = reinterpret_cast<int32_t*>(base + ws.cnt);
   const uint16_t* xh = static_cast<const uint16_t*>(x);
 
-  Q8_TRY(launched(q8::launch_outlier_detect(xh, M, K, threshold, partial, flags, idx, cnt, outlier_idx,
-                                            n_outliers, st)));
-  Q8_TRY(launched(q8::launch_quant_act_i8(x, Q8_F16, M, K, flags, xq, xs, rs, st)));
+  // threshold <= 0: no outlier columns (the decomposition is off)
+  const bool on = threshold > 0.0f;
+  if (on) Q8_TRY(launched(q8::launch_outlier_flags(xh, M, K, threshold, flags, st)));
+  Q8_TRY(launched(q8::launch_quant_act_f16_outliers(xh, M, K, on ? flags : nullptr, xq, xs, rs, idx, cnt,
+                                                    outlier_idx, n_outliers, st)));
   q8::GemmArgs g{};
   g.a = reinterpret_cast<const uint8_t*>(xq);
   g.b = reinterpret_cast<const uint8_t*>(wq);

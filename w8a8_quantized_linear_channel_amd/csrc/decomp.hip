@@ -1,113 +1,79 @@
-// Outlier feature columns of the LLM.int8() mixed-precision decomposition:
-// O = { k : max_m |x[m,k]| >= threshold }, in ascending order, with |O| kept
-// on the device (no host synchronization).
+// Outlier feature columns of the LLM.int8() mixed-precision decomposition
+// ("Transformers 单 GPU 高效推理：bitsandbytes LLM.int8 …", core idea: feature
+// columns holding values beyond the threshold go through fp16):
+// flags[k] = (max_m |x[m,k]| >= threshold).
 //
-//   k_colmax_partial  grid (ceil(K / 2048), ceil(M / 64)): each thread owns 8
-//                     adjacent columns (one 16-byte fp16 chunk per row, so a
-//                     wave reads 1 KB contiguous per row) and 64 rows, and
-//                     writes their partial |x| maxima to partial[row_block][k].
-//   k_outlier_select  one workgroup of 1024 threads: each thread owns a run of
-//                     adjacent columns, reduces their partial maxima,
-//                     compares with the threshold, and a workgroup prefix sum
-//                     of the per-thread counts gives every flagged column its
-//                     ascending position.  Writes flags[K] (consumed by the
-//                     masked activation quantizer), idx[] and the count.
+//   k_colflag  one workgroup per 16 columns (256 for K = 4096): thread t reads
+//              the 16-byte chunk (t & 1) of rows t/2, t/2 + 128, ..., four
+//              rows in flight per round of 512 rows; the 128 row groups are
+//              combined in LDS and the workgroup writes the 16 flags.
+//
+// The ascending list of flagged columns and its count are compacted from the
+// flags by an extra workgroup of the masked activation quantizer that runs
+// next (quant.hip), which saves a launch; the count stays on the device.
 #include "q8_device.hpp"
 #include "q8_kernels.hpp"
 
 namespace q8 {
 namespace {
 
-constexpr int kColThreads = 256;
-constexpr int kSelThreads = 1024;
+constexpr int kFlagCols = 16;                  // columns per workgroup: 2 chunks of 8 fp16
+constexpr int kFlagThreads = 256;
+constexpr int kRowGroups = kFlagThreads / 2;   // 128 rows per load round
+constexpr int kRounds = 4;                     // rounds per workgroup (512 rows)
+constexpr int kFlagRows = kRowGroups * kRounds;
 
-__global__ __launch_bounds__(kColThreads) void k_colmax_partial(const uint16_t* __restrict__ x, int64_t M,
-                                                                int64_t K, float* __restrict__ partial) {
-  const int64_t c0 = ((int64_t)blockIdx.x * kColThreads + threadIdx.x) * 8;
-  if (c0 >= K) return;
-  const int64_t r0 = (int64_t)blockIdx.y * kColmaxRows;
-  const int64_t r1 = (r0 + kColmaxRows) < M ? (r0 + kColmaxRows) : M;
+__global__ __launch_bounds__(kFlagThreads) void k_colflag(const uint16_t* __restrict__ x, int M, int K,
+                                                          float threshold, uint8_t* __restrict__ flags) {
+  __shared__ float red[kRowGroups][kFlagCols + 1];
+  __shared__ float red2[kFlagThreads / kFlagCols][kFlagCols];
+  const int tid = threadIdx.x;
+  const int c2 = tid & 1, rg = tid >> 1;
+  const int col = blockIdx.x * kFlagCols + c2 * 8;       // K is a multiple of 16: always < K
   float mx[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) mx[e] = 0.0f;
-  for (int64_t r = r0; r < r1; ++r) {
-    float v[8];
-    Chunk<DT_F16>::decode(*(const v4i*)(x + r * K + c0), v);
+  for (int m0 = 0; m0 < M; m0 += kFlagRows) {
+    v4i ch[kRounds];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(v[e]));
-  }
-  float* out = partial + (int64_t)blockIdx.y * K + c0;
-  *(v4f*)out = v4f{mx[0], mx[1], mx[2], mx[3]};
-  *(v4f*)(out + 4) = v4f{mx[4], mx[5], mx[6], mx[7]};
-}
-
-__global__ __launch_bounds__(kSelThreads) void k_outlier_select(const float* __restrict__ partial, int nparts,
-                                                                 int64_t K, float threshold,
-                                                                 uint8_t* __restrict__ flags,
-                                                                 int32_t* __restrict__ idx,
-                                                                 int32_t* __restrict__ cnt,
-                                                                 int32_t* __restrict__ user_idx,
-                                                                 int32_t* __restrict__ user_cnt) {
-  __shared__ int wave_tot[kSelThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool on = threshold > 0.0f;
-  const int64_t per = (K + kSelThreads - 1) / kSelThreads;
-  const int64_t c0 = (int64_t)tid * per;
-  const int64_t c1 = (c0 + per) < K ? (c0 + per) : K;
-
-  int mine = 0;
-  for (int64_t k = c0; k < c1; ++k) {
-    bool f = false;
-    if (on) {
-      float c = 0.0f;
-      for (int p = 0; p < nparts; ++p) c = fmaxf(c, partial[(int64_t)p * K + k]);
-      f = c >= threshold;
+    for (int u = 0; u < kRounds; ++u) {
+      int m = m0 + u * kRowGroups + rg;
+      m = m < M ? m : M - 1;                  // rows past M repeat row M-1: the max is unchanged
+      ch[u] = *(const v4i*)(x + (size_t)m * K + col);
     }
-    flags[k] = f ? 1 : 0;
-    mine += f ? 1 : 0;
-  }
-
-  // inclusive scan of `mine` over the workgroup
-  int incl = mine;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
+    for (int u = 0; u < kRounds; ++u) {
+      float v[8];
+      Chunk<DT_F16>::decode(ch[u], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf(v[e]));
+    }
   }
-  if (lane == 63) wave_tot[wave] = incl;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][c2 * 8 + e] = mx[e];
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_tot[w];
-  int pos = before + incl - mine;
-
-  for (int64_t k = c0; k < c1; ++k) {
-    if (flags[k]) {
-      idx[pos] = (int32_t)k;
-      if (user_idx) user_idx[pos] = (int32_t)k;
-      ++pos;
-    }
+  {
+    // 16 parts of 8 row groups for each of the 16 columns
+    const int c = tid & 15, part = tid >> 4;
+    float v = red[part * 8][c];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) v = fmaxf(v, red[part * 8 + g][c]);
+    red2[part][c] = v;
   }
-  if (tid == kSelThreads - 1) {
-    const int total = before + incl;
-    *cnt = total;
-    if (user_cnt) *user_cnt = total;
+  __syncthreads();
+  if (tid < kFlagCols) {
+    float v = red2[0][tid];
+#pragma unroll
+    for (int p = 1; p < kFlagThreads / kFlagCols; ++p) v = fmaxf(v, red2[p][tid]);
+    flags[blockIdx.x * kFlagCols + tid] = v >= threshold ? 1 : 0;
   }
 }
 
 }  // namespace
 
-hipError_t launch_outlier_detect(const uint16_t* x_f16, int64_t M, int64_t K, float threshold,
-                                 float* partial, uint8_t* flags, int32_t* idx, int32_t* cnt,
-                                 int32_t* user_idx, int32_t* user_cnt, hipStream_t st) {
-  const int nparts = (int)((M + kColmaxRows - 1) / kColmaxRows);
-  if (threshold > 0.0f) {
-    dim3 grid((unsigned)((K + 8 * kColThreads - 1) / (8 * kColThreads)), (unsigned)nparts);
-    k_colmax_partial<<<grid, kColThreads, 0, st>>>(x_f16, M, K, partial);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  k_outlier_select<<<1, kSelThreads, 0, st>>>(partial, nparts, K, threshold, flags, idx, cnt, user_idx,
-                                               user_cnt);
+hipError_t launch_outlier_flags(const uint16_t* x_f16, int64_t M, int64_t K, float threshold, uint8_t* flags,
+                                hipStream_t st) {
+  k_colflag<<<(unsigned)(K / kFlagCols), kFlagThreads, 0, st>>>(x_f16, (int)M, (int)K, threshold, flags);
   return hipGetLastError();
 }
 

@@ -43,35 +43,12 @@
 namespace q8 {
 namespace {
 
-typedef __attribute__((address_space(3))) void* lptr_t;   // LDS
-
-// global_load_lds_dwordx4: 64 lanes x 16 bytes from gbase + voff (per lane)
-// into 1 KB of LDS at `lds` (lane l at lds + 16 l), counted by vmcnt.  Issued
-// as inline asm on purpose: the compiler's own wait insertion cannot tell the
-// buffer a DMA fills from the buffer the fragment reads come from and would
-// put a vmcnt(0) before every LDS read, draining the prefetch each stage.
-// The kernel therefore waits for the DMA itself (s_waitcnt vmcnt + barrier).
-// M0 carries the LDS address; nothing else in these kernels uses M0, and the
-// s_nop covers the M0-write -> LDS-DMA hazard.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint8_t* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(gbase)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 constexpr int kBK = 64;             // bytes of K per stage
 constexpr int kStages = 4;          // LDS buffers (prefetch distance kStages - 1)
 constexpr int kThreads = 256;       // 4 waves
 constexpr int kGroupM = 4;          // tile-rows per L2 group
 constexpr int kXcds = 8;
-// s_waitcnt immediate for lgkmcnt(0) alone on gfx9: vmcnt 63 (bits 3:0 and
-// 15:14), expcnt 7 (bits 6:4), lgkmcnt 0 (bits 11:8)
-constexpr int kLgkmcnt0 = 0xC07F;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
@@ -590,6 +567,9 @@ hipError_t launch_kind(const GemmArgs& g, int ydt, hipStream_t st) {
     if (tiles(256, 256) >= 192) return launch_tiles<256, 256, KIND>(g, ydt, st);
   }
   if (tiles(128, 128) >= 192) return launch_tiles<128, 128, KIND>(g, ydt, st);
+  // e.g. the LLM.int8 shape 512 x 4096: one round of 256 tiles, two
+  // independent accumulators per wave
+  if (tiles(64, 128) >= 192) return launch_tiles<64, 128, KIND>(g, ydt, st);
   return launch_tiles<64, 64, KIND>(g, ydt, st);
 }
 

@@ -2,22 +2,28 @@
 // activations per token and streams the int8 weights at HBM rate.
 //
 // A workgroup owns 16 weight rows (output features) and all of K; the grid is
-// ceil(N / 16) workgroups (256 for the 4096-row q_proj, one per CU).  Its 8
-// waves split into two roles so the two latencies overlap:
-//   * 4 "streamer" waves issue every 16-byte load of their weight rows for
-//     the current K segment up front (64 KB in flight per workgroup at
-//     K = 4096), then run v_mfma_i32_16x16x64_i8 with the weights as the
-//     A operand (rows n) and the activation codes from LDS as B (columns m);
-//   * 4 "quantizer" waves meanwhile read X (L2-resident: at most 16 rows),
-//     take each row's absmax, and write the int8 codes of the segment to LDS
-//     together with the per-row code sum.
-// Loads of one wave retire in order, so giving the weight stream and the
-// activation reads to different waves is what lets them overlap; the weight
-// loads are unconditional (clamped addresses) so nothing makes a streamer wait
-// for them before the MFMAs.  Code positions past K and rows past M are zero
-// in LDS, so whatever the clamped weight loads bring there adds nothing.
-// The four streamers' partial INT32 tiles are summed through LDS and one wave
-// applies the epilogue y = S_x S_w (acc - Z_w sum_k q_x) (+ bias).
+// ceil(N / 16) workgroups (256 for the 4096-row q_proj, one per CU).  Its 4
+// waves split K: inside each 4096-wide K segment, wave w owns the 1024
+// columns [1024 w, 1024 w + 1024) for everything it does --
+//   * it first copies those columns of every X row into its own LDS region
+//     (global_load_lds, so no registers are held), then issues its 16
+//     16-byte weight loads (16 rows x 1024 bytes): the activations, which
+//     every workgroup reads, are not queued behind 64 KB of weight traffic;
+//   * it takes each row's partial absmax over its columns; one barrier
+//     combines the four partials into the row scale;
+//   * it overwrites each row's X values in LDS with their int8 codes and runs
+//     v_mfma_i32_16x16x64_i8 over them with the weights as the A operand
+//     (rows n) and the codes as B (columns m).  Only this wave touches the
+//     region, so no barrier is needed between coding and the MFMAs.
+// Rows are processed in run-time loops: the kernel runs once per call, so
+// every instruction is fetched cold, and compact code is what keeps the
+// activation work short.  The four partial INT32 tiles and the per-row code
+// sums meet in LDS and wave 0 applies y = S_x S_w (acc - Z_w sum_k q_x)
+// (+ bias) with the per-row factors it loaded at the start.
+//
+// Code columns past K are zero, so the clamped weight loads there add
+// nothing.  Code rows m >= M hold stale bytes: they only feed MFMA output
+// columns that are not stored.
 #include "q8_device.hpp"
 #include "q8_kernels.hpp"
 
@@ -25,193 +31,261 @@ namespace q8 {
 namespace {
 
 constexpr int kRows = 16;               // weight rows per workgroup
-constexpr int kSeg = 4096;              // K bytes per LDS segment
-constexpr int kStreamers = 4, kQuantizers = 4;
-constexpr int kThreads = 64 * (kStreamers + kQuantizers);
-constexpr int kStepsPerWave = kSeg / 64 / kStreamers;   // 16 x 16-byte loads per lane
-constexpr int kXStride = kSeg + 16;     // padded LDS row: 8 rows of one column hit 8 bank groups
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSeg = 4096;              // K columns per segment
+constexpr int kKW = kSeg / kWaves;      // columns of a segment per wave (1024)
+constexpr int kSteps = kKW / 64;        // 64-byte MFMA k-steps per wave per segment (16)
+// One row's area in a wave's LDS region: 1024 16-bit X values (2048 bytes),
+// later overwritten by their 1024 codes.  The 16-byte pad puts the 16 code
+// rows read by one MFMA operand fetch in 16 different bank quarters.
+constexpr int kArea = 2 * kKW + 16;
 
-template <int DT, int YDT>
-__global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict__ x, int M, int64_t K,
+// ONE: K <= 4096, a single segment (the host picks the instantiation, so each
+// kernel has one straight path and the compiler's wait insertion sees it alone)
+template <int DT, int YDT, bool ONE>
+__global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict__ x, int M, int K,
                                                          const int8_t* __restrict__ wq,
                                                          const float* __restrict__ w_scale,
-                                                         const float* __restrict__ w_zp, int64_t N,
+                                                         const float* __restrict__ w_zp, int N,
                                                          const float* __restrict__ bias, void* __restrict__ y,
                                                          int32_t* __restrict__ acc_out) {
-  constexpr int E = Chunk<DT>::kElems;
-  constexpr int esz = (DT == DT_F32) ? 4 : 2;
-  constexpr int CPL = kSeg / E / 64;    // chunks per lane for one row-segment
-  __shared__ __attribute__((aligned(16))) int8_t xs[kRows * kXStride];
-  __shared__ float sx[kRows];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves][kRows * kArea];
+  // Per-thread partials of every row (absmax in pass 1, then code sums in
+  // pass 2): no reduction inside the row loops; one block-wide pass per
+  // quantity reduces all rows at once.
+  __shared__ __attribute__((aligned(16))) float lred[kRows][kThreads];
+  __shared__ float rscale[kRows];
   __shared__ int rsum[kRows];
-  __shared__ v4i part[kStreamers][64];
+  __shared__ v4i part[kWaves][64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * kRows;
-  const char* xb = (const char*)x;
+  const int n0 = blockIdx.x * kRows;
+  const uint8_t* xb = (const uint8_t*)x;
+  uint8_t* const xw = xs[wave];
+  const int nseg = (K + kSeg - 1) / kSeg;
+  auto seg_len = [&](int sg) { return (K - sg * kSeg) < kSeg ? (K - sg * kSeg) : kSeg; };
 
-  // ---- streamers: every weight load of a K segment in flight at once
-  v4i wv[kStepsPerWave];
-  const int64_t wrow = (n0 + lr < N ? n0 + lr : N - 1) * K;
-  auto issue = [&](int64_t k0) {
-    const int seg = (int)((K - k0) < kSeg ? (K - k0) : kSeg);
-#pragma unroll
-    for (int j = 0; j < kStepsPerWave; ++j) {
-      int kk = (wave + j * kStreamers) * 64 + lg * 16;
-      kk = kk < seg ? kk : seg - 16;
-      wv[j] = *(const v4i*)(wq + wrow + k0 + kk);
-    }
-  };
+  // The lane's columns inside the wave's 1024: chunk j (0, 1) is columns
+  // [512 j + 8 lane, 512 j + 8 lane + 8); a chunk lies wholly inside or
+  // wholly outside the segment (both are multiples of 8 or 16).
+  auto col = [&](int j) { return wave * kKW + 512 * j + 8 * lane; };
 
-  // ---- quantizers: one row-segment of X is CPL chunks per lane
-  auto load_seg = [&](int m, int64_t k0, int seg, v4i* ch) {
+  // ---- X of one segment into LDS, 16-bit inputs: two 1 KB DMA per row
+  auto dma_x = [&](int k0, int seg) {
+    for (int m = 0; m < M; ++m) {
+      const uint8_t* base = xb + ((size_t)m * K + k0) * 2;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      ch[j] = c < seg / E ? *(const v4i*)(xb + ((int64_t)m * K + k0 + (int64_t)c * E) * esz)
-                          : v4i{0, 0, 0, 0};
-    }
-  };
-  auto seg_absmax = [&](const v4i* ch) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      float v[E];
-      Chunk<DT>::decode(ch[j], v);
-#pragma unroll
-      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-    }
-    return amax;
-  };
-  // codes of one row-segment into LDS; returns this lane's code sum.  For
-  // 16-bit inputs the quotient comes from two FMAs on RN(1/s) (same codes as
-  // the division for a scale taken from the row absmax).
-  auto seg_codes = [&](int m, int seg, const v4i* ch, float s, float r) {
-    int qsum = 0;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      if (c < seg / E) {
-        float v[E];
-        Chunk<DT>::decode(ch[j], v);
-        uint32_t words[E / 4];
-#pragma unroll
-        for (int gq = 0; gq < E / 4; ++gq) {
-          uint32_t b[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float xv = v[4 * gq + e];
-            b[e] = rne_int8_bits(DT == DT_F32 ? xv / s : quot_fma(xv, s, r));
-          }
-          words[gq] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
-          qsum = sum_i8x4(words[gq], qsum);
-        }
-        if constexpr (E == 8) {
-          *(v2i*)(xs + m * kXStride + c * E) = v2i{(int)words[0], (int)words[1]};
-        } else {
-          *(uint32_t*)(xs + m * kXStride + c * E) = words[0];
-        }
+      for (int j = 0; j < 2; ++j) {
+        const int c = col(j) < seg ? col(j) : seg - 8;     // clamped: masked after the read
+        dma16(base, (uint32_t)c * 2, xw + m * kArea + 1024 * j);
       }
     }
-    return qsum;
   };
-
-  const int qw = wave - kStreamers;
-  const bool one_seg = K <= kSeg;
-  v4i cur[CPL];
-  if (wave < kStreamers) {
-    issue(0);
-  } else {
-    // rows M..15 of the code buffer stay zero for every segment
-    for (int i = qw * 64 + lane; i < (kRows - M) * (kSeg / 16); i += kQuantizers * 64) {
-      const int m = M + i / (kSeg / 16), c = i % (kSeg / 16);
-      *(v4i*)(xs + m * kXStride + c * 16) = v4i{0, 0, 0, 0};
-    }
-    if (!one_seg) {
-      // per-row absmax over every segment of the row
-      for (int m = qw; m < M; m += kQuantizers) {
-        float amax = 0.0f;
-        for (int64_t k0 = 0; k0 < K; k0 += kSeg) {
-          const int seg = (int)((K - k0) < kSeg ? (K - k0) : kSeg);
-          load_seg(m, k0, seg, cur);
-          amax = fmaxf(amax, seg_absmax(cur));
+  // the lane's 16 values of row m: from LDS (16-bit) or from global (fp32)
+  auto get_x = [&](int m, int k0, int seg, float* v) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = col(j) < seg;
+      if constexpr (DT == DT_F32) {
+        const int c = ok ? col(j) : seg - 8;
+        const float* p = (const float*)xb + (size_t)m * K + k0 + c;
+        const v4i a = *(const v4i*)p, b = *(const v4i*)(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * j + e] = ok ? __int_as_float(a[e]) : 0.0f;
+          v[8 * j + 4 + e] = ok ? __int_as_float(b[e]) : 0.0f;
         }
-        amax = wave_max(amax);
-        float s = amax / 127.0f;
-        s = s < kEps ? kEps : s;
-        if (lane == 0) { sx[m] = s; rsum[m] = 0; }
+      } else {
+        v4i ch = *(const v4i*)(xw + m * kArea + 1024 * j + 16 * lane);
+        // a chunk past K reads as +0 (only a partial segment has one)
+        if (seg != kSeg && !ok) ch = v4i{0, 0, 0, 0};
+        Chunk<DT>::decode(ch, v + 8 * j);
       }
     }
-  }
+  };
 
+  // ---- weights: 16 loads of 16 bytes per lane (rows n0 + lane%16)
+  v4i wv[kSteps];
+  const int wrow = (n0 + lr < N ? n0 + lr : N - 1);
+  auto load_w = [&](int k0, int seg) {
+    if (seg == kSeg) {
+      // one address per lane, the 16 steps as immediate offsets
+      const int8_t* p = wq + (size_t)wrow * K + k0 + wave * kKW + lg * 16;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) wv[s] = *(const v4i*)(p + s * 64);
+    } else {
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        int kk = wave * kKW + s * 64 + lg * 16;
+        kk = kk < seg ? kk : seg - 16;
+        wv[s] = *(const v4i*)(wq + (size_t)wrow * K + k0 + kk);
+      }
+    }
+  };
+  // epilogue factors (wave 0): acc register r of lane (lr, lg) is
+  // D[n = 4 lg + r][m = lr].
+  float fsc[4] = {0, 0, 0, 0}, fzp[4] = {0, 0, 0, 0}, fbi[4] = {0, 0, 0, 0};
+  auto load_factors = [&]() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + 4 * lg + r;
+      const int nc = n < N ? n : N - 1;
+      fsc[r] = w_scale[nc];
+      fzp[r] = w_zp[nc];
+      fbi[r] = bias ? bias[nc] : 0.0f;
+    }
+  };
+
+  // Block-wide reduction of lred over the 256 threads, all rows at once:
+  // thread t takes row t/16 and 16 of its partials, then the 16 threads of
+  // the row (one DPP row) combine theirs; every one of them gets the result.
+  auto reduce_rows = [&](auto op) {
+    const int m = tid >> 4, sub = tid & 15;
+    const v4i* src = (const v4i*)&lred[m][sub * 16];
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4i c = src[i];
+      r = i == 0 ? op(op(c[0], c[1]), op(c[2], c[3])) : op(r, op(op(c[0], c[1]), op(c[2], c[3])));
+    }
+    return dpp_row_reduce(r, op);
+  };
+  auto fmax_bits = [](int a, int b) { return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b))); };
+  auto add_int = [](int a, int b) { return a + b; };
+  auto row_scale = [&](int m) { return rscale[m]; };
   v4i acc = {0, 0, 0, 0};
-  for (int64_t k0 = 0; k0 < K; k0 += kSeg) {
-    const int seg = (int)((K - k0) < kSeg ? (K - k0) : kSeg);
-    __syncthreads();   // the previous segment's codes have been consumed
-    if (wave >= kStreamers) {
-      // a partial segment: code positions past K are zero
-      if (seg < kSeg) {
-        for (int m = qw; m < M; m += kQuantizers)
-          for (int b = seg + lane * 16; b < kSeg; b += 64 * 16) *(v4i*)(xs + m * kXStride + b) = v4i{0, 0, 0, 0};
-      }
-      // rows of this wave, the next row's loads in flight while one is coded
-      v4i nxt[CPL];
-      if (qw < M) load_seg(qw, k0, seg, cur);
-      for (int m = qw; m < M; m += kQuantizers) {
-        if (m + kQuantizers < M) load_seg(m + kQuantizers, k0, seg, nxt);
-        float s;
-        if (one_seg) {
-          const float amax = wave_max(seg_absmax(cur));
-          s = amax / 127.0f;
-          s = s < kEps ? kEps : s;
-        } else {
-          s = sx[m];
-        }
-        const float r = 1.0f / s;
-        const int qsum = wave_sum(seg_codes(m, seg, cur, s, r));
-        if (lane == 0) {
-          if (one_seg) { sx[m] = s; rsum[m] = qsum; }
-          else rsum[m] += qsum;
-        }
+
+  // ---- pass 1 over one segment: per-row partial absmax
+  auto pass1 = [&](int sg, int k0, int seg) {
+    if constexpr (DT != DT_F32) {
+      if (sg > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // reads of the last segment are done
+      dma_x(k0, seg);
+    }
+    if (sg == 0) load_w(0, seg);
+    if constexpr (DT != DT_F32) {
+      // this segment's X: everything but the 16 weight loads issued last
+      if (sg > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
+    }
+    // issued after the wait, so X does not wait for them; they have the
+    // whole coding and MFMA phase to arrive
+    if (sg == 0 && wave == 0) load_factors();
+#pragma unroll 4
+    for (int m = 0; m < M; ++m) {
+      float v[16];
+      get_x(m, k0, seg, v);
+      float a = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) cur[j] = nxt[j];
+      for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(v[e]));
+      lred[m][tid] = sg == 0 ? a : fmaxf(lred[m][tid], a);
+    }
+  };
+  // row scales from the partial absmax of every thread
+  auto finish_scales = [&]() {
+    __syncthreads();   // every thread's partial absmax is in LDS
+    const int r = reduce_rows(fmax_bits);
+    if ((tid & 15) == 0 && (tid >> 4) < M) {
+      const float s = __int_as_float(r) / 127.0f;
+      rscale[tid >> 4] = s < kEps ? kEps : s;
+    }
+    __syncthreads();   // the scales are in LDS; lred is free for the code sums
+  };
+  // ---- pass 2 over one segment: codes, then the MFMAs on them.  reload:
+  // X (and, past the first segment, W) must be fetched again.
+  auto pass2 = [&](int sg, int k0, int seg, bool reload) {
+    if (reload) {
+      if constexpr (DT != DT_F32) {
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+        dma_x(k0, seg);
+      }
+      if (sg > 0) load_w(k0, seg);
+      if constexpr (DT != DT_F32) {
+        if (sg > 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
     }
-    __syncthreads();   // the codes of this segment are in LDS
-    if (wave < kStreamers) {
+#pragma unroll 4
+    for (int m = 0; m < M; ++m) {
+      float v[16];
+      get_x(m, k0, seg, v);
+      const float s = row_scale(m);
+      const float r = 1.0f / s;
+      // For 16-bit inputs the quotient comes from two FMAs on RN(1/s), which
+      // gives the codes of the correctly rounded division for a scale taken
+      // from the row absmax; fp32 inputs use the IEEE division.
+      uint32_t words[4];
 #pragma unroll
-      for (int j = 0; j < kStepsPerWave; ++j) {
-        const int st = wave + j * kStreamers;
-        const v4i xv = *(const v4i*)(xs + lr * kXStride + st * 64 + lg * 16);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[j], xv, acc, 0, 0, 0);
+      for (int g = 0; g < 4; ++g) {
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xv = v[4 * g + e];
+          b[e] = rne_int8_bits(DT == DT_F32 ? xv / s : quot_fma(xv, s, r));
+        }
+        words[g] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
       }
-      if (k0 + kSeg < K) issue(k0 + kSeg);
+      int q = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) q = sum_i8x4(words[g], q);
+      // the row's X values have all been read (same wave, in order) before
+      // their codes overwrite the start of the area
+      uint8_t* area = xw + m * kArea;
+      *(v2i*)(area + 8 * lane) = v2i{(int)words[0], (int)words[1]};
+      *(v2i*)(area + 512 + 8 * lane) = v2i{(int)words[2], (int)words[3]};
+      ((int*)lred[m])[tid] = sg == 0 ? q : ((int*)lred[m])[tid] + q;
     }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const v4i xv = *(const v4i*)(xw + lr * kArea + s * 64 + lg * 16);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[s], xv, acc, 0, 0, 0);
+    }
+  };
+
+  if constexpr (ONE) {
+    // the common case, straight-line: X is copied once and coded in place
+    pass1(0, 0, K);
+    finish_scales();
+    pass2(0, 0, K, false);
+  } else {
+    for (int sg = 0; sg < nseg; ++sg) pass1(sg, sg * kSeg, seg_len(sg));
+    finish_scales();
+    for (int sg = 0; sg < nseg; ++sg) pass2(sg, sg * kSeg, seg_len(sg), true);
   }
 
-  // ---- sum the streamers' partial tiles, epilogue.  acc register r of lane
-  // (lr, lg) is D[n = 4*lg + r][m = lr].
-  if (wave < kStreamers) part[wave][lane] = acc;
+  // ---- partial tiles and code sums meet in LDS; wave 0 applies the epilogue
+  part[wave][lane] = acc;
+  __syncthreads();
+  {
+    const int r = reduce_rows(add_int);
+    if ((tid & 15) == 0) rsum[tid >> 4] = r;
+  }
   __syncthreads();
   if (wave == 0) {
     v4i t = part[0][lane];
 #pragma unroll
-    for (int w = 1; w < kStreamers; ++w) t += part[w][lane];
+    for (int w = 1; w < kWaves; ++w) t += part[w][lane];
     const int m = lr;
     if (m < M) {
-      const float s_m = sx[m];
+      const float s_m = row_scale(m);
       const int r_m = rsum[m];
+      // The factors are first used here: the empty asm keeps their uses
+      // (the zero point's conversion would otherwise be hoisted next to its
+      // load, making the weight stream wait for the factor loads).
+#pragma unroll
+      for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(fsc[r]), "+v"(fzp[r]), "+v"(fbi[r]));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t n = n0 + lg * 4 + r;
+        const int n = n0 + lg * 4 + r;
         if (n < N) {
           const int a = t[r];
-          if (acc_out) acc_out[(int64_t)m * N + n] = a;
-          const int c = a - (int)w_zp[n] * r_m;
-          float v = (s_m * w_scale[n]) * (float)c;
-          if (bias) v += bias[n];
-          store_out<YDT>(y, (int64_t)m * N + n, v);
+          if (acc_out) acc_out[(size_t)m * N + n] = a;
+          const int c = a - (int)fzp[r] * r_m;
+          float v = (s_m * fsc[r]) * (float)c;
+          if (bias) v += fbi[r];
+          store_out<YDT>(y, (size_t)m * N + n, v);
         }
       }
     }
@@ -223,11 +297,17 @@ hipError_t launch_dt(const void* x, int64_t M, int64_t K, const int8_t* wq, cons
                      const float* wz, int64_t N, const float* bias, void* y, int ydt, int32_t* acc_out,
                      hipStream_t st) {
   dim3 grid((unsigned)((N + kRows - 1) / kRows)), block(kThreads);
+  const int m = (int)M, k = (int)K, n = (int)N;
+  const bool one = K <= kSeg;
+#define Q8_GEMV(YT)                                                                                     \
+  (one ? (k_gemv_i8<DT, YT, true><<<grid, block, 0, st>>>(x, m, k, wq, ws, wz, n, bias, y, acc_out))   \
+       : (k_gemv_i8<DT, YT, false><<<grid, block, 0, st>>>(x, m, k, wq, ws, wz, n, bias, y, acc_out)))
   switch (ydt) {
-    case DT_F32: k_gemv_i8<DT, DT_F32><<<grid, block, 0, st>>>(x, (int)M, K, wq, ws, wz, N, bias, y, acc_out); break;
-    case DT_F16: k_gemv_i8<DT, DT_F16><<<grid, block, 0, st>>>(x, (int)M, K, wq, ws, wz, N, bias, y, acc_out); break;
-    default: k_gemv_i8<DT, DT_BF16><<<grid, block, 0, st>>>(x, (int)M, K, wq, ws, wz, N, bias, y, acc_out); break;
+    case DT_F32: Q8_GEMV(DT_F32); break;
+    case DT_F16: Q8_GEMV(DT_F16); break;
+    default: Q8_GEMV(DT_BF16); break;
   }
+#undef Q8_GEMV
   return hipGetLastError();
 }
 

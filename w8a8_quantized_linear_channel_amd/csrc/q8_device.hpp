@@ -76,20 +76,44 @@ template <> __device__ __forceinline__ void store_out<DT_BF16>(void* y, int64_t 
 }
 
 // Wave64 reductions (butterfly over all 64 lanes).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Wave-wide reductions; every lane gets the result.  Four DPP steps reduce
+// each row of 16 lanes (quad_perm [1,0,3,2] and [2,3,0,1] pair lanes within a
+// quad, row_half_mirror pairs the two quads of each half-row, row_mirror the
+// two halves of the row); the four row results are then read as scalars.
+// DPP moves run in the VALU, unlike a ds_bpermute butterfly whose six steps
+// each wait on the LDS crossbar.
+template <typename Op>
+__device__ __forceinline__ int dpp_row_reduce(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
   return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  const int r = dpp_row_reduce(__float_as_int(v), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  });
+  const float a = __int_as_float(__builtin_amdgcn_readlane(r, 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(r, 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(r, 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(r, 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+  const int r = dpp_row_reduce(__float_as_int(v), [](int a, int b) {
+    return __float_as_int(fminf(__int_as_float(a), __int_as_float(b)));
+  });
+  const float a = __int_as_float(__builtin_amdgcn_readlane(r, 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(r, 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(r, 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(r, 48));
+  return fminf(fminf(a, b), fminf(c, d));
 }
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  const int r = dpp_row_reduce(v, [](int a, int b) { return a + b; });
+  return __builtin_amdgcn_readlane(r, 0) + __builtin_amdgcn_readlane(r, 16) +
+         __builtin_amdgcn_readlane(r, 32) + __builtin_amdgcn_readlane(r, 48);
 }
 
 // Block-wide reductions for blocks of NW waves; `red` is LDS of >= NW slots.
@@ -181,5 +205,30 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
          ((uint32_t)(d & 0xff) << 24);
 }
+
+// s_waitcnt immediate for lgkmcnt(0) alone on gfx9: vmcnt 63 (bits 3:0 and
+// 15:14), expcnt 7 (bits 6:4), lgkmcnt 0 (bits 11:8)
+constexpr int kLgkmcnt0 = 0xC07F;
+
+typedef __attribute__((address_space(3))) void* lptr_t;   // LDS
+
+// global_load_lds_dwordx4: 64 lanes x 16 bytes from gbase + voff (per lane)
+// into 1 KB of LDS at `lds` (lane l at lds + 16 l), counted by vmcnt.  Issued
+// as inline asm on purpose: the compiler's own wait insertion cannot tell the
+// LDS a DMA fills from the LDS other reads come from and would put a
+// vmcnt(0) before every LDS read, draining any prefetch.  Callers wait for
+// the DMA themselves (s_waitcnt vmcnt, plus a barrier when other waves read
+// the data).  M0 carries the LDS address; nothing else in these kernels uses
+// M0, and the s_nop covers the M0-write -> LDS-DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 }  // namespace q8

@@ -10,8 +10,15 @@ hipError_t launch_quant_weight_i8(const void* w, int dt, int64_t N, int64_t K, i
                                   float* w_scale, float* w_zp, hipStream_t st);
 hipError_t launch_quant_rows_fp8(const void* x, int dt, int64_t R, int64_t K, float bound,
                                  uint8_t* xq, float* x_scale, hipStream_t st);
-hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, const uint8_t* colflag,
-                               int8_t* xq, float* x_scale, int32_t* x_rowsum, hipStream_t st);
+hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, int8_t* xq, float* x_scale,
+                               int32_t* x_rowsum, hipStream_t st);
+// fp16 activations of the LLM.int8 step: columns with flags[k] != 0 read as 0
+// (flags may be null: none); also writes the ascending outlier list idx[] and
+// its count cnt[0] (and copies to user_idx / user_cnt when not null).
+hipError_t launch_quant_act_f16_outliers(const uint16_t* x, int64_t M, int64_t K, const uint8_t* flags,
+                                         int8_t* xq, float* x_scale, int32_t* x_rowsum, int32_t* idx,
+                                         int32_t* cnt, int32_t* user_idx, int32_t* user_cnt,
+                                         hipStream_t st);
 
 // Operands and epilogue inputs of the MFMA GEMM (gemm.hip).
 struct GemmArgs {
@@ -41,10 +48,9 @@ hipError_t launch_gemv_i8(const void* x, int xdt, int64_t M, int64_t K, const in
                           void* y, int ydt, int32_t* acc_out, hipStream_t st);
 constexpr int64_t kGemvMaxM = 16;
 
-// LLM.int8 outlier detection (decomp.hip).  partial: [ceil(M/64), K] floats.
-hipError_t launch_outlier_detect(const uint16_t* x_f16, int64_t M, int64_t K, float threshold,
-                                 float* partial, uint8_t* flags, int32_t* idx, int32_t* cnt,
-                                 int32_t* user_idx, int32_t* user_cnt, hipStream_t st);
-constexpr int64_t kColmaxRows = 64;
+// LLM.int8 outlier columns (decomp.hip): flags[k] = max_m |x[m,k]| >= threshold
+// (threshold > 0).
+hipError_t launch_outlier_flags(const uint16_t* x_f16, int64_t M, int64_t K, float threshold, uint8_t* flags,
+                                hipStream_t st);
 
 }  // namespace q8

@@ -2,16 +2,18 @@
 // and per-token activations (INT8 symmetric with the code row-sum, FP8 e4m3
 // with the activation-scale upper bound).
 //
-// Weights (offline, once per model): one 256-thread workgroup per row, IEEE
-// division for every code.  Activations (every forward, HBM-bound): one wave
-// per row, four rows per 256-thread workgroup, no workgroup barriers; each
-// lane keeps its 16-byte chunks of the row in registers so the row is read
-// from HBM once, the absmax is a wave reduction, and the codes are emitted
-// from the registers.  For 16-bit inputs the quotient x / S comes from two
-// FMAs on RN(1/S) (same codes as the division over that whole input domain),
-// the integer rounding from adding 1.5 * 2^23, the byte packing from v_perm
-// and the code row sum from v_dot4.  Per row: K * sizeof(in) bytes in, K
-// bytes + 8 bytes of metadata out.
+// One 256-thread workgroup per row.  Each thread keeps its 16-byte chunks of
+// the row (chunks tid, tid + 256, ...) in registers, so the row is read from
+// HBM once; the absmax (or min/max) is a DPP wave reduction plus four LDS
+// slots, and the codes are emitted from the registers, 8 or 4 bytes per
+// chunk, consecutive threads writing consecutive bytes.  Many short
+// workgroups per CU keep enough loads in flight to approach HBM bandwidth
+// even when there are few rows.  Weights (offline) use IEEE division for
+// every code.  Activations: for 16-bit inputs the quotient x / S comes from
+// two FMAs on RN(1/S) (same codes as the division over that whole input
+// domain), the integer rounding from adding 1.5 * 2^23, the byte packing from
+// v_perm and the code row sum from v_dot4.  Per row: K * sizeof(in) bytes in,
+// K bytes + 8 bytes of metadata out.
 #include "q8_device.hpp"
 #include "q8_kernels.hpp"
 
@@ -109,146 +111,199 @@ __global__ __launch_bounds__(kThreads) void k_quant_weight_i8(const void* __rest
   if (tid == 0) { w_scale[n] = s; w_zp[n] = z; }
 }
 
-// ---------------------------------------------------------------- one wave per row
-constexpr int kRowsPerBlock = kThreads / 64;
-
-// Chunk loads for a row handled by one wave: lane l owns chunks l, l+64, ...
-// of which the first CACHE stay in registers.
-template <int DT, int CACHE>
-struct WaveRow {
-  static constexpr int E = Chunk<DT>::kElems;
-  v4i cache[CACHE];
-  template <class F>
-  __device__ __forceinline__ void load(const void* base, int64_t row, int nch, int lane, F&& each) {
-#pragma unroll
-    for (int j = 0; j < CACHE; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nch) {
-        cache[j] = load_chunk<DT>(base, row, c);
-        each(cache[j], c);
-      }
-    }
-    for (int c = lane + 64 * CACHE; c < nch; c += 64) each(load_chunk<DT>(base, row, c), c);
-  }
-  template <class F>
-  __device__ __forceinline__ void replay(const void* base, int64_t row, int nch, int lane, F&& each) {
-#pragma unroll
-    for (int j = 0; j < CACHE; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nch) each(cache[j], c);
-    }
-    for (int c = lane + 64 * CACHE; c < nch; c += 64) each(load_chunk<DT>(base, row, c), c);
-  }
+// ---------------------------------------------------------------- rows (activations; FP8 weights)
+enum RowMode : int {
+  RM_I8 = 0,         // INT8 symmetric, S = absmax / 127, code row sums
+  RM_I8_OUTLIER = 1, // as RM_I8 (fp16 only) with the flagged outlier columns read as 0
+  RM_FP8 = 2,        // e4m3, S = min(absmax, bound) / 448
 };
+constexpr int kRowCache = 8;   // chunks per thread held in registers: 16-bit rows up to 16384 values
 
-// ---------------------------------------------------------------- rows -> FP8 e4m3 (weights and activations)
-// bound: activation scale upper bound on the row absmax (+inf for none).
-template <int DT, int CACHE>
-__global__ __launch_bounds__(kThreads) void k_quant_rows_fp8(const void* __restrict__ x, int64_t R, int64_t K,
-                                                             float bound, uint8_t* __restrict__ xq,
-                                                             float* __restrict__ x_scale) {
+// RM_I8_OUTLIER: the outlier columns (flags[k] != 0) are left out of the row
+// absmax and get code 0 (their product goes through the fp16 outlier flow);
+// each chunk's 8 flag bytes are one 8-byte load issued with the chunk, and
+// chunks that no lane of the wave flags skip the masking.  One extra
+// workgroup (the last) compacts the flags into the ascending list of outlier
+// columns and its count (for the GEMM's outlier flow and the caller) while
+// the others quantize; flags == NULL means no outlier columns.
+// At least 4 waves per SIMD (<= 128 VGPRs): several rows per CU keep loads in flight.
+template <int MODE, int DT>
+__global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
+    const void* __restrict__ x, int64_t R, int64_t K, const uint8_t* __restrict__ flags, float bound,
+    uint8_t* __restrict__ xq, float* __restrict__ x_scale, int32_t* __restrict__ x_rowsum,
+    int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int32_t* __restrict__ user_idx,
+    int32_t* __restrict__ user_cnt) {
   constexpr int E = Chunk<DT>::kElems;
-  const int lane = threadIdx.x & 63;
-  const int64_t m = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (m >= R) return;                                  // whole wave
-  const int nch = (int)(K / E);
-  const int64_t row = m * K;
-  WaveRow<DT, CACHE> wr;
-  float amax = 0.0f;
-  wr.load(x, row, nch, lane, [&](const v4i& ch, int) {
-    float v[E];
-    Chunk<DT>::decode(ch, v);
+  __shared__ float redf[kWaves];
+  __shared__ int redi[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if constexpr (MODE == RM_I8_OUTLIER) {
+    if (blockIdx.x == gridDim.x - 1) {
+      // Thread t owns the run [t*per, (t+1)*per) of 16-byte flag blocks (K is
+      // a multiple of 16); a block prefix sum of the runs' counts places every
+      // flagged column in ascending order.
+      int total = 0;
+      if (flags != nullptr) {
+        const int per = 16 * (int)((K + 16 * kThreads - 1) / (16 * kThreads));
+        const int c0 = tid * per;
+        int mine = 0;
+        for (int c = c0; c < c0 + per && c < (int)K; c += 16) {
+          const v4i f = *(const v4i*)(flags + c);
 #pragma unroll
-    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  });
-  amax = wave_max(amax);
-  const float a = fminf(amax, bound);
-  float s = a / kFp8Max;
-  s = s < kEps ? kEps : s;
-  const float r = 1.0f / s;
-  // the two-FMA quotient is used where the scale comes from a 16-bit row absmax
-  const bool fast = (DT != DT_F32) && (amax <= bound);
-  wr.replay(x, row, nch, lane, [&](const v4i& ch, int c) {
-    float v[E];
-    Chunk<DT>::decode(ch, v);
-    uint32_t words[E / 4];
+          for (int i = 0; i < 4; ++i) mine = sum_i8x4((uint32_t)f[i], mine);   // bytes are 0 or 1
+        }
+        int incl = mine;
 #pragma unroll
-    for (int g = 0; g < E / 4; ++g) {
-      float q[4];
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        if (lane == 63) redi[wave] = incl;
+        __syncthreads();
+        int before = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xv = v[4 * g + e];
-        const float y = fast ? __builtin_copysignf(quot_fma(xv, s, r), xv) : xv / s;
-        q[e] = fminf(fmaxf(y, -kFp8Max), kFp8Max);
+        for (int w = 0; w < kWaves; ++w) {
+          if (w < wave) before += redi[w];
+          total += redi[w];
+        }
+        int pos = before + incl - mine;
+        if (mine > 0) {
+          for (int c = c0; c < c0 + per && c < (int)K; c += 16) {
+            const v4i f = *(const v4i*)(flags + c);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (((uint32_t)f[e >> 2] >> (8 * (e & 3))) & 0xffu) {
+                idx[pos] = c + e;
+                if (user_idx) user_idx[pos] = c + e;
+                ++pos;
+              }
+          }
+        }
       }
-      words[g] = pack4_e4m3(q[0], q[1], q[2], q[3]);
+      if (tid == 0) {
+        *cnt = total;
+        if (user_cnt) *user_cnt = total;
+      }
+      return;
     }
-    store_codes<E>(xq, row + (int64_t)c * E, words);
-  });
-  if (lane == 0) x_scale[m] = s;
-}
+  }
 
-// ---------------------------------------------------------------- activations, INT8 sym (+ row sum)
-// colflag (nullable, [K] bytes): nonzero marks a column whose values are
-// treated as 0 (the outlier columns of the mixed-precision decomposition).
-template <int DT, int CACHE>
-__global__ __launch_bounds__(kThreads) void k_quant_act_i8(const void* __restrict__ x, int64_t M, int64_t K,
-                                                           const uint8_t* __restrict__ colflag,
-                                                           int8_t* __restrict__ xq,
-                                                           float* __restrict__ x_scale,
-                                                           int32_t* __restrict__ x_rowsum) {
-  constexpr int E = Chunk<DT>::kElems;
-  const int lane = threadIdx.x & 63;
-  const int64_t m = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (m >= M) return;                                  // whole wave
+  const int64_t m = blockIdx.x;
   const int nch = (int)(K / E);
   const int64_t row = m * K;
-  auto decode_masked = [&](const v4i& ch, int c, float* v) {
+  const bool masked = MODE == RM_I8_OUTLIER && flags != nullptr;
+  auto flag_word = [&](int c) -> uint64_t {
+    if constexpr (MODE == RM_I8_OUTLIER) return masked ? *(const uint64_t*)(flags + (int64_t)c * 8) : 0;
+    return 0;
+  };
+  auto values = [&](const v4i& ch, uint64_t f, float* v) {
     Chunk<DT>::decode(ch, v);
-    if (colflag != nullptr) {
-      const uint8_t* f = colflag + (int64_t)c * E;
+    if constexpr (MODE == RM_I8_OUTLIER) {
+      if (__any(f != 0)) {
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (f[e]) v[e] = 0.0f;
+        for (int e = 0; e < E; ++e)
+          if ((f >> (8 * e)) & 0xffu) v[e] = 0.0f;
+      }
     }
   };
-  WaveRow<DT, CACHE> wr;
+
+  v4i d[kRowCache];
+  uint64_t fw[kRowCache];
+#pragma unroll
+  for (int j = 0; j < kRowCache; ++j) {
+    const int c = tid + kThreads * j;
+    if (c < nch) {
+      d[j] = load_chunk<DT>(x, row, c);
+      fw[j] = flag_word(c);
+    }
+  }
   float amax = 0.0f;
-  wr.load(x, row, nch, lane, [&](const v4i& ch, int c) {
+  auto take_max = [&](const v4i& ch, uint64_t f) {
     float v[E];
-    decode_masked(ch, c, v);
+    values(ch, f, v);
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  });
-  amax = wave_max(amax);
-  float s = amax / 127.0f;
+  };
+#pragma unroll
+  for (int j = 0; j < kRowCache; ++j)
+    if (tid + kThreads * j < nch) take_max(d[j], fw[j]);
+  for (int c = tid + kThreads * kRowCache; c < nch; c += kThreads) take_max(load_chunk<DT>(x, row, c), flag_word(c));
+  amax = block_max<kWaves>(amax, redf);
+
+  float s;
+  bool fast;   // the two-FMA quotient applies where the scale comes from a 16-bit row absmax
+  if constexpr (MODE == RM_FP8) {
+    const float a = fminf(amax, bound);
+    s = a / kFp8Max;
+    fast = (DT != DT_F32) && (amax <= bound);
+  } else {
+    s = amax / 127.0f;
+    fast = DT != DT_F32;
+  }
   s = s < kEps ? kEps : s;
   const float r = 1.0f / s;
   int qsum = 0;
-  // |x / s| <= 127 (s = absmax/127 rounded, or the 1e-8 floor), so the codes
-  // need no clamp and the 1.5 * 2^23 rounding applies.
-  wr.replay(x, row, nch, lane, [&](const v4i& ch, int c) {
+  auto emit = [&](const v4i& ch, uint64_t f, int c) {
     float v[E];
-    decode_masked(ch, c, v);
+    values(ch, f, v);
     uint32_t words[E / 4];
 #pragma unroll
     for (int g = 0; g < E / 4; ++g) {
-      uint32_t b[4];
+      if constexpr (MODE == RM_FP8) {
+        float q[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xv = v[4 * g + e];
-        const float y = (DT == DT_F32) ? xv / s : quot_fma(xv, s, r);
-        b[e] = rne_int8_bits(y);
+        for (int e = 0; e < 4; ++e) {
+          const float xv = v[4 * g + e];
+          const float y = fast ? __builtin_copysignf(quot_fma(xv, s, r), xv) : xv / s;
+          q[e] = fminf(fmaxf(y, -kFp8Max), kFp8Max);
+        }
+        words[g] = pack4_e4m3(q[0], q[1], q[2], q[3]);
+      } else {
+        // |x / s| <= 127 (s = absmax/127 rounded, or the 1e-8 floor), so the
+        // codes need no clamp and the 1.5 * 2^23 rounding applies
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xv = v[4 * g + e];
+          b[e] = rne_int8_bits(fast ? quot_fma(xv, s, r) : xv / s);
+        }
+        words[g] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
+        qsum = sum_i8x4(words[g], qsum);
       }
-      words[g] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
-      qsum = sum_i8x4(words[g], qsum);
     }
     store_codes<E>(xq, row + (int64_t)c * E, words);
-  });
-  qsum = wave_sum(qsum);
-  if (lane == 0) {
+  };
+#pragma unroll
+  for (int j = 0; j < kRowCache; ++j) {
+    const int c = tid + kThreads * j;
+    if (c < nch) emit(d[j], fw[j], c);
+  }
+  for (int c = tid + kThreads * kRowCache; c < nch; c += kThreads) emit(load_chunk<DT>(x, row, c), flag_word(c), c);
+  if constexpr (MODE != RM_FP8) qsum = block_sum<kWaves>(qsum, redi);
+  if (tid == 0) {
     x_scale[m] = s;
-    if (x_rowsum) x_rowsum[m] = qsum;
+    if (MODE != RM_FP8 && x_rowsum) x_rowsum[m] = qsum;
+  }
+}
+
+template <int MODE>
+void launch_rows(const void* x, int dt, int64_t R, int64_t K, const uint8_t* flags, float bound, uint8_t* xq,
+                 float* x_scale, int32_t* x_rowsum, int32_t* idx, int32_t* cnt, int32_t* user_idx,
+                 int32_t* user_cnt, unsigned grid, hipStream_t st) {
+  switch (dt) {
+    case DT_F32:
+      k_quant_rows<MODE, DT_F32><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
+                                                            cnt, user_idx, user_cnt);
+      break;
+    case DT_F16:
+      k_quant_rows<MODE, DT_F16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
+                                                            cnt, user_idx, user_cnt);
+      break;
+    default:
+      k_quant_rows<MODE, DT_BF16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
+                                                             cnt, user_idx, user_cnt);
+      break;
   }
 }
 
@@ -267,45 +322,25 @@ hipError_t launch_quant_weight_i8(const void* w, int dt, int64_t N, int64_t K, i
 
 hipError_t launch_quant_rows_fp8(const void* x, int dt, int64_t R, int64_t K, float bound,
                                  uint8_t* xq, float* x_scale, hipStream_t st) {
-  dim3 grid((unsigned)((R + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
-  const int64_t per_lane = K / (dt == DT_F32 ? 4 : 8) / 64;
-  const bool big = per_lane > 8;
-  switch (dt) {
-    case DT_F32:
-      if (big) k_quant_rows_fp8<DT_F32, 32><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
-      else k_quant_rows_fp8<DT_F32, 8><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
-      break;
-    case DT_F16:
-      if (big) k_quant_rows_fp8<DT_F16, 32><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
-      else k_quant_rows_fp8<DT_F16, 8><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
-      break;
-    default:
-      if (big) k_quant_rows_fp8<DT_BF16, 32><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
-      else k_quant_rows_fp8<DT_BF16, 8><<<grid, block, 0, st>>>(x, R, K, bound, xq, x_scale);
-      break;
-  }
+  launch_rows<RM_FP8>(x, dt, R, K, nullptr, bound, xq, x_scale, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      (unsigned)R, st);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, const uint8_t* colflag,
-                               int8_t* xq, float* x_scale, int32_t* x_rowsum, hipStream_t st) {
-  dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(kThreads);
-  const int64_t per_lane = K / (dt == DT_F32 ? 4 : 8) / 64;
-  const bool big = per_lane > 8;
-  switch (dt) {
-    case DT_F32:
-      if (big) k_quant_act_i8<DT_F32, 32><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
-      else k_quant_act_i8<DT_F32, 8><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
-      break;
-    case DT_F16:
-      if (big) k_quant_act_i8<DT_F16, 32><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
-      else k_quant_act_i8<DT_F16, 8><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
-      break;
-    default:
-      if (big) k_quant_act_i8<DT_BF16, 32><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
-      else k_quant_act_i8<DT_BF16, 8><<<grid, block, 0, st>>>(x, M, K, colflag, xq, x_scale, x_rowsum);
-      break;
-  }
+hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, int8_t* xq, float* x_scale,
+                               int32_t* x_rowsum, hipStream_t st) {
+  launch_rows<RM_I8>(x, dt, M, K, nullptr, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, nullptr, nullptr, nullptr,
+                     nullptr, (unsigned)M, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_f16_outliers(const uint16_t* x, int64_t M, int64_t K, const uint8_t* flags,
+                                         int8_t* xq, float* x_scale, int32_t* x_rowsum, int32_t* idx,
+                                         int32_t* cnt, int32_t* user_idx, int32_t* user_cnt,
+                                         hipStream_t st) {
+  // one workgroup per row, plus the compaction workgroup
+  k_quant_rows<RM_I8_OUTLIER, DT_F16><<<(unsigned)(M + 1), kThreads, 0, st>>>(
+      x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt);
   return hipGetLastError();
 }
 
