@@ -85,6 +85,12 @@ struct MmaF8 {                       // v_mfma_f32_32x32x64_f8f6f4, both operand
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
   }
 };
+// The 32-bit pattern of an accumulator element, taken by value: a bit_cast
+// applied directly to an element of an ext_vector_type is lowered to a read
+// of element 0 by this compiler.
+__device__ __forceinline__ int raw32(int x) { return x; }
+__device__ __forceinline__ int raw32(float x) { return __float_as_int(x); }
+
 // 32 x 32 output fragment layout (all 32x32 MFMAs): register r of lane l is
 // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 __device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
@@ -146,6 +152,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+
+  // Epilogue factors, loaded now and parked in registers (thread t: row m0+t
+  // and column n0+t of the tile), so their latency is long over when the
+  // epilogue puts them in LDS.
+  float pf_sx = 0.0f, pf_sb = 0.0f, pf_bb = 0.0f;
+  int pf_rs = 0, pf_zi = 0;
+  if (tid < BM) {
+    const int m = m0 + tid < M ? m0 + tid : M - 1;
+    pf_sx = g.a_scale[m];
+    if constexpr (KIND != GEMM_FP8) pf_rs = g.a_rowsum[m];
+  }
+  if (tid < BN) {
+    const int n = n0 + tid < N ? n0 + tid : N - 1;
+    pf_sb = g.b_scale[n];
+    if constexpr (KIND != GEMM_FP8) pf_zi = (int)g.b_zp[n];
+    pf_bb = g.bias ? g.bias[n] : 0.0f;
+  }
 
   // ---- DMA loader.  One wave instruction fills 1 KB = 16 LDS rows; lane l
   // lands at row l/4, physical chunk l%4, which holds logical chunk
@@ -356,10 +379,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   // ---- epilogue.  The weight fragment is the MFMA's first operand, so
   // fragment (i, j) holds D[n][m]: register r of lane l is output
   // m = mw + i*32 + l%32, n = nw + j*32 + out_row(r, l); registers 4q..4q+3
-  // are four consecutive n of one m.  Factors go through LDS once; each
-  // wave then converts one 32-row slab at a time into a padded LDS staging
-  // tile (four values per 8-byte write) and stores it back row-contiguous.
-  const int mw = wm * TL::TM, nw = wn * TL::TN;        // wave offsets inside the tile
+  // are four consecutive n of one m.  Each wave moves one 32-row slab at a
+  // time through a padded LDS staging tile as raw accumulators (16-byte
+  // writes, no arithmetic), reads it back row-contiguous -- lane l then
+  // always holds the same 8 columns, 8*(l % (TN/8)) .. +7, whose factors it
+  // keeps in registers -- applies the dequantization there, and stores 16
+  // bytes per lane (two rows of 256 bytes per instruction at TN = 128).
+  const int mw = wm * TL::TM, nw = wn * TL::TN;
   const int lm = lane & 31, lh = lane >> 5;
   constexpr int kFacBytes = ((2 * BM + 3 * BN) * 4 + 15) / 16 * 16;
   float* const f_sx = (float*)smem;                     // [BM]
@@ -368,17 +394,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   int* const f_zi = (int*)(f_sb + BN);                  // [BN] zero points (exact integers)
   float* const f_bb = (float*)(f_zi + BN);              // [BN]
   __syncthreads();                                      // the main loop's LDS reads are done
-  if (tid < BM) {
-    const int m = m0 + tid < M ? m0 + tid : M - 1;
-    f_sx[tid] = g.a_scale[m];
-    if constexpr (KIND != GEMM_FP8) f_rs[tid] = g.a_rowsum[m];
-  }
-  if (tid < BN) {
-    const int n = n0 + tid < N ? n0 + tid : N - 1;
-    f_sb[tid] = g.b_scale[n];
-    f_zi[tid] = KIND != GEMM_FP8 ? (int)g.b_zp[n] : 0;
-    f_bb[tid] = g.bias ? g.bias[n] : 0.0f;
-  }
+  if (tid < BM) { f_sx[tid] = pf_sx; f_rs[tid] = pf_rs; }
+  if (tid < BN) { f_sb[tid] = pf_sb; f_zi[tid] = pf_zi; f_bb[tid] = pf_bb; }
   __syncthreads();
 
   if constexpr (KIND == GEMM_INT8_DECOMP) {
@@ -442,98 +459,102 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
     }
   }
 
-  // Slab i of the wave (32 rows m, TN columns n) through the wave's LDS
-  // staging tile, row pitch TN*ES + 8 bytes (the pad spreads the 32 rows of
-  // one 8-byte write over all banks), then row-contiguous 8-byte stores to
-  // dst ([M, N] of ES-byte elements).  words(j, q) gives the four values
-  // n = nw + j*32 + 8q + 4*(lane/32) + 0..3 of row m = mw + i*32 + lane%32 as
-  // ES-byte elements packed into 32-bit words.
-  auto emit = [&](auto ESC, int i, auto&& words, uint8_t* dst) {
-    constexpr int ES = decltype(ESC)::value;
-    constexpr int kPitch = TL::TN * ES + 8;
-    constexpr int kChunks = TL::TN * ES / 8;             // 8-byte chunks per staged row
-    // each wave owns a fixed region sized for the widest pitch, so regions
-    // of different waves never overlap whatever each one is staging
-    constexpr int kWaveStage = 32 * (TL::TN * 4 + 8);
-    static_assert(kPitch * 32 <= kWaveStage, "staging pitch");
-    static_assert(kFacBytes + 4 * kWaveStage <= kStages * kStageBytes, "epilogue staging does not fit");
-    uint8_t* const stg = smem + kFacBytes + wave * kWaveStage;
+  // staging: per wave 32 rows of TN raw 32-bit values, pitch TN*4 + 16 bytes
+  // (16-byte aligned; the 16 rows of one 16-byte write fall in 16 different
+  // bank quarters)
+  constexpr int kPitch = TL::TN * 4 + 16;
+  constexpr int LPR = TL::TN / 8;                       // readback lanes per row
+  constexpr int RPI = 64 / LPR;                         // rows per readback instruction
+  static_assert(kFacBytes + 4 * 32 * kPitch <= kStages * kStageBytes, "epilogue staging does not fit");
+  uint8_t* const stg = smem + kFacBytes + wave * 32 * kPitch;
+  const int rc = lane % LPR, rr = lane / LPR;
+  const int ncl = nw + 8 * rc;                          // first of the lane's 8 columns in the tile
+  const int n = n0 + ncl;
+  // the lane's column factors
+  const v4f csb0 = *(const v4f*)(f_sb + ncl), csb1 = *(const v4f*)(f_sb + ncl + 4);
+  const v4f cbb0 = *(const v4f*)(f_bb + ncl), cbb1 = *(const v4f*)(f_bb + ncl + 4);
+  const v4i czi0 = *(const v4i*)(f_zi + ncl), czi1 = *(const v4i*)(f_zi + ncl + 4);
+  const float csb[8] = {csb0[0], csb0[1], csb0[2], csb0[3], csb1[0], csb1[1], csb1[2], csb1[3]};
+  const float cbb[8] = {cbb0[0], cbb0[1], cbb0[2], cbb0[3], cbb1[0], cbb1[1], cbb1[2], cbb1[3]};
+  const int czi[8] = {czi0[0], czi0[1], czi0[2], czi0[3], czi1[0], czi1[1], czi1[2], czi1[3]};
+  constexpr int ES = YDT == DT_F32 ? 4 : 2;
+  const bool vec = (N & 7) == 0;                        // 8-column groups start 16-byte aligned
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < TL::FN; ++j)
 #pragma unroll
       for (int q = 0; q < NR / 4; ++q) {
         const int cl = j * 32 + 8 * q + 4 * lh;
-        const v4i w = words(j, q);
-        uint8_t* p = stg + lm * kPitch + cl * ES;
-        *(v2i*)p = v2i{w[0], w[1]};
-        if constexpr (ES == 4) *(v2i*)(p + 8) = v2i{w[2], w[3]};
+        *(v4i*)(stg + lm * kPitch + cl * 4) = v4i{raw32(acc[i][j][4 * q]), raw32(acc[i][j][4 * q + 1]),
+                                                  raw32(acc[i][j][4 * q + 2]), raw32(acc[i][j][4 * q + 3])};
       }
-    const int mrow0 = m0 + mw + i * 32, ncol0 = n0 + nw;
-    if (((N * ES) & 7) == 0) {
-      // rows start 8-byte aligned, and a chunk (4 or 2 elements starting at a
-      // multiple of its length) is either wholly inside N or wholly outside
+    // the wave's own staging writes precede these reads (LDS is in order).
+    // All of the slab's readback reads and row factors are issued before any
+    // is used, so their LDS latency overlaps.
+    constexpr int TI = 32 / RPI;                        // readback instructions per slab
+    v4i ra[TI], rb[TI];
+    float rsx[TI];
+    int rrs[TI];
 #pragma unroll
-      for (int t = 0; t < 32 * kChunks / 64; ++t) {
-        const int id = t * 64 + lane, row = id / kChunks, ch = id % kChunks;
-        const int m = mrow0 + row, n = ncol0 + ch * (8 / ES);
-        const v2i d = *(const v2i*)(stg + row * kPitch + ch * 8);
-        if (m < M && n < N) *(v2i*)(dst + (size_t)(uint32_t)(m * N + n) * ES) = d;
-      }
-    } else {
-      for (int id = lane; id < 32 * TL::TN; id += 64) {
-        const int row = id / TL::TN, c = id % TL::TN;
-        const int m = mrow0 + row, n = ncol0 + c;
-        if (m >= M || n >= N) continue;
-        const size_t o = (size_t)(uint32_t)(m * N + n) * ES;
-        if constexpr (ES == 4) *(int*)(dst + o) = *(const int*)(stg + row * kPitch + c * 4);
-        else *(uint16_t*)(dst + o) = *(const uint16_t*)(stg + row * kPitch + c * 2);
-      }
+    for (int t = 0; t < TI; ++t) {
+      const int row = t * RPI + rr;
+      ra[t] = *(const v4i*)(stg + row * kPitch + rc * 32);
+      rb[t] = *(const v4i*)(stg + row * kPitch + rc * 32 + 16);
+      rsx[t] = f_sx[mw + i * 32 + row];
+      rrs[t] = KIND == GEMM_INT8 ? f_rs[mw + i * 32 + row] : 0;
     }
-    // LDS accesses of one wave complete in order, so the next slab may reuse
-    // the staging tile right away.
-  };
-  using E2 = std::integral_constant<int, 2>;
-  using E4 = std::integral_constant<int, 4>;
 #pragma unroll
-  for (int i = 0; i < TL::FM; ++i) {
-    if constexpr (KIND == GEMM_INT8) {
-      if (g.acc_out)
-        emit(E4{}, i, [&](int j, int q) {
-          return v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        }, (uint8_t*)g.acc_out);
-    }
-    const int ml = mw + i * 32 + lm;
-    const float sx = f_sx[ml];
-    int rs = 0;
-    if constexpr (KIND == GEMM_INT8) rs = f_rs[ml];
-    auto words = [&](int j, int q) {
-      const int nl = nw + j * 32 + 8 * q + 4 * lh;
-      const v4f sb = *(const v4f*)(f_sb + nl);
-      const v4f bb = *(const v4f*)(f_bb + nl);
-      float v[4];
+    for (int t = 0; t < TI; ++t) {
+      const int m = m0 + mw + i * 32 + t * RPI + rr;
+      const bool ok = m < M && n < N;
+      const int a[8] = {ra[t][0], ra[t][1], ra[t][2], ra[t][3], rb[t][0], rb[t][1], rb[t][2], rb[t][3]};
+      const size_t o = (size_t)(uint32_t)(m * N + n);
       if constexpr (KIND == GEMM_INT8) {
-        const v4i zb = *(const v4i*)(f_zi + nl);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (sx * sb[e]) * (float)(acc[i][j][4 * q + e] - zb[e] * rs) + bb[e];
-      } else if constexpr (KIND == GEMM_FP8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * (sx * sb[e]) + bb[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = __int_as_float(acc[i][j][4 * q + e]) + bb[e];
+        if (g.acc_out && ok) {
+          if (vec) {
+            *(v4i*)(g.acc_out + o) = ra[t];
+            *(v4i*)(g.acc_out + o + 4) = rb[t];
+          } else {
+            for (int e = 0; e < 8 && n + e < N; ++e) g.acc_out[o + e] = a[e];
+          }
+        }
       }
-      if constexpr (YDT == DT_F32) {
-        return v4i{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]), __float_as_int(v[3])};
-      } else {
-        uint32_t h[4];
+      const float sx = rsx[t];
+      float v[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = YDT == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
-        return v4i{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16)), 0, 0};
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (KIND == GEMM_INT8) {
+          v[e] = (sx * csb[e]) * (float)(a[e] - czi[e] * rrs[t]) + cbb[e];
+        } else if constexpr (KIND == GEMM_FP8) {
+          v[e] = __int_as_float(a[e]) * (sx * csb[e]) + cbb[e];
+        } else {
+          v[e] = __int_as_float(a[e]) + cbb[e];
+        }
       }
-    };
-    if constexpr (YDT == DT_F32) emit(E4{}, i, words, (uint8_t*)g.y);
-    else emit(E2{}, i, words, (uint8_t*)g.y);
+      if (!ok) continue;
+      if (vec) {
+        // the output is written once and not read back here: non-temporal stores
+        if constexpr (YDT == DT_F32) {
+          v4i* yp = (v4i*)((float*)g.y + o);
+          __builtin_nontemporal_store(v4i{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
+                                          __float_as_int(v[3])}, yp);
+          __builtin_nontemporal_store(v4i{__float_as_int(v[4]), __float_as_int(v[5]), __float_as_int(v[6]),
+                                          __float_as_int(v[7])}, yp + 1);
+        } else {
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = YDT == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
+          __builtin_nontemporal_store(v4i{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16)),
+                                          (int)(h[4] | (h[5] << 16)), (int)(h[6] | (h[7] << 16))},
+                                      (v4i*)((uint16_t*)g.y + o));
+        }
+      } else {
+        for (int e = 0; e < 8 && n + e < N; ++e) store_out<YDT>(g.y, o + e, v[e]);
+      }
+    }
   }
+  (void)ES;
 }
 
 // Output types: int8 GEMM f32 / f16 / bf16; the outlier flow f16 (the
