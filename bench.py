@@ -10,8 +10,11 @@ decode q_proj step (M = 16 and M = 1, N = K = 4096) in GB/s, the LLM.int8
 decomposition and the FP8 rowwise step, each with the roofline of its
 dominant kernel, and the CPU oracle timed on a bounded sample.
 
-Timing: W untimed warmup steps, then exactly K steps between two stream
-synchronizations, timed with HIP events on the stream the kernels run on.
+Timing: at least W untimed warm-up steps, continued until the leg has run
+for 60 ms (the shader clock climbs over the first tens of milliseconds of
+load; the JSON's `warmup` is the count actually run), then exactly K steps
+between two stream synchronizations, timed with HIP events on the stream the
+kernels run on.
 Inside the timed region every launch of the dominant kernel is bracketed by
 its own event pair; their mean is the kernel's average duration.  Decode
 steps (a few microseconds each) are captured into a HIP graph over 32
@@ -46,23 +49,48 @@ def ev():
     return torch.cuda.Event(enable_timing=True)
 
 
-def timed_steps(step, steps, warmup, kernel_pairs):
-    """Run warmup + `steps` steps; return (ms per step, mean ms of the
-    bracketed dominant kernel).  `step(i, pair)` must launch one step and
-    record pair[0]/pair[1] around the dominant kernel."""
+# The shader clock climbs for the first few tens of milliseconds of sustained
+# load (and again after the GPU idles): a quant+GEMM prefill step takes
+# ~170 us at first and settles at ~120 us after ~200 steps.  Every leg is
+# therefore warmed up until it has also run for WARM_MS, so that what is
+# timed is the steady state a serving loop sees.
+WARM_MS = 60.0
+
+
+def warm_up(step, warmup, min_ms=WARM_MS):
+    """Run `warmup` steps, then more (in groups of 8) until `min_ms` has
+    passed on the GPU; return (steps run, ms)."""
     dummy = (ev(), ev())
-    for i in range(warmup):
-        step(i, dummy)
+    t0, t1 = ev(), ev()
+    t0.record()
+    n = 0
+    while True:
+        for _ in range(max(1, warmup - n) if n < warmup else 8):
+            step(n, dummy)
+            n += 1
+        t1.record()
+        t1.synchronize()
+        if n >= warmup and t0.elapsed_time(t1) >= min_ms:
+            return n, t0.elapsed_time(t1)
+
+
+def timed_steps(step, steps, warmup, kernel_pairs):
+    """Warm up (at least `warmup` steps and WARM_MS), then time `steps` steps;
+    return (ms per step, mean ms of the bracketed dominant kernel, (warm-up
+    steps, warm-up ms)).  `step(i, pair)` must launch one step and record
+    pair[0]/pair[1] around the dominant kernel."""
+    warm = warm_up(step, warmup)
     torch.cuda.synchronize()
     t0, t1 = ev(), ev()
     t0.record()
+    dummy = (ev(), ev())
     for i in range(steps):
-        step(i, kernel_pairs[i])
+        step(i, kernel_pairs[i] if kernel_pairs else dummy)
     t1.record()
     torch.cuda.synchronize()
     total = t0.elapsed_time(t1)
-    kern = sum(a.elapsed_time(b) for a, b in kernel_pairs) / steps
-    return total / steps, kern
+    kern = sum(a.elapsed_time(b) for a, b in kernel_pairs) / steps if kernel_pairs else None
+    return total / steps, kern, warm
 
 
 # ------------------------------------------------------------------ prefill
@@ -84,7 +112,7 @@ def bench_prefill(dev, steps, warmup):
         pair[1].record()
 
     pairs = [(ev(), ev()) for _ in range(steps)]
-    ms, gemm_ms = timed_steps(step, steps, warmup, pairs)
+    ms, gemm_ms, warm = timed_steps(step, steps, warmup, pairs)
     ops = 2.0 * M * N * K
     res = {
         "ms_per_step": ms,
@@ -92,17 +120,17 @@ def bench_prefill(dev, steps, warmup):
         "gemm_us": gemm_ms * 1e3,
         "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
         "shape": (M, N, K),
+        "warm": warm,
         "host_inputs": (wl.x, wl.w),
     }
-    # act-quant kernel alone (HBM-bound): bytes = X bf16 in + codes out + 8 B/row
-    pairs = [(ev(), ev()) for _ in range(steps)]
-
+    # act-quant kernel alone (HBM-bound): bytes = X bf16 in + codes out + 8 B/row.
+    # Launched back to back with no event pair per launch (an event pair
+    # costs a few microseconds, as much as this kernel), so its time is the
+    # timed region's total over the launches.
     def qstep(i, pair):
-        pair[0].record()
         q8.q8_quantize_act(x, "int8_sym", out=(xq, xs, xr))
-        pair[1].record()
 
-    _, q_ms = timed_steps(qstep, steps, 2, pairs)
+    q_ms, _, _ = timed_steps(qstep, steps, 2, None)
     qbytes = M * K * 2 + M * K + 8 * M
     res["act_quant_us"] = q_ms * 1e3
     res["act_quant_gbs"] = qbytes / (q_ms * 1e-3) / 1e9
@@ -134,8 +162,7 @@ def bench_decode(dev, M, replays, copies=32):
         with torch.cuda.graph(g, stream=s):
             one_pass()
     torch.cuda.synchronize()
-    for _ in range(3):
-        g.replay()
+    warm_up(lambda i, pair: g.replay(), 3)
     torch.cuda.synchronize()
     t0, t1 = ev(), ev()
     t0.record()
@@ -169,7 +196,7 @@ def bench_decomp(dev, steps, warmup):
         pair[1].record()
 
     pairs = [(ev(), ev()) for _ in range(steps)]
-    ms, _ = timed_steps(step, steps, warmup, pairs)
+    ms, _, _ = timed_steps(step, steps, warmup, pairs)
     ops = 2.0 * M * N * K
     nbytes = N * K + 8 * N + M * K * 2 + M * N * 2
     t_ideal = max(ops / (PEAK_INT8_TOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
@@ -195,7 +222,7 @@ def bench_fp8(dev, steps, warmup):
         pair[1].record()
 
     pairs = [(ev(), ev()) for _ in range(steps)]
-    ms, gemm_ms = timed_steps(step, steps, warmup, pairs)
+    ms, gemm_ms, _ = timed_steps(step, steps, warmup, pairs)
     flops = 2.0 * M * N * K
     return {"M": M, "N": N, "K": K, "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
             "gemm_us": gemm_ms * 1e3,
@@ -229,7 +256,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="minimum warm-up steps per leg (each leg also warms up for %g ms)" % WARM_MS)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8"], default=None,
@@ -248,7 +276,8 @@ def main():
         M, N, K = pf["shape"]
         out.update({
             "value": round(pf["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(pf["ms_per_step"], 5),
+            "warmup": pf["warm"][0], "warmup_ms": round(pf["warm"][1], 1),
+            "ms_per_step": round(pf["ms_per_step"], 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
             "data": "synthetic: seeded numpy PCG64, X ~ N(0,1) in bf16, W ~ N(0,0.02) quantized once",
             "config": {"workload": "prefill FFN-up q8_linear (dynamic per-token int8 X, per-channel "
