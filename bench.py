@@ -147,7 +147,7 @@ def bench_decode(dev, M, replays, copies=32):
         w = wl.w if c == 0 else inputs.decode_weight_copy(c, N, K)
         weights.append(q8.q8_quantize_weight(w.to(dev), "int8_asym"))
     ys = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
-    wsp = torch.empty(1, dtype=torch.uint8, device=dev)
+    wsp = torch.empty(max(1, q8.q8_workspace_bytes("linear", M, N, K)), dtype=torch.uint8, device=dev)
 
     def one_pass():
         for c in range(copies):

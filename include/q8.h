@@ -120,12 +120,14 @@ q8_status q8_quantize_act(q8_format fmt, const void* x, q8_dtype x_dtype,
  * ([OV] §2.1 quantized matmul, read as Y = S_x X_q . (S_w (W_q - Z_w))^T):
  *     acc[m,n] = sum_k xq[m,k] wq[n,k]                      (exact int32)
  *     y[m,n]   = S_x[m] S_w[n] (acc[m,n] - Z_w[n] sum_k xq[m,k]) (+ bias[n])
- * The activation quantization is the Q8_INT8_SYM rule above, fused in.
+ * The activation quantization is the Q8_INT8_SYM rule above.  For M <= 10 it
+ * is fused into the one kernel; for larger M the codes, scales and code sums
+ * pass through the workspace (for M <= 16 into a streaming GEMV, above into
+ * the MFMA GEMM).
  * x: [M, K] of x_dtype (F32, F16, BF16); wq/w_scale/w_zp: from
  * q8_quantize_weight(Q8_INT8_ASYM); bias: float [N] or NULL; y: [M, N] of
  * y_dtype (F32, F16, BF16).  acc_out: int32 [M, N] debug copy of acc, or NULL.
- * workspace: q8_workspace_bytes(Q8_OP_LINEAR, M, N, K) bytes (0 for M <= 16,
- * where the activation quantization happens inside the one kernel).
+ * workspace: q8_workspace_bytes(Q8_OP_LINEAR, M, N, K) bytes (0 for M <= 10).
  */
 q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
                     const int8_t* wq, const float* w_scale, const float* w_zp,
@@ -184,7 +186,7 @@ q8_status q8_linear_fp8(const void* x, int64_t M, int64_t K, const uint8_t* wq,
  * ([NOTE] "INT8 这么小的范围不会导致溢出吗？": INT32 accumulation; [OV] §2.1
  * quantized matmul with r = S (q - Z)).  xq: int8 [M, K]; x_scale: float [M];
  * x_rowsum: int32 [M] (= sum_k xq, required); weights, bias, y, y_dtype and
- * acc_out as for q8_linear.  No workspace.  q8_linear with M > 16 is exactly
+ * acc_out as for q8_linear.  No workspace.  q8_linear with M > 10 is exactly
  * q8_quantize_act followed by this call.
  */
 q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_rowsum,

@@ -51,9 +51,12 @@ def test_status_strings():
 def test_workspace_sizes():
     L = _lib.lib()
     ws = lambda op, M, N, K: L.q8_workspace_bytes(op, M, N, K)  # noqa: E731
-    # decode: the activation quantization is fused, no workspace
-    for M in (1, 2, 4, 8, 16):
+    # decode up to 10 tokens: the activation quantization is fused, no workspace
+    for M in (1, 2, 4, 10):
         assert ws(_lib.Q8_OP_LINEAR, M, 4096, 4096) == 0
+    # 11..16 tokens: codes, scales and code sums for the streaming GEMV
+    for M in (11, 16):
+        assert ws(_lib.Q8_OP_LINEAR, M, 4096, 4096) == M * 4096 + 2 * 256
     # GEMM path: codes + scale + row sum, each 256-byte aligned
     assert ws(_lib.Q8_OP_LINEAR, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192
     assert ws(_lib.Q8_OP_FP8, 4096, 4096, 14336) == 4096 * 14336 + 16384
@@ -111,12 +114,14 @@ def test_linear_validation():
     assert call(K=100) == 2
     assert call(wz=None) == 1
     assert call(y=None) == 1
-    assert call(w=None) == 7                   # workspace needed for M > 16
+    assert call(w=None) == 7                   # workspace needed for M > 10
     assert call(wb=100) == 7
     assert call(b=MIS) == 6
     assert call(acc=MIS) == 6
-    # decode needs no workspace: with none given, the next check (alignment) decides
-    assert call(M=8, w=None, wb=0, y=MIS) == 6
+    assert call(M=11, w=None, wb=0) == 7
+    # decode up to 10 tokens needs no workspace: with none given, the next
+    # check (alignment) decides
+    assert call(M=10, w=None, wb=0, y=MIS) == 6
 
 
 def test_decomp_and_fp8_validation():

@@ -211,8 +211,8 @@ def run_linear_case(x, w, out_dtype, rows=None, bias=None, what=""):
     y_g = out_f64(y) if rows is None else out_f64(y)[rows]
     assert_equal(acc_g, inter["acc"].astype(np.int32), f"{what} INT32 accumulator")
     check_close(y_g, y_ref, f"{what} output")
-    if x.shape[0] > 16:
-        # q8_linear above the decode size is q8_quantize_act + q8_gemm_int8, bit for bit
+    if x.shape[0] > 10:
+        # q8_linear above 10 tokens is q8_quantize_act + q8_gemm_int8, bit for bit
         xq, xs, xr_ = q8.q8_quantize_act(g(x), "int8_sym")
         y2, acc2 = q8.q8_gemm_int8(xq, xs, xr_, wq, ws, wz, bias=b, out_dtype=out_dtype, acc_out=True)
         assert torch.equal(acc, acc2), f"{what}: q8_gemm_int8 accumulator differs"
@@ -240,10 +240,15 @@ def test_linear_decode_qproj_full_size(M):
     check_close(out_f64(y)[:, cols], y_ref, "output")
 
 
-@pytest.mark.parametrize("M,N,K,dt", [(3, 100, 4112, torch.bfloat16),      # two K segments, N tail
-                                      (16, 48, 16, torch.float32),          # smallest K
-                                      (7, 33, 208, torch.float16),          # partial MFMA k-step
-                                      (1, 1, 8192, torch.bfloat16)])
+@pytest.mark.parametrize("M,N,K,dt", [(3, 100, 4112, torch.bfloat16),      # fused: two K segments, N tail
+                                      (16, 48, 16, torch.float32),          # on codes: smallest K
+                                      (7, 33, 208, torch.float16),          # fused: partial MFMA k-step
+                                      (14, 33, 208, torch.float16),         # on codes: partial MFMA k-step
+                                      (1, 1, 8192, torch.bfloat16),         # fused: one output feature
+                                      (11, 100, 4112, torch.bfloat16),      # on codes, just above fused
+                                      (16, 37, 8240, torch.float16),        # on codes: two K segments, N tail
+                                      (13, 1, 64, torch.float32),           # on codes: one output feature
+                                      (10, 40, 4112, torch.float16)])       # fused, largest M
 def test_linear_decode_ragged(M, N, K, dt):
     log(f"[linear] decode ragged M={M} N={N} K={K} {dt}")
     x = inputs.random_matrix(30 + M, (M, K), 1.0, dt)
@@ -274,7 +279,7 @@ def test_linear_prefill_full_size_sampled():
     assert torch.equal(acc, acc2) and torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("M", [5, 200])
+@pytest.mark.parametrize("M", [5, 12, 200])
 def test_linear_bias_and_output_dtypes(M):
     log(f"[linear] bias + output dtypes M={M}")
     x = inputs.random_matrix(70, (M, 256), 1.0, torch.bfloat16)

@@ -47,10 +47,33 @@ struct Carve {
   }
 };
 
+// The int8 product and epilogue on quantized activations: the streaming GEMV
+// for decode-sized M, the MFMA GEMM tiles above.
+hipError_t int8_on_codes(const int8_t* xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                         const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N, const float* bias,
+                         void* y, q8_dtype y_dtype, int32_t* acc_out, hipStream_t st) {
+  if (M <= q8::kGemvMaxM)
+    return q8::launch_gemv_q8(xq, xs, rs, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st);
+  q8::GemmArgs g{};
+  g.a = reinterpret_cast<const uint8_t*>(xq);
+  g.b = reinterpret_cast<const uint8_t*>(wq);
+  g.a_scale = xs;
+  g.a_rowsum = rs;
+  g.b_scale = w_scale;
+  g.b_zp = w_zp;
+  g.bias = bias;
+  g.y = y;
+  g.acc_out = acc_out;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return q8::launch_gemm(q8::GEMM_INT8, g, y_dtype, st);
+}
+
 struct LinearWs { size_t xq, xs, rs, total; };
 LinearWs linear_ws(int64_t M, int64_t K) {
   LinearWs w{0, 0, 0, 0};
-  if (M <= q8::kGemvMaxM) return w;     // decode path: quantization is fused, no scratch
+  if (M <= q8::kGemvFusedMaxM) return w;   // fused decode path: the codes stay in LDS, no scratch
   Carve c;
   w.xq = c.take((size_t)M * K);
   w.xs = c.take((size_t)M * 4);
@@ -239,7 +262,7 @@ q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace, acc_out}));
 
-  if (M <= q8::kGemvMaxM)
+  if (M <= q8::kGemvFusedMaxM)
     return launched(q8::launch_gemv_i8(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype,
                                        acc_out, st));
 
@@ -248,20 +271,7 @@ q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const
   float* xs = reinterpret_cast<float*>(base + ws.xs);
   int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
   Q8_TRY(launched(q8::launch_quant_act_i8(x, x_dtype, M, K, xq, xs, rs, st)));
-  q8::GemmArgs g{};
-  g.a = reinterpret_cast<const uint8_t*>(xq);
-  g.b = reinterpret_cast<const uint8_t*>(wq);
-  g.a_scale = xs;
-  g.a_rowsum = rs;
-  g.b_scale = w_scale;
-  g.b_zp = w_zp;
-  g.bias = bias;
-  g.y = y;
-  g.acc_out = acc_out;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  return launched(q8::launch_gemm(q8::GEMM_INT8, g, y_dtype, st));
+  return launched(int8_on_codes(xq, xs, rs, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st));
 }
 
 q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_t* wq,
@@ -360,20 +370,7 @@ q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {xq, x_scale, x_rowsum, wq, w_scale, w_zp, bias, y, acc_out}));
-  q8::GemmArgs g{};
-  g.a = reinterpret_cast<const uint8_t*>(xq);
-  g.b = reinterpret_cast<const uint8_t*>(wq);
-  g.a_scale = x_scale;
-  g.a_rowsum = x_rowsum;
-  g.b_scale = w_scale;
-  g.b_zp = w_zp;
-  g.bias = bias;
-  g.y = y;
-  g.acc_out = acc_out;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  return launched(q8::launch_gemm(q8::GEMM_INT8, g, y_dtype, st));
+  return launched(int8_on_codes(xq, x_scale, x_rowsum, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st));
 }
 
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,

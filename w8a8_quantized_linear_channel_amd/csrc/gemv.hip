@@ -1,5 +1,7 @@
-// Decode-shaped W8A8 linear (M <= 16 tokens): one launch that quantizes the
-// activations per token and streams the int8 weights at HBM rate.
+// Decode-shaped W8A8 linear.  Up to ten tokens: one launch that quantizes the
+// activations per token and streams the int8 weights (k_gemv_i8, below).
+// From eleven to sixteen tokens the rows are quantized once by the row
+// quantizer and k_gemv_q8 (further down) streams weights against the codes.
 //
 // A workgroup owns 16 weight rows (output features) and all of K; the grid is
 // ceil(N / 16) workgroups (256 for the 4096-row q_proj, one per CU).  Its 4
@@ -7,8 +9,9 @@
 // columns [1024 w, 1024 w + 1024) for everything it does --
 //   * it first copies those columns of every X row into its own LDS region
 //     (global_load_lds, so no registers are held), then issues its 16
-//     16-byte weight loads (16 rows x 1024 bytes): the activations, which
-//     every workgroup reads, are not queued behind 64 KB of weight traffic;
+//     16-byte weight loads (16 rows x 1024 bytes, non-temporal buffer
+//     loads): the activations, which every workgroup reads, are not queued
+//     behind 64 KB of weight traffic;
 //   * it takes each row's partial absmax over its columns; one barrier
 //     combines the four partials into the row scale;
 //   * it overwrites each row's X values in LDS with their int8 codes and runs
@@ -40,6 +43,16 @@ constexpr int kSteps = kKW / 64;        // 64-byte MFMA k-steps per wave per seg
 // later overwritten by their 1024 codes.  The 16-byte pad puts the 16 code
 // rows read by one MFMA operand fetch in 16 different bank quarters.
 constexpr int kArea = 2 * kKW + 16;
+
+// A buffer resource for raw byte loads over [p, p + bytes): loads past the
+// end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset off, non-temporal (streamed once)
+__device__ __forceinline__ v4i load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 
 // ONE: K <= 4096, a single segment (the host picks the instantiation, so each
 // kernel has one straight path and the compiler's wait insertion sees it alone)
@@ -107,23 +120,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     }
   };
 
-  // ---- weights: 16 loads of 16 bytes per lane (rows n0 + lane%16)
+  // ---- weights: 16 loads of 16 bytes per lane (rows n0 + lane%16), through
+  // a buffer resource over the whole matrix: one offset per lane, the 16
+  // steps as immediate offsets, and the non-temporal hint, so the stream
+  // does not push the activations and the code out of the caches.  Columns
+  // past the segment read the next row's bytes (or, past the matrix, the
+  // zeros the hardware's range check returns): their codes are zero.
   v4i wv[kSteps];
   const int wrow = (n0 + lr < N ? n0 + lr : N - 1);
-  auto load_w = [&](int k0, int seg) {
-    if (seg == kSeg) {
-      // one address per lane, the 16 steps as immediate offsets
-      const int8_t* p = wq + (size_t)wrow * K + k0 + wave * kKW + lg * 16;
+  const __amdgpu_buffer_rsrc_t wres = byte_buffer(wq, (uint32_t)N * (uint32_t)K);
+  auto load_w = [&](int k0) {
+    const uint32_t base = (uint32_t)(wrow * K + k0 + wave * kKW + lg * 16);
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) wv[s] = *(const v4i*)(p + s * 64);
-    } else {
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        int kk = wave * kKW + s * 64 + lg * 16;
-        kk = kk < seg ? kk : seg - 16;
-        wv[s] = *(const v4i*)(wq + (size_t)wrow * K + k0 + kk);
-      }
-    }
+    for (int s = 0; s < kSteps; ++s) wv[s] = load16_nt(wres, base + s * 64);
   };
   // epilogue factors (wave 0): acc register r of lane (lr, lg) is
   // D[n = 4 lg + r][m = lr].
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
       if (sg > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // reads of the last segment are done
       dma_x(k0, seg);
     }
-    if (sg == 0) load_w(0, seg);
+    if (sg == 0) load_w(0);
     if constexpr (DT != DT_F32) {
       // this segment's X: everything but the 16 weight loads issued last
       if (sg > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
         __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
         dma_x(k0, seg);
       }
-      if (sg > 0) load_w(k0, seg);
+      if (sg > 0) load_w(k0);
       if constexpr (DT != DT_F32) {
         if (sg > 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -292,6 +301,103 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   }
 }
 
+// ---- Decode on codes quantized beforehand (the row quantizer's codes, scales
+// and code sums).  Past about ten tokens, quantizing every X row in every
+// workgroup costs more vector work than the weight stream takes to arrive, so
+// the rows are quantized once and this kernel only streams.  A workgroup owns
+// 16 weight rows and its 4 waves split K; each wave copies its 1 KB share of
+// the 16 weight rows and of the M code rows into its own LDS region, one
+// contiguous 1 KB DMA per row, and runs v_mfma_i32_16x16x64_i8 on them
+// (weights as A, codes as B).  Only the wave itself reads its region, so a
+// wait on its own DMA replaces a barrier.  Rows past N (or M) repeat the last
+// row and only feed outputs that are not stored; columns past K repeat the
+// segment's last 16 bytes and their codes are masked to zero.
+constexpr int kWPitch = kKW + 16;   // LDS bytes per row of a wave's K share (16-byte pad)
+
+template <int YDT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemv_q8(const int8_t* __restrict__ xq,
+                                                         const float* __restrict__ x_scale,
+                                                         const int32_t* __restrict__ x_rowsum, int M, int K,
+                                                         const int8_t* __restrict__ wq,
+                                                         const float* __restrict__ w_scale,
+                                                         const float* __restrict__ w_zp, int N,
+                                                         const float* __restrict__ bias, void* __restrict__ y,
+                                                         int32_t* __restrict__ acc_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t wsm[kWaves][kRows * kWPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t csm[kWaves][kRows * kWPitch];
+  __shared__ v4i part[kWaves][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * kRows;
+  // epilogue factors first (wave 0): register r of lane (lr, lg) is
+  // D[n = n0 + 4 lg + r][m = lr]
+  float fsc[4] = {0, 0, 0, 0}, fzp[4] = {0, 0, 0, 0}, fbi[4] = {0, 0, 0, 0};
+  float s_m = 0.0f;
+  int r_m = 0;
+  const int m = lr;
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + 4 * lg + r;
+      const int nc = n < N ? n : N - 1;
+      fsc[r] = w_scale[nc];
+      fzp[r] = w_zp[nc];
+      fbi[r] = bias ? bias[nc] : 0.0f;
+    }
+    const int mc = m < M ? m : M - 1;
+    s_m = x_scale[mc];
+    r_m = x_rowsum[mc];
+  }
+  uint8_t* const wl = wsm[wave];
+  uint8_t* const cl = csm[wave];
+  const int xr = lr < M ? lr : M - 1;     // code rows past M repeat the last: they feed unstored columns
+  v4i acc = {0, 0, 0, 0};
+  for (int k0 = 0; k0 < K; k0 += kSeg) {
+    const int seg = (K - k0) < kSeg ? (K - k0) : kSeg;
+    int c = wave * kKW + 16 * lane;
+    c = c < seg ? c : seg - 16;                       // clamped; its codes are masked below
+    if (k0 > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // this wave's reads of the last segment are done
+    // the wave's 1 KB share of each of the 16 weight rows, then of the 16 code
+    // rows: contiguous 1 KB per instruction (rows past N or M repeat the last)
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int n = n0 + i < N ? n0 + i : N - 1;
+      dma16((const uint8_t*)wq, (uint32_t)(n * K + k0 + c), wl + i * kWPitch);
+    }
+    const int mr = M < kRows ? M : kRows;
+    for (int i = 0; i < mr; ++i) dma16((const uint8_t*)xq, (uint32_t)(i * K + k0 + c), cl + i * kWPitch);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int o = s * 64 + lg * 16;
+      const v4i a = *(const v4i*)(wl + lr * kWPitch + o);
+      v4i b = *(const v4i*)(cl + xr * kWPitch + o);
+      if (seg != kSeg && wave * kKW + s * 64 + lg * 16 >= seg) b = v4i{0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+    }
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && m < M) {
+    v4i t = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += part[w][lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + lg * 4 + r;
+      if (n < N) {
+        const int a = t[r];
+        if (acc_out) acc_out[(size_t)m * N + n] = a;
+        const int cc = a - (int)fzp[r] * r_m;
+        float v = (s_m * fsc[r]) * (float)cc;
+        if (bias) v += fbi[r];
+        store_out<YDT>(y, (size_t)m * N + n, v);
+      }
+    }
+  }
+}
+
 template <int DT>
 hipError_t launch_dt(const void* x, int64_t M, int64_t K, const int8_t* wq, const float* ws,
                      const float* wz, int64_t N, const float* bias, void* y, int ydt, int32_t* acc_out,
@@ -312,6 +418,19 @@ hipError_t launch_dt(const void* x, int64_t M, int64_t K, const int8_t* wq, cons
 }
 
 }  // namespace
+
+hipError_t launch_gemv_q8(const int8_t* xq, const float* x_scale, const int32_t* x_rowsum, int64_t M, int64_t K,
+                          const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N, const float* bias,
+                          void* y, int ydt, int32_t* acc_out, hipStream_t st) {
+  dim3 grid((unsigned)((N + kRows - 1) / kRows)), block(kThreads);
+  const int m = (int)M, k = (int)K, n = (int)N;
+  switch (ydt) {
+    case DT_F32: k_gemv_q8<DT_F32><<<grid, block, 0, st>>>(xq, x_scale, x_rowsum, m, k, wq, w_scale, w_zp, n, bias, y, acc_out); break;
+    case DT_F16: k_gemv_q8<DT_F16><<<grid, block, 0, st>>>(xq, x_scale, x_rowsum, m, k, wq, w_scale, w_zp, n, bias, y, acc_out); break;
+    default: k_gemv_q8<DT_BF16><<<grid, block, 0, st>>>(xq, x_scale, x_rowsum, m, k, wq, w_scale, w_zp, n, bias, y, acc_out); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv_i8(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq,
                           const float* w_scale, const float* w_zp, int64_t N, const float* bias,

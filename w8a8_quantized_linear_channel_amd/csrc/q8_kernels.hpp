@@ -42,10 +42,16 @@ enum GemmKind : int { GEMM_INT8 = 0, GEMM_INT8_DECOMP = 1, GEMM_FP8 = 2 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, int ydt, hipStream_t st);
 
-// Decode-shaped int8 linear, M <= 16, activation quantization fused (gemv.hip).
+// Decode-shaped int8 linear (gemv.hip).  M <= kGemvFusedMaxM: one launch with
+// the activation quantization fused in; kGemvFusedMaxM < M <= kGemvMaxM: on
+// codes, scales and code sums from the row quantizer.
 hipError_t launch_gemv_i8(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq,
                           const float* w_scale, const float* w_zp, int64_t N, const float* bias,
                           void* y, int ydt, int32_t* acc_out, hipStream_t st);
+hipError_t launch_gemv_q8(const int8_t* xq, const float* x_scale, const int32_t* x_rowsum, int64_t M, int64_t K,
+                          const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N, const float* bias,
+                          void* y, int ydt, int32_t* acc_out, hipStream_t st);
+constexpr int64_t kGemvFusedMaxM = 10;
 constexpr int64_t kGemvMaxM = 16;
 
 // LLM.int8 outlier columns (decomp.hip): flags[k] = max_m |x[m,k]| >= threshold
