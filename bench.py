@@ -24,6 +24,7 @@ replayed, so host launch overhead and cache reuse do not enter the figure.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -45,6 +46,33 @@ PEAK_HBM_GBS = 8000.0         # HBM3E, MI355X
 METRIC = "q8_linear int8 TOPS (prefill) + GB/s (decode) and % of MI355X roofline"
 
 
+# HBM traffic of one launch of the prefill GEMM, from two rocprofv3 --pmc
+# runs of `bench.py --only prefill --steps 3 --warmup 1 --warm-ms 0
+# --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
+# scaled by what the same counter reads for a plain 256 MiB device copy
+# (`bench.py --only copy`): FETCH_SIZE reads 131085 KiB for 262144 KiB moved
+# (x 2.0), WRITE_SIZE 262144 KiB (x 1.0).  Valid for the GEMM sources whose
+# hash is recorded here; after any change to them the figure is withheld.
+GEMM_TRAFFIC = {
+    "sources_sha256": "a5fc3452ab4e161471df0bf71dd9f94811effa10dec84832d9578add6e40b7b6",
+    "fetch_kib": 90649.45, "fetch_scale": 262144.0 / 131085.44,
+    "write_kib": 57345.25, "write_scale": 262144.0 / 262144.0,
+}
+
+
+def gemm_traffic_bytes():
+    """Per-launch HBM bytes of the prefill GEMM, or None if its sources changed."""
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "w8a8_quantized_linear_channel_amd", "csrc")
+    for f in ("gemm.hip", "q8_device.hpp", "q8_kernels.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    t = GEMM_TRAFFIC
+    if h.hexdigest() != t["sources_sha256"]:
+        return None
+    return int((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024)
+
+
 def ev():
     return torch.cuda.Event(enable_timing=True)
 
@@ -57,9 +85,15 @@ def ev():
 WARM_MS = 60.0
 
 
-def warm_up(step, warmup, min_ms=WARM_MS):
+def set_warm_ms(ms):
+    global WARM_MS
+    WARM_MS = ms
+
+
+def warm_up(step, warmup, min_ms=None):
     """Run `warmup` steps, then more (in groups of 8) until `min_ms` has
     passed on the GPU; return (steps run, ms)."""
+    min_ms = WARM_MS if min_ms is None else min_ms
     dummy = (ev(), ev())
     t0, t1 = ev(), ev()
     t0.record()
@@ -260,9 +294,13 @@ def main():
                     help="minimum warm-up steps per leg (each leg also warms up for %g ms)" % WARM_MS)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8"], default=None,
-                    help="run one workload (for profiling)")
+    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "copy"], default=None,
+                    help="run one workload (for profiling); 'copy' runs a plain 256 MiB device copy, "
+                         "the known-size kernel that scales the HBM byte counters")
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="minimum warm-up time per leg in ms (0 for counter runs)")
     args = ap.parse_args()
+    set_warm_ms(args.warm_ms)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -271,6 +309,15 @@ def main():
     torch.cuda.set_device(dev)
 
     out = {"metric": METRIC}
+    if args.only == "copy":
+        n = 256 << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
     if args.only in (None, "prefill"):
         pf = bench_prefill(dev, args.steps, args.warmup)
         M, N, K = pf["shape"]
@@ -286,7 +333,9 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "k_gemm int8 256x256",
                          "achieved": round(pf["gemm_tops"], 1), "peak": PEAK_INT8_TOPS,
                          "unit": "TOP/s", "frac": round(pf["gemm_tops"] / PEAK_INT8_TOPS, 4),
-                         "traffic": None, "kernel_us": round(pf["gemm_us"], 2)},
+                         "traffic": gemm_traffic_bytes(), "traffic_unit": "bytes per launch",
+                         "algorithmic_bytes": M * K + N * K + 8 * N + 8 * M + 2 * M * N,
+                         "kernel_us": round(pf["gemm_us"], 2)},
             "act_quant": {"us": round(pf["act_quant_us"], 2), "gbs": round(pf["act_quant_gbs"], 1),
                           "frac_hbm": round(pf["act_quant_gbs"] / PEAK_HBM_GBS, 4)},
         })
