@@ -13,7 +13,8 @@
 //                     accumulation, y = S_a[m] S_b[n] acc (+ bias)
 //
 // Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile; each wave
-// owns (BM/2) x (BN/2) built from 32 x 32 MFMA fragments.  K advances 64
+// owns (BM/2) x (BN/2) built from 32 x 32 MFMA fragments.  The 256 x 256 int8
+// tile uses 8 waves (2 x 4, two per SIMD), each 128 x 64.  K advances 64
 // bytes per stage.  Four LDS buffers hold four stages, filled by
 // global_load_lds_dwordx4 (global -> LDS without registers) three stages
 // ahead of the MFMAs, so a stage's loads have three stages of compute to
@@ -46,7 +47,6 @@ namespace {
 
 constexpr int kBK = 64;             // bytes of K per stage
 constexpr int kStages = 4;          // LDS buffers (prefetch distance kStages - 1)
-constexpr int kThreads = 256;       // 4 waves
 constexpr int kGroupM = 4;          // tile-rows per L2 group
 constexpr int kXcds = 8;
 
@@ -95,12 +95,14 @@ __device__ __forceinline__ int raw32(float x) { return __float_as_int(x); }
 // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 __device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 struct Tile {
-  static constexpr int TM = BM / 2, TN = BN / 2;            // wave tile
+  static constexpr int NT = 64 * NW;                        // threads
+  static constexpr int WN = NW == 8 ? 4 : 2, WM = NW / WN;  // wave grid
+  static constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;          // 32x32 fragments per wave
-  static constexpr int ALOADS = BM * (kBK / 16) / kThreads;   // 16-byte chunks per thread
-  static constexpr int BLOADS = BN * (kBK / 16) / kThreads;
+  static constexpr int ALOADS = BM * (kBK / 16) / NT;   // 16-byte chunks per thread
+  static constexpr int BLOADS = BN * (kBK / 16) / NT;
   static constexpr int LOADS = ALOADS + BLOADS;               // DMA instructions per wave per stage
   static_assert(ALOADS >= 1 && BLOADS >= 1 && FM >= 1 && FN >= 1, "tile too small");
 };
@@ -122,10 +124,11 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int& tm, int& tn) 
   tn = inner / gsize;
 }
 
-template <int BM, int BN, int KIND, int YDT>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
+template <int BM, int BN, int KIND, int YDT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g) {
   using MM = typename std::conditional<KIND == GEMM_FP8, MmaF8, MmaI8>::type;
-  using TL = Tile<BM, BN>;
+  using TL = Tile<BM, BN, NW>;
+  constexpr int kThreads = TL::NT;
   using Acc = typename MM::Acc;
   constexpr int NR = MM::NR;
   constexpr int KS = kBK / MM::KSTEP;
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
 
   // Epilogue factors, loaded now and parked in registers (thread t: row m0+t
   // and column n0+t of the tile), so their latency is long over when the
@@ -561,20 +564,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
 // decomposition's output is fp16); fp8 bf16.
 template <int BM, int BN, int KIND>
 hipError_t launch_tiles(const GemmArgs& g, int ydt, hipStream_t st) {
+  // 256 x 256 int8 tiles run 8 waves (two per SIMD, 128 x 64 each), so one
+  // wave's stalls on the DMA issue are covered by the other's MFMAs; the fp8
+  // operands are twice as wide and would spill at that register budget
+  constexpr int NW = BM == 256 && BN == 256 && KIND != GEMM_FP8 ? 8 : 4;
   const int64_t ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
-  dim3 grid((unsigned)(ntm * ntn)), block(kThreads);
+  dim3 grid((unsigned)(ntm * ntn)), block(64 * NW);
   if constexpr (KIND == GEMM_INT8) {
     switch (ydt) {
-      case DT_F32: k_gemm<BM, BN, KIND, DT_F32><<<grid, block, 0, st>>>(g); break;
-      case DT_F16: k_gemm<BM, BN, KIND, DT_F16><<<grid, block, 0, st>>>(g); break;
-      default: k_gemm<BM, BN, KIND, DT_BF16><<<grid, block, 0, st>>>(g); break;
+      case DT_F32: k_gemm<BM, BN, KIND, DT_F32, NW><<<grid, block, 0, st>>>(g); break;
+      case DT_F16: k_gemm<BM, BN, KIND, DT_F16, NW><<<grid, block, 0, st>>>(g); break;
+      default: k_gemm<BM, BN, KIND, DT_BF16, NW><<<grid, block, 0, st>>>(g); break;
     }
   } else if constexpr (KIND == GEMM_INT8_DECOMP) {
     if (ydt != DT_F16) return hipErrorInvalidValue;
-    k_gemm<BM, BN, KIND, DT_F16><<<grid, block, 0, st>>>(g);
+    k_gemm<BM, BN, KIND, DT_F16, NW><<<grid, block, 0, st>>>(g);
   } else {
     if (ydt != DT_BF16) return hipErrorInvalidValue;
-    k_gemm<BM, BN, KIND, DT_BF16><<<grid, block, 0, st>>>(g);
+    k_gemm<BM, BN, KIND, DT_BF16, NW><<<grid, block, 0, st>>>(g);
   }
   return hipGetLastError();
 }
