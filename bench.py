@@ -265,6 +265,49 @@ def bench_fp8(dev, steps, warmup):
                          "frac": flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}}
 
 
+# ------------------------------------------------------------------ measured ceilings
+def bench_ceilings(dev, steps):
+    """What this machine reaches with plain device copies and with the vendor
+    GEMM library on the same shapes (steady state, same warm-up rule), beside
+    the specification peaks: the copy for the HBM-bound rows, hipBLASLt
+    (torch._int_mm with INT32 output, torch._scaled_mm rowwise) for the GEMMs."""
+    out = {}
+
+    def t_ms(fn):
+        _, ms, _ = timed_steps(lambda i, pair: (pair[0].record(), fn(), pair[1].record()), steps, 2,
+                               [(ev(), ev()) for _ in range(steps)])
+        return ms
+
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
+    dst = torch.empty_like(src)
+    ms = t_ms(lambda: dst.copy_(src))
+    out["hbm_copy_GBs"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    g = torch.Generator(device="cpu").manual_seed(5)
+    try:
+        M, N, K = 2048, 14336, 4096
+        a = (torch.randn(M, K, generator=g) * 30).round().clamp(-127, 127).to(torch.int8).to(dev)
+        b = (torch.randn(N, K, generator=g) * 30).round().clamp(-127, 127).to(torch.int8).to(dev)
+        ms = t_ms(lambda: torch._int_mm(a, b.t()))
+        out["lib_int8_gemm_2048x14336x4096"] = {"us": round(ms * 1e3, 2), "TOPS": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1),
+                                                "output": "int32, no epilogue"}
+    except Exception as e:  # the library call is context, not part of the path
+        out["lib_int8_gemm_2048x14336x4096"] = f"unavailable: {str(e)[:80]}"
+    try:
+        M, N, K = 4096, 4096, 14336
+        fa = torch.randn(M, K, generator=g).to(dev).to(torch.float8_e4m3fn)
+        fb = torch.randn(N, K, generator=g).to(dev).to(torch.float8_e4m3fn)
+        sa = torch.rand(M, 1, device=dev)
+        sb = torch.rand(1, N, device=dev)
+        ms = t_ms(lambda: torch._scaled_mm(fa, fb.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16))
+        out["lib_fp8_rowwise_gemm_4096x4096x14336"] = {"us": round(ms * 1e3, 2),
+                                                       "TFLOPS": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+    except Exception as e:
+        out["lib_fp8_rowwise_gemm_4096x4096x14336"] = f"unavailable: {str(e)[:80]}"
+    return out
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline(x_host, w_host, target_s):
     """The oracle (untuned numpy) on a bounded sample of the prefill step: the
@@ -363,6 +406,8 @@ def main():
                       "gemm_us": round(d["gemm_us"], 2),
                       "roofline": {k: round(v, 4) if isinstance(v, float) else v
                                    for k, v in d["roofline"].items()}}
+    if args.only is None:
+        out["ceilings"] = bench_ceilings(dev, args.steps)
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(*pf["host_inputs"], args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -30,6 +30,9 @@ listed with its reason in the design notes of the repository):
       BitsAndBytesConfig table)
   R11 the int8 part of the decomposition takes its per-token scale over the regular columns only
   R12 outlier weights are the fp16 rounding of the dequantized int8 columns (no fp16 copy kept)
+  R13 weight-only (W8A16): the dequantized weights S (q - Z) enter the product exactly; the
+      pages' "dequantized back to 16 bits" is the storage of an implementation, whose rounding
+      (<= 2^-9 relative) the output tolerance covers
 """
 from __future__ import annotations
 
@@ -290,6 +293,22 @@ def fp8_abs_dot(x, wq_codes, w_scale, scale_ub=1200.0) -> np.ndarray:
     xq, xs = quantize_fp8_rowwise(x, scale_ub)
     a = np.abs(e4m3_decode(xq)) @ np.abs(e4m3_decode(wq_codes)).T
     return a * xs.astype(np.float64)[:, None] * w_scale.astype(np.float64)[None, :]
+
+
+# --------------------------------------------------------------------------
+# O10: weight-only W8A16 (16-bit activations, INT8 asymmetric weights)
+# --------------------------------------------------------------------------
+def linear_w8a16(x, wq, ws, wz, bias=None):
+    """Weight-only linear ([NOTE] PTQ section, weight quantization: the weights
+    are stored as INT8, read from memory and dequantized for a product in the
+    activations' 16-bit format; the activations are not quantized):
+        y[m,n] = Sum_k x[m,k] S_w[n] (q_w[n,k] - Z_w[n])  (+ b[n])
+    with the dequantized weights exact (R13: no rounding of S (q - Z) to 16
+    bits) and the product in float64.  Returns y float64 [M,N]."""
+    y = to_f32(x).astype(np.float64) @ dequantize_weight_int8(wq, ws, wz).T
+    if bias is not None:
+        y = y + to_f32(bias).astype(np.float64)[None, :]
+    return y
 
 
 # --------------------------------------------------------------------------

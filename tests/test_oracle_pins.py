@@ -406,3 +406,56 @@ def test_fp8_abs_dot_bounds_the_output():
     wq2, ws2 = O.quantize_fp8_rowwise(wp)
     y2, _ = O.linear_fp8(xp, wq2, ws2, 1200.0)
     np.testing.assert_allclose(y2, O.fp8_abs_dot(xp, wq2, ws2, 1200.0), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- O10 weight-only W8A16
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 3, 5), (3, 4, 16)])
+def test_w8a16_brute_force(M, N, K):
+    """Pure-Python triple loop over the definition on tiny shapes: pins the
+    operand roles and the transpose (y[m,n] uses row n of W)."""
+    rng = np.random.default_rng(70 + K)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    w = rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.05)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    xf = O.to_f32(x)
+    y = O.linear_w8a16(x, wq, ws, wz)
+    for m in range(M):
+        for n in range(N):
+            ref = Fraction(0)
+            for k in range(K):
+                ref += Fraction(float(xf[m, k])) * Fraction(float(ws[n])) * (int(wq[n, k]) - int(wz[n]))
+            assert abs(y[m, n] - float(ref)) <= 1e-12 * max(1.0, abs(float(ref)))
+
+
+def test_w8a16_equals_w8a8_when_activations_are_on_the_grid():
+    """X = c q with c a power of two and max|q| = 127 is reproduced exactly by
+    the per-token INT8 quantizer (S = 127 c / 127 = c, x / S = q), so the
+    weight-only product must equal the W8A8 path (O3-O5), which is pinned on
+    its own; both are float64."""
+    rng = np.random.default_rng(71)
+    M, N, K = 4, 24, 96
+    q = rng.integers(-127, 128, (M, K))
+    q[:, 0] = 127
+    c = np.float32(2.0 ** -5)
+    x = (q.astype(np.float32) * c)
+    w = rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    xq, xs, _ = O.quantize_act_int8_sym(x)
+    assert np.array_equal(xq.astype(np.int64), q) and np.all(xs == c)
+    y16 = O.linear_w8a16(x, wq, ws, wz)
+    y8, _ = O.linear_int8(x, wq, ws, wz)
+    assert np.allclose(y16, y8, rtol=1e-12, atol=1e-12)
+
+
+def test_w8a16_integer_identity():
+    """Integer rows spanning [-128, 127] give S = 1, Z = 0, so the product is the
+    exact integer product of X and the weights."""
+    rng = np.random.default_rng(72)
+    N, K = 8, 64
+    w = rng.integers(-128, 128, (N, K)).astype(np.float32)
+    w[:, 0], w[:, 1] = -128.0, 127.0
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    assert np.all(ws == 1.0) and np.all(wz == 0.0)
+    x = rng.integers(-50, 51, (3, K)).astype(np.float32)
+    y = O.linear_w8a16(torch.from_numpy(x).to(torch.bfloat16), wq, ws, wz)
+    assert np.array_equal(y, x.astype(np.int64) @ w.astype(np.int64).T)
