@@ -206,6 +206,24 @@ q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_
                       const uint8_t* wq, const float* w_scale, int64_t N, const float* bias,
                       void* y, void* stream);
 
+/*
+ * q8_linear_w8a16 -- weight-only linear for decode-sized M: the INT8
+ * asymmetric weights are dequantized for a product with the 16-bit
+ * activations, which are not quantized ("lecture notes on LLM quantization",
+ * PTQ section, weight quantization):
+ *     y[m,n] = S_w[n] Sum_k x[m,k] (wq[n,k] - Z_w[n])  (+ bias[n])
+ * The widened weights are exact; products accumulate in fp32.
+ * x: [M, K] of x_dtype (BF16 or F16 only); wq/w_scale/w_zp: from
+ * q8_quantize_weight(Q8_INT8_ASYM); bias: float [N] or NULL; y: [M, N] of
+ * y_dtype (F32, F16, BF16).  No workspace.
+ * Errors: Q8_ERR_BAD_DTYPE for an F32 x; Q8_ERR_BAD_SHAPE for M > 16, besides
+ * the preconditions above.
+ */
+q8_status q8_linear_w8a16(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
+                          const int8_t* wq, const float* w_scale, const float* w_zp,
+                          int64_t N, const float* bias, void* y, q8_dtype y_dtype,
+                          void* stream);
+
 /* Bytes of workspace the call `op` needs at this shape (0 if none); returns 0
  * for invalid shapes as well, which the call itself then rejects. */
 size_t q8_workspace_bytes(q8_op op, int64_t M, int64_t N, int64_t K);

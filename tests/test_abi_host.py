@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
     for f in ["q8_quantize_weight", "q8_quantize_act", "q8_linear", "q8_linear_int8_decomp",
-              "q8_linear_fp8", "q8_workspace_bytes", "q8_status_str"]:
+              "q8_linear_fp8", "q8_linear_w8a16", "q8_workspace_bytes", "q8_status_str"]:
         assert f in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -147,3 +147,20 @@ def test_valid_arguments_without_a_device_report_device_error():
     E = _lib
     st = _lib.lib().q8_quantize_weight(E.Q8_INT8_ASYM, P, E.Q8_F32, 4, 16, P, P, P, None)
     assert st == 8
+
+
+def test_w8a16_validation():
+    f = _lib.lib().q8_linear_w8a16
+    E = _lib
+    ok = dict(x=P, xd=E.Q8_BF16, M=4, K=64, wq=P, ws=P, wz=P, N=64, b=None, y=P, yd=E.Q8_BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["xd"], a["M"], a["K"], a["wq"], a["ws"], a["wz"], a["N"], a["b"], a["y"], a["yd"], None)
+
+    assert call(xd=E.Q8_F32) == 3            # 16-bit activations only
+    assert call(yd=9) == 3
+    assert call(M=17) == 2                    # decode sizes only
+    assert call(K=40) == 2
+    assert call(wz=None) == 1
+    assert call(y=MIS) == 6

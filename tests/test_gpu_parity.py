@@ -392,3 +392,57 @@ def test_fp8_linear_full_size_sampled():
     wl = inputs.fp8_rowwise()
     rows = sample_rows(4096, 8, seed=5, extra=(255, 256))
     run_fp8_case(wl.x, wl.w, 1200.0, rows=rows, what="fp8 full")
+
+
+# ---------------------------------------------------------------- weight-only W8A16
+def run_w8a16_case(x, w, out_dtype, cols=None, bias=None, what=""):
+    """GPU q8_linear_w8a16 on the full problem; oracle O10 on output columns
+    `cols` (all if None)."""
+    wq, ws, wz = q8.q8_quantize_weight(g(w), "int8_asym")
+    b = g(bias) if bias is not None else None
+    y = q8.q8_linear_w8a16(g(x), wq, ws, wz, bias=b, out_dtype=out_dtype)
+    rq, rs, rz = oracle_weights(w)
+    if cols is None:
+        y_ref = O.linear_w8a16(x, rq, rs, rz, bias=bias)
+        y_g = out_f64(y)
+    else:
+        y_ref = O.linear_w8a16(x, rq[cols], rs[cols], rz[cols], bias=None if bias is None else bias[cols])
+        y_g = out_f64(y)[:, cols]
+    check_close(y_g, y_ref, f"{what} output")
+    return y
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_w8a16_decode_qproj_full_size(M, dt):
+    log(f"[w8a16] decode q_proj M={M} N=K=4096 {dt}")
+    wl = inputs.decode_qproj(M=M)
+    cols = np.sort(np.random.default_rng(100 + M).choice(4096, 384, replace=False))
+    cols = np.unique(np.r_[cols, [0, 15, 16, 4095]])
+    run_w8a16_case(wl.x.to(dt), wl.w, torch.bfloat16, cols=cols, what=f"w8a16 M={M}")
+
+
+@pytest.mark.parametrize("M,N,K,dt", [(3, 100, 4112, torch.bfloat16),     # two K segments, N tail
+                                      (16, 37, 8240, torch.float16),      # two segments, 16 rows
+                                      (1, 1, 16, torch.float16),          # smallest K, one feature
+                                      (7, 33, 208, torch.bfloat16),       # partial MFMA k-steps
+                                      (5, 64, 1024, torch.float16)])
+def test_w8a16_ragged(M, N, K, dt):
+    log(f"[w8a16] ragged M={M} N={N} K={K} {dt}")
+    x = inputs.random_matrix(110 + M, (M, K), 1.0, dt)
+    w = inputs.random_matrix(120 + N, (N, K), 0.02, torch.float32)
+    run_w8a16_case(x, w, torch.float32, what="w8a16 ragged")
+
+
+def test_w8a16_one_signed_rows_and_bias():
+    """Rows with all-positive or all-negative weights (zero points at the ends
+    of the code range) and a bias, for each output dtype."""
+    log("[w8a16] one-signed weight rows, bias, output dtypes")
+    x = inputs.random_matrix(130, (4, 512), 1.0, torch.bfloat16)
+    w = inputs.random_matrix(131, (48, 512), 0.02, torch.float32).numpy().copy()
+    w[:8] = np.abs(w[:8])
+    w[8:16] = -np.abs(w[8:16])
+    w = torch.from_numpy(w)
+    bias = inputs.random_matrix(132, (48,), 0.5, torch.float32)
+    for od in (torch.float32, torch.float16, torch.bfloat16):
+        run_w8a16_case(x, w, od, bias=bias, what=f"w8a16 bias {od}")

@@ -36,6 +36,7 @@ SIGNATURES = {
     "q8_linear_fp8": (_INT, [_P, _I64, _I64, _P, _P, _I64, _F, _P, _P, _P, _SZ, _P]),
     "q8_gemm_int8": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P, _P]),
     "q8_gemm_fp8": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
+    "q8_linear_w8a16": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P]),
     "q8_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     "q8_status_str": (ctypes.c_char_p, [_INT]),
 }

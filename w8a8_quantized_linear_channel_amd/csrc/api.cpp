@@ -373,6 +373,22 @@ q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_
   return launched(int8_on_codes(xq, x_scale, x_rowsum, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st));
 }
 
+q8_status q8_linear_w8a16(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const int8_t* wq,
+                          const float* w_scale, const float* w_zp, int64_t N, const float* bias, void* y,
+                          q8_dtype y_dtype, void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype) || x_dtype == Q8_F32) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mnk(M, N, K));
+  if (M > q8::kW8A16MaxM) return Q8_ERR_BAD_SHAPE;
+  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
+      (bias && !aligned16(bias)))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y}));
+  return launched(q8::launch_gemv_w8a16(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, st));
+}
+
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,
                       const float* w_scale, int64_t N, const float* bias, void* y, void* stream) {
   Q8_TRY(check_mnk(M, N, K));

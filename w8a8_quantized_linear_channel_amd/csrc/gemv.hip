@@ -44,15 +44,6 @@ constexpr int kSteps = kKW / 64;        // 64-byte MFMA k-steps per wave per seg
 // rows read by one MFMA operand fetch in 16 different bank quarters.
 constexpr int kArea = 2 * kKW + 16;
 
-// A buffer resource for raw byte loads over [p, p + bytes): loads past the
-// end return zeros instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-// 16 bytes at byte offset off, non-temporal (streamed once)
-__device__ __forceinline__ v4i load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
-}
 
 // ONE: K <= 4096, a single segment (the host picks the instantiation, so each
 // kernel has one straight path and the compiler's wait insertion sees it alone)

@@ -222,6 +222,16 @@ typedef __attribute__((address_space(3))) void* lptr_t;   // LDS
 // M0, and the s_nop covers the M0-write -> LDS-DMA hazard.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// A buffer resource for raw byte loads over [p, p + bytes) (word 3 for raw
+// byte access on gfx9): loads past the end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset off with the non-temporal cache policy (streamed once)
+__device__ __forceinline__ v4i load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 __device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint8_t* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"

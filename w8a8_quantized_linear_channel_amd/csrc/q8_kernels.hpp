@@ -52,6 +52,11 @@ hipError_t launch_gemv_q8(const int8_t* xq, const float* x_scale, const int32_t*
                           const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N, const float* bias,
                           void* y, int ydt, int32_t* acc_out, hipStream_t st);
 constexpr int64_t kGemvFusedMaxM = 10;
+
+// Weight-only W8A16 linear for decode-sized M (w8a16.hip): x bf16 or f16.
+hipError_t launch_gemv_w8a16(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq, const float* w_scale,
+                             const float* w_zp, int64_t N, const float* bias, void* y, int ydt, hipStream_t st);
+constexpr int64_t kW8A16MaxM = 16;
 constexpr int64_t kGemvMaxM = 16;
 
 // LLM.int8 outlier columns (decomp.hip): flags[k] = max_m |x[m,k]| >= threshold

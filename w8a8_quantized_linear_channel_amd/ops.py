@@ -223,3 +223,27 @@ def q8_gemm_fp8(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_sca
                                 _ptr(y), _stream(dev))
     _lib.check("q8_gemm_fp8", st)
     return y
+
+
+def q8_linear_w8a16(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, w_zp: torch.Tensor,
+                    bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                    out: Optional[torch.Tensor] = None):
+    """Weight-only W8A16 linear for up to 16 tokens: y = x . (S_w (Wq - Z_w))^T (+ bias),
+    x bf16 or fp16, weights from q8_quantize_weight("int8_asym")."""
+    dev = x.device
+    M, K = x.shape
+    N = wq.shape[0]
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q8_linear_w8a16: x must be bfloat16 or float16")
+    _need(x, "x", x.dtype, (M, K), dev)
+    _need(wq, "wq", torch.int8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    _need(w_zp, "w_zp", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=dev)
+    _need(y, "y", out_dtype, (M, N), dev)
+    st = _lib.lib().q8_linear_w8a16(_ptr(x), _DT[x.dtype], M, K, _ptr(wq), _ptr(w_scale), _ptr(w_zp), N,
+                                    _ptr(bias), _ptr(y), _DT[out_dtype], _stream(dev))
+    _lib.check("q8_linear_w8a16", st)
+    return y
