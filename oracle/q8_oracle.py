@@ -33,6 +33,9 @@ listed with its reason in the design notes of the repository):
   R13 weight-only (W8A16): the dequantized weights S (q - Z) enter the product exactly; the
       pages' "dequantized back to 16 bits" is the storage of an implementation, whose rounding
       (<= 2^-9 relative) the output tolerance covers
+  R14 static quantization: one calibrated scale per activation tensor, symmetric (Z_x = 0, as for
+      the dynamic codes); the INT8 output is the scaling of the float64 epilogue value by the
+      reciprocal of the output scale, rounded half to even and clamped to [-127, 127]
 """
 from __future__ import annotations
 
@@ -309,6 +312,44 @@ def linear_w8a16(x, wq, ws, wz, bias=None):
     if bias is not None:
         y = y + to_f32(bias).astype(np.float64)[None, :]
     return y
+
+
+# --------------------------------------------------------------------------
+# O11 / O12: static activation scale, INT8 requantized output
+# --------------------------------------------------------------------------
+def quantize_act_int8_static(x, scale):
+    """Static INT8 activation quantization ([NOTE] "INT8 这么小的范围不会导致溢出吗？",
+    static quantization: the scale comes from calibration run beforehand and is
+    applied unchanged at inference): one float32 scale S for the tensor,
+    q = clamp(rne(x / S), -127, 127) with the binary32 division (R5, R6, R7),
+    and the per-row code sums.  Returns (q int8 [M,K], rowsum int32 [M])."""
+    x = to_f32(x)
+    s = np.float32(scale)
+    q = np.clip(np.rint(x / s), -127, 127).astype(np.int64)
+    rowsum = q.sum(axis=1)
+    assert np.all(np.abs(rowsum) < 2**31)
+    return q.astype(np.int8), rowsum.astype(np.int32)
+
+
+def requantize_int8(y, y_scale):
+    """INT8 output for the next layer ([NOTE] same section, step 4: the INT32
+    result is scaled and squeezed back into INT8 before it is passed on):
+    q_y = clamp(rne(y * (1 / S_y)), -127, 127), the reciprocal and the product
+    in float64 (R14)."""
+    inv = 1.0 / np.float64(np.float32(y_scale))
+    return np.clip(np.rint(np.asarray(y, dtype=np.float64) * inv), -127, 127).astype(np.int8)
+
+
+def linear_static(x, x_scale, wq, ws, wz, y_scale, bias=None):
+    """W8A8 linear with a static activation scale and an INT8 output:
+    codes by O11, exact INT32 product (O4), the O5 epilogue in float64 with
+    S_x = x_scale on every row, then O12's requantization.
+    Returns (yq int8 [M,N], dict of intermediates)."""
+    xq, rs = quantize_act_int8_static(x, x_scale)
+    acc = int_gemm(xq, wq)
+    xs = np.full(xq.shape[0], np.float32(x_scale), dtype=np.float32)
+    y = epilogue(acc, xs, rs, ws, wz, bias)
+    return requantize_int8(y, y_scale), {"xq": xq, "x_rowsum": rs, "acc": acc, "y": y}
 
 
 # --------------------------------------------------------------------------

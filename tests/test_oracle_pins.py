@@ -459,3 +459,76 @@ def test_w8a16_integer_identity():
     x = rng.integers(-50, 51, (3, K)).astype(np.float32)
     y = O.linear_w8a16(torch.from_numpy(x).to(torch.bfloat16), wq, ws, wz)
     assert np.array_equal(y, x.astype(np.int64) @ w.astype(np.int64).T)
+
+
+# ---------------------------------------------------------------- O11 / O12 static scales, INT8 output
+def test_static_quant_with_the_dynamic_scale_equals_dynamic():
+    """With the per-row dynamic scale supplied as the static scale (one row at
+    a time) the static quantizer must give the dynamic codes (O3 is pinned on
+    its own)."""
+    rng = np.random.default_rng(80)
+    x = torch.from_numpy(rng.standard_normal((5, 300)).astype(np.float32)).to(torch.bfloat16)
+    qd, sd, rd = O.quantize_act_int8_sym(x)
+    for m in range(5):
+        qs, rs = O.quantize_act_int8_static(x[m:m + 1], sd[m])
+        assert np.array_equal(qs[0], qd[m]) and rs[0] == rd[m]
+
+
+def test_static_quant_identity_and_saturation():
+    """S = 1 on integer data gives the data back, clamped to +-127; a value
+    exactly halfway rounds to even."""
+    x = np.array([[-300.0, -127.0, -3.0, 0.0, 2.5, 3.5, 126.0, 1000.0]], dtype=np.float32)
+    q, rs = O.quantize_act_int8_static(x, 1.0)
+    assert q.tolist() == [[-127, -127, -3, 0, 2, 4, 126, 127]]
+    assert rs[0] == sum(q[0].astype(int))
+
+
+def test_static_codes_use_correctly_rounded_division():
+    """Static codes come from fl(x / S) (binary32 division), not x * fl(1/S):
+    values placed next to half-way points between codes separate the two
+    (the exact quotient is computed with fractions and rounded to binary32)."""
+    S = np.float32(0.0371)
+    vals = []
+    for k in range(-126, 126):
+        t = np.float32((k + 0.5) * float(S))
+        for d in (-2, -1, 0, 1, 2):
+            v = t
+            for _ in range(abs(d)):
+                v = np.nextafter(v, np.float32(np.inf if d > 0 else -np.inf))
+            vals.append(np.float32(v))
+    x = np.array([vals], np.float32)
+    q, _ = O.quantize_act_int8_static(x, S)
+    differs = 0
+    for j, v in enumerate(vals):
+        quot = f32_round(Fraction(float(v)) / Fraction(float(S)))
+        ref = max(-127, min(127, round(quot)))          # Python round: half to even
+        assert q[0, j] == ref, (j, float(v))
+        differs += int(np.rint(v * (np.float32(1.0) / S))) != ref
+    assert differs > 0       # the multiply-by-reciprocal reading would give other codes here
+
+
+def test_requantize_integer_values_ties_and_clamp():
+    """S_x = S_w = 1, Z = 0 and integer data make the float64 epilogue value the
+    exact integer product; with S_y = 2 odd products land on .5 and must round
+    to even; large ones saturate."""
+    w = np.array([[1.0, -128.0, 127.0], [-128.0, 127.0, 3.0]], dtype=np.float32)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    assert np.all(ws == 1.0) and np.all(wz == 0.0)
+    x = np.array([[1.0, 0.0, 0.0], [3.0, 0.0, 0.0], [0.0, 0.0, 5.0], [0.0, 2.0, 0.0]], dtype=np.float32)
+    yq, inter = O.linear_static(x, 1.0, wq, ws, wz, 2.0)
+    assert np.array_equal(inter["acc"], x.astype(np.int64) @ w.astype(np.int64).T)
+    # products: [1,-128],[3,-384],[635,15],[-256,254] -> /2: [0.5,-64],[1.5,-192],[317.5,7.5],[-128,127]
+    assert yq.tolist() == [[0, -64], [2, -127], [127, 8], [-127, 127]]
+
+
+def test_static_linear_bias_enters_before_requantization():
+    """The bias is added to the float64 epilogue value, then the sum is
+    requantized: with S_y = 1 and a bias of +-0.75 on integer products the
+    codes move by one step exactly where the sum crosses a half."""
+    w = np.array([[1.0, -128.0, 127.0]], dtype=np.float32)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    x = np.array([[2.0, 0.0, 0.0], [0.0, 0.0, 0.0], [-1.0, 0.0, 0.0]], dtype=np.float32)
+    for b, want in ((0.75, [[3], [1], [0]]), (-0.75, [[1], [-1], [-2]])):
+        yq, inter = O.linear_static(x, 1.0, wq, ws, wz, 1.0, bias=np.float32([b]))
+        assert np.array_equal(inter["y"][:, 0], np.array([2.0, 0.0, -1.0]) + b)
+        assert yq.tolist() == want
