@@ -66,7 +66,7 @@ typedef enum q8_format {
   Q8_FP8_E4M3 = 2   /* weights or activations: per-row OCP e4m3fn, r = S q    */
 } q8_format;
 
-typedef enum q8_op { Q8_OP_LINEAR = 0, Q8_OP_DECOMP = 1, Q8_OP_FP8 = 2 } q8_op;
+typedef enum q8_op { Q8_OP_LINEAR = 0, Q8_OP_DECOMP = 1, Q8_OP_FP8 = 2, Q8_OP_STATIC = 3 } q8_op;
 
 /*
  * q8_quantize_weight -- per-output-channel weight quantization (done once,
@@ -205,6 +205,34 @@ q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K,
                       const uint8_t* wq, const float* w_scale, int64_t N, const float* bias,
                       void* y, void* stream);
+
+/*
+ * q8_quantize_act_static -- static INT8 activation quantization ("lecture
+ * notes on LLM quantization", static quantization: the scale is calibrated
+ * beforehand and applied unchanged at inference): one float scale S for the
+ * tensor, xq = clamp(rne(x / S), -127, 127) with the binary32 division,
+ * x_rowsum[m] = sum_k xq[m,k] (nullable).  x: [M, K] of x_dtype; xq: int8
+ * [M, K].  Errors: Q8_ERR_BAD_ARG unless 0 < x_scale < inf.
+ */
+q8_status q8_quantize_act_static(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
+                                 float x_scale, int8_t* xq, int32_t* x_rowsum, void* stream);
+
+/*
+ * q8_linear_static -- W8A8 linear with a static activation scale and an INT8
+ * output for the next layer (same notes, "INT8 这么小的范围不会导致溢出吗？", step 4:
+ * the INT32 result is scaled back into INT8):
+ *     xq = q8_quantize_act_static(x, x_scale);  acc = sum_k xq wq  (exact int32)
+ *     v  = (x_scale S_w[n]) (acc - Z_w[n] sum_k xq) (+ bias[n])       (float64)
+ *     yq = clamp(rne(v * (1 / y_scale)), -127, 127)                   (float64)
+ * x: [M, K] of x_dtype; weights from q8_quantize_weight(Q8_INT8_ASYM); bias:
+ * float [N] or NULL; yq: int8 [M, N].  workspace:
+ * q8_workspace_bytes(Q8_OP_STATIC, M, N, K) bytes.  Errors: Q8_ERR_BAD_ARG
+ * unless both scales are finite and positive.
+ */
+q8_status q8_linear_static(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, float x_scale,
+                           const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N,
+                           const float* bias, float y_scale, int8_t* yq, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * q8_linear_w8a16 -- weight-only linear for decode-sized M: the INT8

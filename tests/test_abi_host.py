@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
     for f in ["q8_quantize_weight", "q8_quantize_act", "q8_linear", "q8_linear_int8_decomp",
-              "q8_linear_fp8", "q8_linear_w8a16", "q8_workspace_bytes", "q8_status_str"]:
+              "q8_linear_fp8", "q8_linear_w8a16", "q8_quantize_act_static", "q8_linear_static",
+              "q8_workspace_bytes", "q8_status_str"]:
         assert f in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -63,6 +64,9 @@ def test_workspace_sizes():
     # decomposition: codes, scale, row sum, column flags, outlier list, count
     d = ws(_lib.Q8_OP_DECOMP, 512, 4096, 4096)
     assert d == 512 * 4096 + 2048 + 2048 + 4096 + 4096 * 4 + 256
+    # static path: codes, per-row scale copy and code sums at every M
+    assert ws(_lib.Q8_OP_STATIC, 1, 4096, 4096) == 4096 + 2 * 256
+    assert ws(_lib.Q8_OP_STATIC, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192
     # invalid shapes give 0
     assert ws(_lib.Q8_OP_LINEAR, 0, 16, 16) == 0
     assert ws(_lib.Q8_OP_LINEAR, 16, 16, 24) == 0
@@ -164,3 +168,31 @@ def test_w8a16_validation():
     assert call(K=40) == 2
     assert call(wz=None) == 1
     assert call(y=MIS) == 6
+
+
+def test_static_validation():
+    E = _lib
+    q = _lib.lib().q8_quantize_act_static
+    assert q(P, E.Q8_BF16, 4, 64, 0.0, P, P, None) == 5
+    assert q(P, E.Q8_BF16, 4, 64, -1.0, P, P, None) == 5
+    assert q(P, E.Q8_BF16, 4, 64, NAN, P, P, None) == 5
+    assert q(P, E.Q8_BF16, 4, 64, INF, P, P, None) == 5
+    assert q(P, 7, 4, 64, 0.1, P, P, None) == 3
+    assert q(P, E.Q8_BF16, 4, 40, 0.1, P, P, None) == 2
+    assert q(None, E.Q8_BF16, 4, 64, 0.1, P, P, None) == 1
+    assert q(P, E.Q8_BF16, 4, 64, 0.1, MIS, P, None) == 6
+    f = _lib.lib().q8_linear_static
+    ok = dict(x=P, xd=E.Q8_BF16, M=64, K=64, sx=0.1, wq=P, ws=P, wz=P, N=64, b=None, sy=0.5, y=P, w=P2, wb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["xd"], a["M"], a["K"], a["sx"], a["wq"], a["ws"], a["wz"], a["N"], a["b"], a["sy"],
+                 a["y"], a["w"], a["wb"], None)
+
+    assert call(sx=0.0) == 5
+    assert call(sy=NAN) == 5
+    assert call(sy=-2.0) == 5
+    assert call(w=None) == 7
+    assert call(M=1, wb=100) == 7            # the static path always needs its workspace
+    assert call(y=MIS) == 6
+    assert call(wz=None) == 1

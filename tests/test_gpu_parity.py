@@ -446,3 +446,57 @@ def test_w8a16_one_signed_rows_and_bias():
     bias = inputs.random_matrix(132, (48,), 0.5, torch.float32)
     for od in (torch.float32, torch.float16, torch.bfloat16):
         run_w8a16_case(x, w, od, bias=bias, what=f"w8a16 bias {od}")
+
+
+# ---------------------------------------------------------------- static scales, INT8 output
+@pytest.mark.parametrize("name,M,K,dt,scale", [("bf16_2048x4096", 2048, 4096, torch.bfloat16, 0.021),
+                                               ("f32_37x272_saturating", 37, 272, torch.float32, 0.004),
+                                               ("f16_5x1040", 5, 1040, torch.float16, 0.0371)])
+def test_quantize_act_static_codes(name, M, K, dt, scale):
+    log(f"[act static] {name} S={scale}")
+    x = inputs.random_matrix(140 + M, (M, K), 1.0, dt)
+    xq, rs = q8.q8_quantize_act_static(g(x), scale)
+    rows = None if M * K <= 1e6 else sample_rows(M, 24, seed=3)
+    xr = x if rows is None else x[rows]
+    rq, rr = O.quantize_act_int8_static(xr, scale)
+    assert_equal(host(xq) if rows is None else host(xq)[rows], rq, "static codes")
+    assert_equal(host(rs) if rows is None else host(rs)[rows], rr, "static row sums")
+
+
+def run_static_case(x, w, x_scale, rows=None, bias=None, clip_frac=0.2, what=""):
+    """GPU q8_linear_static on the full problem; oracle O12 on `rows` (all if
+    None).  The output scale is set from the oracle's float64 values so that
+    about `clip_frac` of the largest outputs saturate."""
+    wq, ws, wz = q8.q8_quantize_weight(g(w), "int8_asym")
+    rq, rs, rz = oracle_weights(w)
+    xr = x if rows is None else x[rows]
+    _, inter = O.linear_static(xr, x_scale, rq, rs, rz, 1.0, bias=bias)
+    y_scale = float(np.float32(np.quantile(np.abs(inter["y"]), 1.0 - clip_frac) / 127.0))
+    yq_ref, _ = O.linear_static(xr, x_scale, rq, rs, rz, y_scale, bias=bias)
+    b = g(bias) if bias is not None else None
+    yq = q8.q8_linear_static(g(x), x_scale, wq, ws, wz, y_scale, bias=b)
+    got = host(yq) if rows is None else host(yq)[rows]
+    assert_equal(got, yq_ref, f"{what} int8 output")
+    sat = float(np.mean(np.abs(yq_ref.astype(int)) == 127))
+    log(f"  {what}: {yq_ref.size} int8 outputs bit-exact, {sat:.1%} saturated")
+
+
+@pytest.mark.parametrize("M,N,K,sx", [(1, 4096, 4096, 0.03),       # decode: streaming GEMV on codes
+                                      (16, 100, 4112, 0.02),       # decode, N tail, two K segments
+                                      (300, 520, 1040, 0.025),     # 64x64 tiles
+                                      (1000, 3000, 208, 0.03),     # 128x128 tiles
+                                      (2040, 6200, 336, 0.03)])    # 256x256 tiles, ragged M/N
+def test_linear_static_int8_output(M, N, K, sx):
+    log(f"[linear static] M={M} N={N} K={K} S_x={sx}")
+    x = inputs.random_matrix(150 + M, (M, K), 1.0, torch.bfloat16)
+    w = inputs.random_matrix(160 + N, (N, K), 0.02, torch.float32)
+    rows = None if M * N * K <= 2e8 else sample_rows(M, 10, seed=M, extra=(255, 256))
+    run_static_case(x, w, sx, rows=rows, what=f"static {M}x{N}x{K}")
+
+
+def test_linear_static_prefill_full_size_with_bias():
+    log("[linear static] prefill 2048x14336x4096 bf16 with bias, sampled rows")
+    wl = inputs.prefill_ffn_up()
+    bias = inputs.random_matrix(170, (14336,), 0.5, torch.float32)
+    rows = sample_rows(2048, 4, seed=9, extra=(255, 256))
+    run_static_case(wl.x, wl.w, 0.03, rows=rows, bias=bias, what="static prefill")

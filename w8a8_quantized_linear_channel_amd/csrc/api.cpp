@@ -51,9 +51,9 @@ struct Carve {
 // for decode-sized M, the MFMA GEMM tiles above.
 hipError_t int8_on_codes(const int8_t* xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
                          const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N, const float* bias,
-                         void* y, q8_dtype y_dtype, int32_t* acc_out, hipStream_t st) {
+                         void* y, int y_dtype, int32_t* acc_out, hipStream_t st, double y_inv = 0.0) {
   if (M <= q8::kGemvMaxM)
-    return q8::launch_gemv_q8(xq, xs, rs, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st);
+    return q8::launch_gemv_q8(xq, xs, rs, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st, y_inv);
   q8::GemmArgs g{};
   g.a = reinterpret_cast<const uint8_t*>(xq);
   g.b = reinterpret_cast<const uint8_t*>(wq);
@@ -67,10 +67,23 @@ hipError_t int8_on_codes(const int8_t* xq, const float* xs, const int32_t* rs, i
   g.M = M;
   g.N = N;
   g.K = K;
+  g.y_inv = y_inv;
   return q8::launch_gemm(q8::GEMM_INT8, g, y_dtype, st);
 }
 
 struct LinearWs { size_t xq, xs, rs, total; };
+
+// Static path: the codes, the per-row copy of the static scale and the code
+// sums always pass through the workspace.
+LinearWs static_ws(int64_t M, int64_t K) {
+  Carve c;
+  LinearWs w;
+  w.xq = c.take((size_t)M * K);
+  w.xs = c.take((size_t)M * 4);
+  w.rs = c.take((size_t)M * 4);
+  w.total = c.off;
+  return w;
+}
 LinearWs linear_ws(int64_t M, int64_t K) {
   LinearWs w{0, 0, 0, 0};
   if (M <= q8::kGemvFusedMaxM) return w;   // fused decode path: the codes stay in LDS, no scratch
@@ -199,6 +212,7 @@ size_t q8_workspace_bytes(q8_op op, int64_t M, int64_t N, int64_t K) {
     case Q8_OP_LINEAR: return linear_ws(M, K).total;
     case Q8_OP_DECOMP: return decomp_ws(M, K).total;
     case Q8_OP_FP8: return fp8_ws(M, K).total;
+    case Q8_OP_STATIC: return static_ws(M, K).total;
   }
   return 0;
 }
@@ -371,6 +385,45 @@ q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {xq, x_scale, x_rowsum, wq, w_scale, w_zp, bias, y, acc_out}));
   return launched(int8_on_codes(xq, x_scale, x_rowsum, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st));
+}
+
+q8_status q8_quantize_act_static(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, float x_scale,
+                                 int8_t* xq, int32_t* x_rowsum, void* stream) {
+  if (!valid_dtype(x_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mk(M, K));
+  if (!x || !xq) return Q8_ERR_NULL_PTR;
+  if (!std::isfinite(x_scale) || x_scale <= 0.0f) return Q8_ERR_BAD_ARG;
+  if (!aligned16(x) || !aligned16(xq) || (x_rowsum && !aligned16(x_rowsum))) return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, xq, x_rowsum}));
+  return launched(q8::launch_quant_act_i8_static(x, x_dtype, M, K, x_scale, xq, nullptr, x_rowsum, st));
+}
+
+q8_status q8_linear_static(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, float x_scale,
+                           const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N,
+                           const float* bias, float y_scale, int8_t* yq, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(x_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mnk(M, N, K));
+  if (!x || !wq || !w_scale || !w_zp || !yq) return Q8_ERR_NULL_PTR;
+  if (!std::isfinite(x_scale) || x_scale <= 0.0f || !std::isfinite(y_scale) || y_scale <= 0.0f)
+    return Q8_ERR_BAD_ARG;
+  const LinearWs ws = static_ws(M, K);
+  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(yq) ||
+      (bias && !aligned16(bias)) || !aligned16(workspace))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, yq, workspace}));
+  char* base = static_cast<char*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
+  float* xs = reinterpret_cast<float*>(base + ws.xs);
+  int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
+  Q8_TRY(launched(q8::launch_quant_act_i8_static(x, x_dtype, M, K, x_scale, xq, xs, rs, st)));
+  const double y_inv = 1.0 / (double)y_scale;
+  return launched(int8_on_codes(xq, xs, rs, M, K, wq, w_scale, w_zp, N, bias, yq, q8::kOutInt8, nullptr, st, y_inv));
 }
 
 q8_status q8_linear_w8a16(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const int8_t* wq,

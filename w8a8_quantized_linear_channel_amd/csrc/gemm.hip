@@ -42,6 +42,7 @@
 #include "q8_kernels.hpp"
 
 namespace q8 {
+static_assert(DT_I8 == kOutInt8, "INT8 output code");
 namespace {
 
 
@@ -524,6 +525,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g) {
         }
       }
       const float sx = rsx[t];
+      if constexpr (YDT == DT_I8) {
+        // requantized INT8 output (int8 GEMM only): the codes are decided in
+        // float64 exactly as the definition states
+        if (!ok) continue;
+        int qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = requant_i8(sx, csb[e], a[e] - czi[e] * rrs[t], cbb[e], g.y_inv);
+        int8_t* yq = (int8_t*)g.y + o;
+        if (vec) {
+          *(v2i*)yq = v2i{(int)pack_lo_bytes(qv[0], qv[1], qv[2], qv[3]), (int)pack_lo_bytes(qv[4], qv[5], qv[6], qv[7])};
+        } else {
+          for (int e = 0; e < 8 && n + e < N; ++e) yq[e] = (int8_t)qv[e];
+        }
+        continue;
+      }
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -572,6 +588,7 @@ hipError_t launch_tiles(const GemmArgs& g, int ydt, hipStream_t st) {
   dim3 grid((unsigned)(ntm * ntn)), block(64 * NW);
   if constexpr (KIND == GEMM_INT8) {
     switch (ydt) {
+      case DT_I8: k_gemm<BM, BN, KIND, DT_I8, NW><<<grid, block, 0, st>>>(g); break;
       case DT_F32: k_gemm<BM, BN, KIND, DT_F32, NW><<<grid, block, 0, st>>>(g); break;
       case DT_F16: k_gemm<BM, BN, KIND, DT_F16, NW><<<grid, block, 0, st>>>(g); break;
       default: k_gemm<BM, BN, KIND, DT_BF16, NW><<<grid, block, 0, st>>>(g); break;

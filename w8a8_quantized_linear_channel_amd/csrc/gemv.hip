@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_q8(const int8_t* __restric
                                                          const float* __restrict__ w_scale,
                                                          const float* __restrict__ w_zp, int N,
                                                          const float* __restrict__ bias, void* __restrict__ y,
-                                                         int32_t* __restrict__ acc_out) {
+                                                         int32_t* __restrict__ acc_out, double y_inv) {
   __shared__ __attribute__((aligned(16))) uint8_t wsm[kWaves][kRows * kWPitch];
   __shared__ __attribute__((aligned(16))) uint8_t csm[kWaves][kRows * kWPitch];
   __shared__ v4i part[kWaves][64];
@@ -381,9 +381,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_q8(const int8_t* __restric
         const int a = t[r];
         if (acc_out) acc_out[(size_t)m * N + n] = a;
         const int cc = a - (int)fzp[r] * r_m;
-        float v = (s_m * fsc[r]) * (float)cc;
-        if (bias) v += fbi[r];
-        store_out<YDT>(y, (size_t)m * N + n, v);
+        if constexpr (YDT == DT_I8) {
+          ((int8_t*)y)[(size_t)m * N + n] = (int8_t)requant_i8(s_m, fsc[r], cc, fbi[r], y_inv);
+        } else {
+          float v = (s_m * fsc[r]) * (float)cc;
+          if (bias) v += fbi[r];
+          store_out<YDT>(y, (size_t)m * N + n, v);
+        }
       }
     }
   }
@@ -412,14 +416,18 @@ hipError_t launch_dt(const void* x, int64_t M, int64_t K, const int8_t* wq, cons
 
 hipError_t launch_gemv_q8(const int8_t* xq, const float* x_scale, const int32_t* x_rowsum, int64_t M, int64_t K,
                           const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N, const float* bias,
-                          void* y, int ydt, int32_t* acc_out, hipStream_t st) {
+                          void* y, int ydt, int32_t* acc_out, hipStream_t st, double y_inv) {
   dim3 grid((unsigned)((N + kRows - 1) / kRows)), block(kThreads);
   const int m = (int)M, k = (int)K, n = (int)N;
+#define Q8_GEMV_Q8(YT) \
+  k_gemv_q8<YT><<<grid, block, 0, st>>>(xq, x_scale, x_rowsum, m, k, wq, w_scale, w_zp, n, bias, y, acc_out, y_inv)
   switch (ydt) {
-    case DT_F32: k_gemv_q8<DT_F32><<<grid, block, 0, st>>>(xq, x_scale, x_rowsum, m, k, wq, w_scale, w_zp, n, bias, y, acc_out); break;
-    case DT_F16: k_gemv_q8<DT_F16><<<grid, block, 0, st>>>(xq, x_scale, x_rowsum, m, k, wq, w_scale, w_zp, n, bias, y, acc_out); break;
-    default: k_gemv_q8<DT_BF16><<<grid, block, 0, st>>>(xq, x_scale, x_rowsum, m, k, wq, w_scale, w_zp, n, bias, y, acc_out); break;
+    case DT_I8: Q8_GEMV_Q8(DT_I8); break;
+    case DT_F32: Q8_GEMV_Q8(DT_F32); break;
+    case DT_F16: Q8_GEMV_Q8(DT_F16); break;
+    default: Q8_GEMV_Q8(DT_BF16); break;
   }
+#undef Q8_GEMV_Q8
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // Element types of X / W / Y, matching q8_dtype.
-enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum Dt : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 /* requantized INT8 output (internal) */ };
 
 constexpr float kEps = 1e-8f;        // floor of every scale
 constexpr float kFp8Max = 448.0f;    // largest finite OCP e4m3fn value
@@ -222,6 +222,18 @@ typedef __attribute__((address_space(3))) void* lptr_t;   // LDS
 // M0, and the s_nop covers the M0-write -> LDS-DMA hazard.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// INT8 requantized output: clamp(rne(((S_x S_w) C + b) / S_y), +-127) with the
+// division as the product by inv = 1 / S_y, every step in float64 and none
+// contracted, so the code is decided exactly as the definition states.
+__device__ __forceinline__ int requant_i8(float sx, float sw, int c, float b, double inv) {
+#pragma clang fp contract(off)
+  double v = ((double)sx * (double)sw) * (double)c;
+  v = v + (double)b;
+  double q = rint(v * inv);
+  q = q < -127.0 ? -127.0 : (q > 127.0 ? 127.0 : q);
+  return (int)q;
+}
+
 // A buffer resource for raw byte loads over [p, p + bytes) (word 3 for raw
 // byte access on gfx9): loads past the end return zeros instead of faulting.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void* p, uint32_t bytes) {

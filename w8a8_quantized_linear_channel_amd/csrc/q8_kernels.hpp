@@ -10,6 +10,10 @@ hipError_t launch_quant_weight_i8(const void* w, int dt, int64_t N, int64_t K, i
                                   float* w_scale, float* w_zp, hipStream_t st);
 hipError_t launch_quant_rows_fp8(const void* x, int dt, int64_t R, int64_t K, float bound,
                                  uint8_t* xq, float* x_scale, hipStream_t st);
+// Static INT8 activation codes with a given per-tensor scale (quant.hip);
+// x_scale (nullable) receives the scale on every row.
+hipError_t launch_quant_act_i8_static(const void* x, int dt, int64_t M, int64_t K, float scale, int8_t* xq,
+                                      float* x_scale, int32_t* x_rowsum, hipStream_t st);
 hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, int8_t* xq, float* x_scale,
                                int32_t* x_rowsum, hipStream_t st);
 // fp16 activations of the LLM.int8 step: columns with flags[k] != 0 read as 0
@@ -36,7 +40,13 @@ struct GemmArgs {
   const uint16_t* x_f16;    // [M, K] fp16 activations
   const int32_t* out_idx;   // ascending outlier columns
   const int32_t* out_cnt;   // [1] number of outlier columns (device)
+  // INT8 output (ydt DT_I8): 1 / S_y of the static output scale
+  double y_inv;
 };
+
+// Output dtype code of the requantized INT8 output (the device enum's DT_I8;
+// q8_dtype has F32 = 0, F16 = 1, BF16 = 2).
+constexpr int kOutInt8 = 3;
 
 enum GemmKind : int { GEMM_INT8 = 0, GEMM_INT8_DECOMP = 1, GEMM_FP8 = 2 };
 
@@ -50,7 +60,7 @@ hipError_t launch_gemv_i8(const void* x, int xdt, int64_t M, int64_t K, const in
                           void* y, int ydt, int32_t* acc_out, hipStream_t st);
 hipError_t launch_gemv_q8(const int8_t* xq, const float* x_scale, const int32_t* x_rowsum, int64_t M, int64_t K,
                           const int8_t* wq, const float* w_scale, const float* w_zp, int64_t N, const float* bias,
-                          void* y, int ydt, int32_t* acc_out, hipStream_t st);
+                          void* y, int ydt, int32_t* acc_out, hipStream_t st, double y_inv = 0.0);
 constexpr int64_t kGemvFusedMaxM = 10;
 
 // Weight-only W8A16 linear for decode-sized M (w8a16.hip): x bf16 or f16.

@@ -116,6 +116,7 @@ enum RowMode : int {
   RM_I8 = 0,         // INT8 symmetric, S = absmax / 127, code row sums
   RM_I8_OUTLIER = 1, // as RM_I8 (fp16 only) with the flagged outlier columns read as 0
   RM_FP8 = 2,        // e4m3, S = min(absmax, bound) / 448
+  RM_I8_STATIC = 3,  // INT8 symmetric with a given scale S = bound, codes clamped to +-127
 };
 constexpr int kRowCache = 8;   // chunks per thread held in registers: 16-bit rows up to 16384 values
 
@@ -225,11 +226,13 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(v[e]));
   };
+  if constexpr (MODE != RM_I8_STATIC) {
 #pragma unroll
-  for (int j = 0; j < kRowCache; ++j)
-    if (tid + kThreads * j < nch) take_max(d[j], fw[j]);
-  for (int c = tid + kThreads * kRowCache; c < nch; c += kThreads) take_max(load_chunk<DT>(x, row, c), flag_word(c));
-  amax = block_max<kWaves>(amax, redf);
+    for (int j = 0; j < kRowCache; ++j)
+      if (tid + kThreads * j < nch) take_max(d[j], fw[j]);
+    for (int c = tid + kThreads * kRowCache; c < nch; c += kThreads) take_max(load_chunk<DT>(x, row, c), flag_word(c));
+    amax = block_max<kWaves>(amax, redf);
+  }
 
   float s;
   bool fast;   // the two-FMA quotient applies where the scale comes from a 16-bit row absmax
@@ -237,11 +240,14 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
     const float a = fminf(amax, bound);
     s = a / kFp8Max;
     fast = (DT != DT_F32) && (amax <= bound);
+  } else if constexpr (MODE == RM_I8_STATIC) {
+    s = bound;           // the calibrated scale, used as given (no floor)
+    fast = false;        // the two-FMA quotient needs a scale taken from the row absmax
   } else {
     s = amax / 127.0f;
     fast = DT != DT_F32;
   }
-  s = s < kEps ? kEps : s;
+  if constexpr (MODE != RM_I8_STATIC) s = s < kEps ? kEps : s;
   const float r = 1.0f / s;
   int qsum = 0;
   auto emit = [&](const v4i& ch, uint64_t f, int c) {
@@ -261,12 +267,16 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
         words[g] = pack4_e4m3(q[0], q[1], q[2], q[3]);
       } else {
         // |x / s| <= 127 (s = absmax/127 rounded, or the 1e-8 floor), so the
-        // codes need no clamp and the 1.5 * 2^23 rounding applies
+        // codes need no clamp and the 1.5 * 2^23 rounding applies; a static
+        // scale needs the clamp (clamping before rounding to even is the same
+        // for the integer bounds +-127)
         uint32_t b[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float xv = v[4 * g + e];
-          b[e] = rne_int8_bits(fast ? quot_fma(xv, s, r) : xv / s);
+          float y = fast ? quot_fma(xv, s, r) : xv / s;
+          if constexpr (MODE == RM_I8_STATIC) y = fminf(fmaxf(y, -127.0f), 127.0f);
+          b[e] = rne_int8_bits(y);
         }
         words[g] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
         qsum = sum_i8x4(words[g], qsum);
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
   for (int c = tid + kThreads * kRowCache; c < nch; c += kThreads) emit(load_chunk<DT>(x, row, c), flag_word(c), c);
   if constexpr (MODE != RM_FP8) qsum = block_sum<kWaves>(qsum, redi);
   if (tid == 0) {
-    x_scale[m] = s;
+    if (x_scale) x_scale[m] = s;
     if (MODE != RM_FP8 && x_rowsum) x_rowsum[m] = qsum;
   }
 }
@@ -331,6 +341,13 @@ hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, int8
                                int32_t* x_rowsum, hipStream_t st) {
   launch_rows<RM_I8>(x, dt, M, K, nullptr, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, nullptr, nullptr, nullptr,
                      nullptr, (unsigned)M, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_i8_static(const void* x, int dt, int64_t M, int64_t K, float scale, int8_t* xq,
+                                      float* x_scale, int32_t* x_rowsum, hipStream_t st) {
+  launch_rows<RM_I8_STATIC>(x, dt, M, K, nullptr, scale, (uint8_t*)xq, x_scale, x_rowsum, nullptr, nullptr, nullptr,
+                            nullptr, (unsigned)M, st);
   return hipGetLastError();
 }
 

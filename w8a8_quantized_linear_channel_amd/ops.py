@@ -14,7 +14,8 @@ from . import _lib
 
 _DT = {torch.float32: _lib.Q8_F32, torch.float16: _lib.Q8_F16, torch.bfloat16: _lib.Q8_BF16}
 _FMT = {"int8_asym": _lib.Q8_INT8_ASYM, "int8_sym": _lib.Q8_INT8_SYM, "fp8_e4m3": _lib.Q8_FP8_E4M3}
-_OP = {"linear": _lib.Q8_OP_LINEAR, "decomp": _lib.Q8_OP_DECOMP, "fp8": _lib.Q8_OP_FP8}
+_OP = {"linear": _lib.Q8_OP_LINEAR, "decomp": _lib.Q8_OP_DECOMP, "fp8": _lib.Q8_OP_FP8,
+       "static": _lib.Q8_OP_STATIC}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -247,3 +248,41 @@ def q8_linear_w8a16(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, w_
                                     _ptr(bias), _ptr(y), _DT[out_dtype], _stream(dev))
     _lib.check("q8_linear_w8a16", st)
     return y
+
+
+def q8_quantize_act_static(x: torch.Tensor, x_scale: float, out=None):
+    """Static INT8 codes with one calibrated scale: (xq int8 [M,K], rowsum int32 [M])."""
+    dev = x.device
+    M, K = x.shape
+    _need(x, "x", x.dtype, (M, K), dev)
+    xq, rs = out if out is not None else (torch.empty(M, K, dtype=torch.int8, device=dev),
+                                          torch.empty(M, dtype=torch.int32, device=dev))
+    _need(xq, "xq", torch.int8, (M, K), dev)
+    _need(rs, "x_rowsum", torch.int32, (M,), dev)
+    st = _lib.lib().q8_quantize_act_static(_ptr(x), _DT[x.dtype], M, K, float(x_scale), _ptr(xq), _ptr(rs),
+                                           _stream(dev))
+    _lib.check("q8_quantize_act_static", st)
+    return xq, rs
+
+
+def q8_linear_static(x: torch.Tensor, x_scale: float, wq: torch.Tensor, w_scale: torch.Tensor,
+                     w_zp: torch.Tensor, y_scale: float, bias: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """W8A8 linear with a static activation scale and INT8 output codes (scale y_scale)."""
+    dev = x.device
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(x, "x", x.dtype, (M, K), dev)
+    _need(wq, "wq", torch.int8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    _need(w_zp, "w_zp", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    yq = out if out is not None else torch.empty(M, N, dtype=torch.int8, device=dev)
+    _need(yq, "yq", torch.int8, (M, N), dev)
+    ws = workspace if workspace is not None else _workspace("static", M, N, K, dev)
+    st = _lib.lib().q8_linear_static(_ptr(x), _DT[x.dtype], M, K, float(x_scale), _ptr(wq), _ptr(w_scale),
+                                     _ptr(w_zp), N, _ptr(bias), float(y_scale), _ptr(yq), _ptr(ws),
+                                     ws.numel(), _stream(dev))
+    _lib.check("q8_linear_static", st)
+    return yq
