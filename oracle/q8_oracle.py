@@ -299,6 +299,27 @@ def fp8_abs_dot(x, wq_codes, w_scale, scale_ub=1200.0) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# O13: FP8 expert projection over routed tokens (grouped by expert)
+# --------------------------------------------------------------------------
+def linear_fp8_grouped(x, offsets, wq_codes, w_scale, scale_ub=1200.0):
+    """Mixture-of-experts FP8 projection ([FB] §5.4, Llama4 experts: the expert
+    weights are kept as one FP8 tensor with a per-row scale for each expert;
+    every expert's tokens get their own per-token activation quantization and
+    the rowwise FP8 product with that expert's weights).  Rows
+    offsets[e] .. offsets[e+1]-1 of X belong to expert e; each group is O8 + O9
+    with wq_codes[e], w_scale[e].  Returns y float64 [T, N]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E, N = wq_codes.shape[0], wq_codes.shape[1]
+    xf = to_f32(x)
+    y = np.zeros((xf.shape[0], N), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y[lo:hi], _ = linear_fp8(xf[lo:hi], wq_codes[e], w_scale[e], scale_ub)
+    return y
+
+
+# --------------------------------------------------------------------------
 # O10: weight-only W8A16 (16-bit activations, INT8 asymmetric weights)
 # --------------------------------------------------------------------------
 def linear_w8a16(x, wq, ws, wz, bias=None):

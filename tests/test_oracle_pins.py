@@ -532,3 +532,38 @@ def test_static_linear_bias_enters_before_requantization():
         yq, inter = O.linear_static(x, 1.0, wq, ws, wz, 1.0, bias=np.float32([b]))
         assert np.array_equal(inter["y"][:, 0], np.array([2.0, 0.0, -1.0]) + b)
         assert yq.tolist() == want
+
+
+# ---------------------------------------------------------------- O13 FP8 expert projection
+def test_fp8_grouped_row_by_row_and_empty_experts():
+    """Every token row equals the plain FP8 linear of that one row with its
+    expert's weights (the per-token scales make rows independent), whatever the
+    grouping; experts with no token (at the start, middle and end) are allowed."""
+    rng = np.random.default_rng(90)
+    E, N, K = 5, 12, 64
+    counts = [0, 3, 0, 4, 0]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    x = torch.from_numpy(rng.standard_normal((sum(counts), K)).astype(np.float32)).to(torch.bfloat16)
+    codes, scales = [], []
+    for e in range(E):
+        q, s_ = O.quantize_fp8_rowwise(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02))
+        codes.append(q)
+        scales.append(s_)
+    codes, scales = np.stack(codes), np.stack(scales)
+    y = O.linear_fp8_grouped(x, offsets, codes, scales)
+    owner = np.repeat(np.arange(E), counts)
+    for t in range(y.shape[0]):
+        ref, _ = O.linear_fp8(x[t:t + 1], codes[owner[t]], scales[owner[t]])
+        assert np.array_equal(y[t], ref[0])
+    # a row routed to another expert gives another result
+    alt, _ = O.linear_fp8(x[0:1], codes[3], scales[3])
+    assert not np.array_equal(y[0], alt[0])
+
+
+def test_fp8_grouped_single_expert_is_plain_fp8():
+    rng = np.random.default_rng(91)
+    x = torch.from_numpy(rng.standard_normal((7, 96)).astype(np.float32)).to(torch.bfloat16)
+    q, s_ = O.quantize_fp8_rowwise(rng.standard_normal((10, 96)).astype(np.float32) * np.float32(0.02))
+    y = O.linear_fp8_grouped(x, [0, 7], q[None], s_[None])
+    ref, _ = O.linear_fp8(x, q, s_)
+    assert np.array_equal(y, ref)

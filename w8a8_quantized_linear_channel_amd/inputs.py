@@ -111,6 +111,26 @@ def fp8_rowwise(seed: int = 4, M: int = 4096, K: int = 14336, N: int = 4096,
                     _cast(w, torch.float32), torch.bfloat16, {"scale_ub": 1200.0})
 
 
+def moe_fp8(seed: int = 5, T: int = 4096, E: int = 8, K: int = 4096, N: int = 4096,
+            alpha: float = 1.0) -> Workload:
+    """One FP8 expert projection of a mixture-of-experts layer on routed tokens:
+    X bf16 [T,K] ~ N(0,1), already grouped by expert; W [E,N,K] ~ N(0,0.02),
+    one matrix per expert; the token count of each expert is drawn from a
+    multinomial over Dirichlet(alpha) expert probabilities (a top-1 routing
+    stand-in), and extra["offsets"] are the cumulative counts [E+1].
+
+    Draw order: expert probabilities, counts, X, W.
+    """
+    rng = np.random.default_rng(seed)
+    p = rng.dirichlet(np.full(E, alpha))
+    counts = rng.multinomial(T, p)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = normal(rng, (T, K))
+    w = normal(rng, (E, N, K), 0.02)
+    return Workload(f"moe_fp8_T{T}_E{E}_N{N}_K{K}", _cast(x, torch.bfloat16), _cast(w, torch.float32),
+                    torch.bfloat16, {"offsets": torch.from_numpy(offsets), "scale_ub": 1200.0})
+
+
 def random_matrix(seed: int, shape, std: float = 1.0,
                   dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """Generic N(0, std) matrix for ragged-shape parity cases."""
