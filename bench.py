@@ -268,6 +268,33 @@ def bench_fp8(dev, steps, warmup):
                          "frac": flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}}
 
 
+# ------------------------------------------------------------------ FP8 experts on routed tokens
+def bench_moe_fp8(dev, steps, warmup):
+    """One FP8 expert projection over routed tokens (T = 4096 tokens, 8
+    experts, N = K = 4096, Dirichlet-multinomial routing): per-token FP8
+    quantization of all rows, then the grouped rowwise FP8 GEMM whose tiles
+    follow the device-side expert offsets."""
+    wl = inputs.moe_fp8()
+    off = wl.extra["offsets"]
+    E = off.numel() - 1
+    T, K = wl.x.shape
+    N = wl.w.shape[1]
+    x = wl.x.to(dev)
+    wq, ws, _ = q8.q8_quantize_weight(wl.w.reshape(E * N, K).to(dev), "fp8_e4m3")
+    wq, ws = wq.view(E, N, K), ws.view(E, N)
+    offd = off.to(dev)
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    wsp = torch.empty(q8.q8_workspace_bytes("fp8", T, N, K), dtype=torch.uint8, device=dev)
+
+    def step(i, pair):
+        q8.q8_linear_fp8_grouped(x, offd, wq, ws, scale_ub=1200.0, out=y, workspace=wsp)
+
+    ms, _, _ = timed_steps(step, steps, warmup, None)
+    flops = 2.0 * T * N * K
+    return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_expert": torch.diff(off).tolist(),
+            "shape": (T, N, K, E)}
+
+
 # ------------------------------------------------------------------ static scales, INT8 output
 def bench_static(dev, steps, warmup):
     """Prefill FFN-up shape with a static activation scale and an INT8 output:
@@ -446,6 +473,12 @@ def main():
                       "roofline": {k: round(v, 4) if isinstance(v, float) else v
                                    for k, v in d["roofline"].items()}}
     if args.only is None:
+        d = bench_moe_fp8(dev, args.steps, args.warmup)
+        T, N, K, E = d["shape"]
+        out["moe_fp8"] = {"workload": f"FP8 expert projection, {T} routed tokens over {E} experts "
+                                      f"{d['tokens_per_expert']}, N = K = {N}, bf16 out, ub 1200",
+                          "ms_per_step": round(d["ms_per_step"], 5), "TFLOPS": round(d["tflops"], 1),
+                          "frac_of_fp8_peak": round(d["tflops"] / PEAK_FP8_TFLOPS, 4)}
         d = bench_static(dev, args.steps, args.warmup)
         out["static_int8_out"] = {"workload": "prefill FFN-up 2048x14336x4096, static activation scale, INT8 output "
                                               "(q8_linear_static: static quantization + int8 GEMM, float64 requantize)",

@@ -207,6 +207,29 @@ q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_
                       void* y, void* stream);
 
 /*
+ * q8_linear_fp8_grouped -- FP8 expert projection of a mixture-of-experts layer
+ * on routed tokens ([FB] §5.4, Llama4 experts: per-expert FP8 weights with
+ * per-row scales; each expert's tokens get per-token FP8 quantization and the
+ * rowwise FP8 product with that expert's weights).  Rows
+ * expert_offsets[e] .. expert_offsets[e+1]-1 of x belong to expert e:
+ *     y[t,n] = S_x[t] S_w[e,n] sum_k e4m3(xq[t,k]) e4m3(wq[e,n,k])   (fp32 acc)
+ * with the activation quantization of q8_quantize_act(Q8_FP8_E4M3, scale_ub).
+ * x: bf16 [T, K] grouped by expert; expert_offsets: int32 [E+1] in DEVICE
+ * memory, non-decreasing from 0 to T (the offsets are read on the device and
+ * never copied to the host; values outside [0, T] or decreasing are clamped,
+ * which may leave rows of y unwritten but never reads or writes outside the
+ * arrays); wq: e4m3 [E, N, K] and w_scale: float [E, N] from
+ * q8_quantize_weight(Q8_FP8_E4M3) on the [E*N, K] view; y: bf16 [T, N].
+ * workspace: q8_workspace_bytes(Q8_OP_FP8, T, N, K).  Errors: Q8_ERR_BAD_SHAPE
+ * unless 1 <= E <= 65536; Q8_ERR_BAD_ARG for a NaN or non-positive scale_ub.
+ */
+q8_status q8_linear_fp8_grouped(const void* x_bf16, int64_t T, int64_t K,
+                                const int32_t* expert_offsets, int64_t E,
+                                const uint8_t* wq, const float* w_scale, int64_t N,
+                                float scale_ub, void* y_bf16, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * q8_quantize_act_static -- static INT8 activation quantization ("lecture
  * notes on LLM quantization", static quantization: the scale is calibrated
  * beforehand and applied unchanged at inference): one float scale S for the

@@ -32,6 +32,7 @@ def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
     for f in ["q8_quantize_weight", "q8_quantize_act", "q8_linear", "q8_linear_int8_decomp",
               "q8_linear_fp8", "q8_linear_w8a16", "q8_quantize_act_static", "q8_linear_static",
+              "q8_linear_fp8_grouped",
               "q8_workspace_bytes", "q8_status_str"]:
         assert f in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -196,3 +197,22 @@ def test_static_validation():
     assert call(M=1, wb=100) == 7            # the static path always needs its workspace
     assert call(y=MIS) == 6
     assert call(wz=None) == 1
+
+
+def test_fp8_grouped_validation():
+    f = _lib.lib().q8_linear_fp8_grouped
+    ok = dict(x=P, T=64, K=64, off=P, E=4, wq=P, ws=P, N=64, ub=1200.0, y=P, w=P2, wb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["T"], a["K"], a["off"], a["E"], a["wq"], a["ws"], a["N"], a["ub"], a["y"], a["w"],
+                 a["wb"], None)
+
+    assert call(E=0) == 2
+    assert call(E=(1 << 16) + 1) == 2
+    assert call(K=40) == 2
+    assert call(off=None) == 1
+    assert call(ub=NAN) == 5
+    assert call(ub=0.0) == 5
+    assert call(w=None) == 7
+    assert call(y=MIS) == 6

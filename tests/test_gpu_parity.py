@@ -500,3 +500,57 @@ def test_linear_static_prefill_full_size_with_bias():
     bias = inputs.random_matrix(170, (14336,), 0.5, torch.float32)
     rows = sample_rows(2048, 4, seed=9, extra=(255, 256))
     run_static_case(wl.x, wl.w, 0.03, rows=rows, bias=bias, what="static prefill")
+
+
+# ---------------------------------------------------------------- FP8 experts on routed tokens
+def run_grouped_case(x, w, offsets, rows_per_expert=None, ub=1200.0, what=""):
+    """GPU q8_linear_fp8_grouped; oracle O13 on every row (rows_per_expert None)
+    or on a sample of each expert's rows.  Also checks that the grouped call on
+    each expert's rows equals the plain FP8 linear of those rows, bit for bit."""
+    E, N, K = w.shape
+    T = x.shape[0]
+    wq, ws, _ = q8.q8_quantize_weight(g(w.reshape(E * N, K)), "fp8_e4m3")
+    wq, ws = wq.view(E, N, K), ws.view(E, N)
+    off = torch.tensor(np.asarray(offsets), dtype=torch.int32)
+    y = q8.q8_linear_fp8_grouped(g(x), g(off), wq, ws, scale_ub=ub)
+    rq, rs = O.quantize_fp8_rowwise(w.reshape(E * N, K))
+    rq, rs = rq.reshape(E, N, K), rs.reshape(E, N)
+    y_g = out_f64(y)
+    rows, ref, a = [], [], []
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        r = np.arange(lo, hi) if rows_per_expert is None else \
+            np.unique(np.r_[lo, hi - 1, np.random.default_rng(e).integers(lo, hi, rows_per_expert)])
+        yr, _ = O.linear_fp8(x[r], rq[e], rs[e], ub)
+        rows.append(r)
+        ref.append(yr)
+        a.append(O.fp8_abs_dot(x[r], rq[e], rs[e], ub))
+        if hi - lo <= 600:
+            # the same rows through the plain rowwise FP8 path give the same bits
+            y1 = q8.q8_linear_fp8(g(x[lo:hi]), wq[e].contiguous(), ws[e].contiguous(), scale_ub=ub)
+            assert torch.equal(y[lo:hi].view(torch.int16), y1.view(torch.int16)), f"{what}: expert {e} differs"
+    rows = np.concatenate(rows)
+    check_close(y_g[rows], np.concatenate(ref), f"{what} output ({len(rows)} rows)", abs_dot=np.concatenate(a))
+
+
+def test_fp8_grouped_moe_full_size():
+    wl = inputs.moe_fp8()
+    off = wl.extra["offsets"].numpy()
+    log(f"[fp8 experts] {wl.name}, tokens per expert {np.diff(off).tolist()}")
+    E = off.size - 1
+    run_grouped_case(wl.x, wl.w.view(E, -1, wl.w.shape[-1]), off, rows_per_expert=8, what="moe full")
+
+
+@pytest.mark.parametrize("counts,N,K", [([0, 130, 0, 7, 300, 0], 200, 528),     # empty experts, 64x128 tiles
+                                        ([513], 256, 256),                       # one expert, 256x256 tiles
+                                        ([1, 1, 1, 1], 96, 64),                  # one token each
+                                        ([150, 0, 400, 100], 1000, 1040)])       # 128x128 tiles (mean 162)
+def test_fp8_grouped_ragged(counts, N, K):
+    log(f"[fp8 experts] counts={counts} N={N} K={K}")
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    x = inputs.random_matrix(180 + sum(counts), (max(int(offsets[-1]), 1), K), 1.0, torch.bfloat16)
+    w = inputs.random_matrix(190 + N, (E, N, K), 0.02, torch.float32)
+    run_grouped_case(x[:int(offsets[-1])], w, offsets, what="moe ragged")

@@ -37,6 +37,7 @@ SIGNATURES = {
     "q8_gemm_int8": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P, _P]),
     "q8_gemm_fp8": (_INT, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
     "q8_linear_w8a16": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P]),
+    "q8_linear_fp8_grouped": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _I64, _F, _P, _P, _SZ, _P]),
     "q8_quantize_act_static": (_INT, [_P, _INT, _I64, _I64, _F, _P, _P, _P]),
     "q8_linear_static": (_INT, [_P, _INT, _I64, _I64, _F, _P, _P, _P, _I64, _P, _F, _P, _P, _SZ, _P]),
     "q8_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),

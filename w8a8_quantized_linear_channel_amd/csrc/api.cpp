@@ -18,7 +18,9 @@ namespace {
 constexpr int64_t kMaxK = 65536;          // keeps acc - Z*rowsum inside int32 (|.| <= 32512 K)
 constexpr int64_t kMaxRows = (1LL << 31) - 1;
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxGroups = 1 << 16;         // experts of one grouped call
 
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_dtype(int d) { return d == Q8_F32 || d == Q8_F16 || d == Q8_BF16; }
 
@@ -369,6 +371,41 @@ q8_status q8_linear_fp8(const void* x, int64_t M, int64_t K, const uint8_t* wq, 
   g.N = N;
   g.K = K;
   return launched(q8::launch_gemm(q8::GEMM_FP8, g, Q8_BF16, st));
+}
+
+q8_status q8_linear_fp8_grouped(const void* x, int64_t T, int64_t K, const int32_t* expert_offsets, int64_t E,
+                                const uint8_t* wq, const float* w_scale, int64_t N, float scale_ub, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  Q8_TRY(check_mnk(T, N, K));
+  if (E < 1 || E > kMaxGroups || E * N > kMaxRows) return Q8_ERR_BAD_SHAPE;
+  if (!x || !expert_offsets || !wq || !w_scale || !y) return Q8_ERR_NULL_PTR;
+  if (std::isnan(scale_ub) || scale_ub <= 0.0f) return Q8_ERR_BAD_ARG;
+  const Fp8Ws ws = fp8_ws(T, K);
+  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) || !aligned16(workspace) ||
+      !aligned4(expert_offsets))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, expert_offsets, wq, w_scale, y, workspace}));
+
+  char* base = static_cast<char*>(workspace);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + ws.xq);
+  float* xs = reinterpret_cast<float*>(base + ws.xs);
+  // per-token scales do not depend on the expert: one pass over all routed rows
+  Q8_TRY(launched(q8::launch_quant_rows_fp8(x, Q8_BF16, T, K, scale_ub, xq, xs, st)));
+  q8::GemmArgs g{};
+  g.a = xq;
+  g.b = wq;
+  g.a_scale = xs;
+  g.b_scale = w_scale;
+  g.y = y;
+  g.M = T;
+  g.N = N;
+  g.K = K;
+  g.groups = (int)E;
+  g.group_offsets = expert_offsets;
+  return launched(q8::launch_gemm_fp8_grouped(g, st));
 }
 
 q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,

@@ -125,8 +125,43 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int& tm, int& tn) 
   tn = inner / gsize;
 }
 
-template <int BM, int BN, int KIND, int YDT, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g) {
+// Grouped problems (experts over routed rows): rows offsets[e] .. offsets[e+1]-1
+// of A and Y belong to group e, whose B and column scales start at e N K and
+// e N.  Tile t of the launch is tile-column t % ntn of tile-row t / ntn,
+// counted over the groups' tile-rows in order; the offsets are clamped to
+// [0, M] and made non-decreasing, so no group reaches outside the arrays.
+// Returns false for the tiles past the last group (the grid is an upper bound).
+template <int BM, int BN, int ES>
+__device__ __forceinline__ bool group_tile(GemmArgs& g, int& tm, int& tn) {
+  const int T = (int)g.M, N = (int)g.N, K = (int)g.K;
+  const int ntn = (N + BN - 1) / BN;
+  const int t = blockIdx.x;
+  tn = t % ntn;
+  int r = t / ntn;
+  int lo = 0;
+  for (int e = 0; e < g.groups; ++e) {
+    int a = g.group_offsets[e], b = g.group_offsets[e + 1];
+    a = a < lo ? lo : (a > T ? T : a);
+    b = b < a ? a : (b > T ? T : b);
+    lo = b;
+    const int tr = (b - a + BM - 1) / BM;
+    if (r < tr) {
+      tm = r;
+      g.M = b - a;
+      g.a += (size_t)a * K;
+      g.a_scale += a;
+      g.y = (uint8_t*)g.y + (size_t)a * N * ES;
+      g.b += (size_t)e * N * K;
+      g.b_scale += (size_t)e * N;
+      return true;
+    }
+    r -= tr;
+  }
+  return false;
+}
+
+template <int BM, int BN, int KIND, int YDT, int NW, bool GROUPED = false>
+__global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   using MM = typename std::conditional<KIND == GEMM_FP8, MmaF8, MmaI8>::type;
   using TL = Tile<BM, BN, NW>;
   constexpr int kThreads = TL::NT;
@@ -147,10 +182,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g) {
   uint8_t* const sa3 = smem + 3 * kStageBytes;
   uint8_t* const sb3 = sa3 + BM * kBK;
 
-  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
-  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  GemmArgs g = g0;
   int tm, tn;
-  tile_coords(ntm, ntn, tm, tn);
+  if constexpr (GROUPED) {
+    if (!group_tile<BM, BN, YDT == DT_F32 ? 4 : 2>(g, tm, tn)) return;   // whole workgroup: no barrier yet
+  } else {
+    tile_coords((int)((g.M + BM - 1) / BM), (int)((g.N + BN - 1) / BN), tm, tn);
+  }
+  const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
@@ -619,6 +658,22 @@ hipError_t launch_kind(const GemmArgs& g, int ydt, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_gemm_fp8_grouped(const GemmArgs& g, hipStream_t st) {
+  // tile size from the mean rows per group; the grid bounds the tile count:
+  // sum_e ceil(M_e / BM) <= M / BM + groups
+  const int64_t mean = g.M / (g.groups > 0 ? g.groups : 1);
+  auto grid_for = [&](int bm, int bn) {
+    return dim3((unsigned)(((g.M + bm - 1) / bm + g.groups) * ((g.N + bn - 1) / bn)));
+  };
+  if (mean >= 256)
+    k_gemm<256, 256, GEMM_FP8, DT_BF16, 4, true><<<grid_for(256, 256), 256, 0, st>>>(g);
+  else if (mean >= 128)
+    k_gemm<128, 128, GEMM_FP8, DT_BF16, 4, true><<<grid_for(128, 128), 256, 0, st>>>(g);
+  else
+    k_gemm<64, 128, GEMM_FP8, DT_BF16, 4, true><<<grid_for(64, 128), 256, 0, st>>>(g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, int ydt, hipStream_t st) {
   switch (kind) {

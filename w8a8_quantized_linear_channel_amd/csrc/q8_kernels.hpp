@@ -42,6 +42,9 @@ struct GemmArgs {
   const int32_t* out_cnt;   // [1] number of outlier columns (device)
   // INT8 output (ydt DT_I8): 1 / S_y of the static output scale
   double y_inv;
+  // grouped problems (experts): groups > 0 and the device row offsets [groups+1]
+  int groups;
+  const int32_t* group_offsets;
 };
 
 // Output dtype code of the requantized INT8 output (the device enum's DT_I8;
@@ -51,6 +54,9 @@ constexpr int kOutInt8 = 3;
 enum GemmKind : int { GEMM_INT8 = 0, GEMM_INT8_DECOMP = 1, GEMM_FP8 = 2 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, int ydt, hipStream_t st);
+// FP8 rowwise GEMM over groups of rows (bf16 out): g.M is the total row count,
+// g.b / g.b_scale hold groups consecutive [N, K] / [N] blocks.
+hipError_t launch_gemm_fp8_grouped(const GemmArgs& g, hipStream_t st);
 
 // Decode-shaped int8 linear (gemv.hip).  M <= kGemvFusedMaxM: one launch with
 // the activation quantization fused in; kGemvFusedMaxM < M <= kGemvMaxM: on

@@ -286,3 +286,24 @@ def q8_linear_static(x: torch.Tensor, x_scale: float, wq: torch.Tensor, w_scale:
                                      ws.numel(), _stream(dev))
     _lib.check("q8_linear_static", st)
     return yq
+
+
+def q8_linear_fp8_grouped(x: torch.Tensor, expert_offsets: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                          scale_ub: float = 1200.0, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """FP8 expert projection on routed tokens: x bf16 [T,K] grouped by expert,
+    expert_offsets int32 [E+1] on the device, wq e4m3 [E,N,K], w_scale [E,N]."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    T, K = x.shape
+    E, N = wq.shape[0], wq.shape[1]
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    _need(wq, "wq", torch.uint8, (E, N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (E, N), dev)
+    y = out if out is not None else torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (T, N), dev)
+    ws = workspace if workspace is not None else _workspace("fp8", T, N, K, dev)
+    st = _lib.lib().q8_linear_fp8_grouped(_ptr(x), T, K, _ptr(expert_offsets), E, _ptr(wq), _ptr(w_scale), N,
+                                          float(scale_ub), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check("q8_linear_fp8_grouped", st)
+    return y
