@@ -36,6 +36,10 @@ listed with its reason in the design notes of the repository):
   R14 static quantization: one calibrated scale per activation tensor, symmetric (Z_x = 0, as for
       the dynamic codes); the INT8 output is the scaling of the float64 epilogue value by the
       reciprocal of the output scale, rounded half to even and clamped to [-127, 127]
+  R15 per-group weights: a group is a run of g consecutive weights along K inside one output row
+      (g = 64 or 128, K a multiple of g), quantized as O2 quantizes a row (range widened to 0,
+      eps floor, Z = -128 - rne(lo/S)); the activations stay per token; the parameters are stored
+      group-major, [K/g, N]
 """
 from __future__ import annotations
 
@@ -371,6 +375,77 @@ def linear_static(x, x_scale, wq, ws, wz, y_scale, bias=None):
     xs = np.full(xq.shape[0], np.float32(x_scale), dtype=np.float32)
     y = epilogue(acc, xs, rs, ws, wz, bias)
     return requantize_int8(y, y_scale), {"xq": xq, "x_rowsum": rs, "acc": acc, "y": y}
+
+
+# --------------------------------------------------------------------------
+# O14 / O15: per-group asymmetric INT8 weights
+# --------------------------------------------------------------------------
+def quantize_weight_int8_grouped(w, group: int):
+    """Per-group asymmetric INT8 quantization of W [N, K].
+
+    [OV] §2.2 (granularity table: between per-tensor and per-channel sit
+    groups of 64 to 128 parameters, each group with its own quantization
+    parameters) and [NOTE] quantization granularity passage (per-group: the
+    data is cut into blocks, each with its own scale and zero point).  R15:
+    group j of row n is w[n, j g : (j+1) g]; for each group, as O2 for a row,
+        lo = min(0, min w), hi = max(0, max w)
+        S  = max((hi - lo) / 255, eps)                 binary32
+        Z  = -128 - rne(lo / S)
+        q  = clamp(rne(w / S) + Z, -128, 127)
+    Returns (q int8 [N,K], S float32 [K/g, N], Z float32 [K/g, N]); the
+    parameters are group-major: S[j, n] belongs to group j of row n.
+    """
+    w = to_f32(w)
+    N, K = w.shape
+    assert group > 0 and K % group == 0
+    G = K // group
+    q = np.empty((N, K), dtype=np.int8)
+    S = np.empty((G, N), dtype=np.float32)
+    Z = np.empty((G, N), dtype=np.float32)
+    for j in range(G):
+        blk = w[:, j * group:(j + 1) * group]
+        lo = np.minimum(blk.min(axis=1), np.float32(0))
+        hi = np.maximum(blk.max(axis=1), np.float32(0))
+        s = np.maximum((hi - lo) / INT8_ASYM_LEVELS, EPS).astype(np.float32)
+        z = (np.float32(-128) - np.rint(lo / s)).astype(np.float32)
+        q[:, j * group:(j + 1) * group] = np.clip(np.rint(blk / s[:, None]) + z[:, None], -128, 127)
+        S[j] = s
+        Z[j] = z
+    return q, S, Z
+
+
+def group_code_sums(xq, group: int) -> np.ndarray:
+    """Sum of the activation codes over each group of columns:
+    gsum[j, m] = Sum_{k in group j} q_x[m, k], group-major [K/g, M], int32."""
+    xq = np.asarray(xq).astype(np.int64)
+    M, K = xq.shape
+    assert K % group == 0
+    return xq.reshape(M, K // group, group).sum(axis=2).T.astype(np.int32)
+
+
+def linear_int8_grouped(x, wq, S, Z, group: int, bias=None):
+    """W8A8 linear with per-group asymmetric weights (O14) and dynamic
+    per-token INT8 activations (O3).  The quantized-matmul identity of O5
+    ([OV] §2.1, R2) taken group by group, since S and Z change with the group:
+        C_j[m,n] = Sum_{k in j} q_x[m,k] q_w[n,k] - Z[j,n] Sum_{k in j} q_x[m,k]   (exact integers)
+        y[m,n]   = S_x[m] Sum_j S[j,n] C_j[m,n]  (+ b[n])                          (float64)
+    Returns (y float64 [M,N], dict of intermediates)."""
+    xq, xs, _ = quantize_act_int8_sym(x)
+    M, K = xq.shape
+    N = wq.shape[0]
+    G = K // group
+    assert K % group == 0 and S.shape == (G, N) and Z.shape == (G, N)
+    gsum = group_code_sums(xq, group)
+    t = np.zeros((M, N), dtype=np.float64)
+    for j in range(G):
+        cols = slice(j * group, (j + 1) * group)
+        acc = xq[:, cols].astype(np.int64) @ wq[:, cols].astype(np.int64).T
+        c = acc - Z[j].astype(np.int64)[None, :] * gsum[j].astype(np.int64)[:, None]
+        t += S[j].astype(np.float64)[None, :] * c.astype(np.float64)
+    y = xs.astype(np.float64)[:, None] * t
+    if bias is not None:
+        y = y + to_f32(bias).astype(np.float64)[None, :]
+    return y, {"xq": xq, "x_scale": xs, "gsum": gsum}
 
 
 # --------------------------------------------------------------------------

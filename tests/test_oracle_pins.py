@@ -567,3 +567,121 @@ def test_fp8_grouped_single_expert_is_plain_fp8():
     y = O.linear_fp8_grouped(x, [0, 7], q[None], s_[None])
     ref, _ = O.linear_fp8(x, q, s_)
     assert np.array_equal(y, ref)
+
+
+# ---------------------------------------------------------------- O14 / O15 per-group weights
+def test_grouped_quant_hand_worked_row():
+    """One row, two groups of 4, worked by hand from the min-max definition
+    (S = (hi - lo)/255 over the group's range widened to 0, Z = -128 - rne(lo/S)):
+      [-1, 0, 1, 2]  lo = -1, hi = 2:  S = 3/255,  Z = -128 + 85 = -43,
+                     codes -85-43, -43, 85-43, 170-43 -> -128, -43, 42, 127
+      [4, 8, -2, 0]  lo = -2, hi = 8:  S = 10/255, Z = -128 + 51 = -77,
+                     codes 102-77, 204-77, -51-77, -77 -> 25, 127, -128, -77"""
+    w = np.array([[-1, 0, 1, 2, 4, 8, -2, 0]], np.float32)
+    q, S, Z = O.quantize_weight_int8_grouped(w, 4)
+    assert S.shape == (2, 1) and Z.shape == (2, 1)
+    assert q[0].tolist() == [-128, -43, 42, 127, 25, 127, -128, -77]
+    assert Z[:, 0].tolist() == [-43.0, -77.0]
+    assert S[0, 0] == np.float32(f32_round(Fraction(3) / 255))
+    assert S[1, 0] == np.float32(f32_round(Fraction(10) / 255))
+
+
+def test_grouped_quant_one_group_is_per_channel():
+    rng = np.random.default_rng(80)
+    w = (rng.standard_normal((32, 128)) * 0.02).astype(np.float32)
+    q, S, Z = O.quantize_weight_int8_grouped(w, 128)
+    q1, s1, z1 = O.quantize_weight_int8_asym(w)
+    assert np.array_equal(q, q1) and np.array_equal(S[0], s1) and np.array_equal(Z[0], z1)
+
+
+def test_grouped_quant_layout_is_rows_of_groups():
+    """Group j of row n is w[n, j g:(j+1) g] and its parameters sit at [j, n]:
+    quantizing the matrix of all groups as rows (per-channel, O2, pinned above)
+    must give the same codes, and the parameters transposed."""
+    rng = np.random.default_rng(81)
+    N, K, g = 12, 256, 64
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w *= np.float32(10.0) ** rng.integers(-2, 3, (N, K // g)).repeat(g, axis=1).astype(np.float32)
+    q, S, Z = O.quantize_weight_int8_grouped(w, g)
+    qr, sr, zr = O.quantize_weight_int8_asym(w.reshape(N * (K // g), g))
+    assert np.array_equal(q.reshape(N * (K // g), g), qr)
+    assert np.array_equal(S.T.reshape(-1), sr) and np.array_equal(Z.T.reshape(-1), zr)
+
+
+def test_grouped_quant_roundtrip_within_half_step_per_group():
+    rng = np.random.default_rng(82)
+    N, K, g = 16, 512, 128
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[:, :g] = np.abs(w[:, :g])            # one-signed groups: Z = -128
+    w[:, g:2 * g] = -np.abs(w[:, g:2 * g])  # Z = 127
+    w[:, 3 * g:] *= np.float32(100.0)
+    q, S, Z = O.quantize_weight_int8_grouped(w, g)
+    assert np.all(Z[0] == -128) and np.all(Z[1] == 127)
+    Se = np.repeat(S.T, g, axis=1).astype(np.float64)
+    Ze = np.repeat(Z.T, g, axis=1).astype(np.float64)
+    err = np.abs(w.astype(np.float64) - Se * (q.astype(np.float64) - Ze))
+    assert np.all(err <= Se * (0.5 + 1e-5))
+
+
+def _grouped_weights(rng, N, K, g):
+    """Weights whose groups differ by orders of magnitude and include
+    one-signed groups, so a parameter taken from the wrong group shows."""
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w *= np.float32(10.0) ** rng.integers(-2, 3, (N, K // g)).repeat(g, axis=1).astype(np.float32)
+    w[:, :g] = np.abs(w[:, :g])
+    if K >= 2 * g:
+        w[:, g:2 * g] = -np.abs(w[:, g:2 * g])
+    return w
+
+
+def test_grouped_linear_one_group_equals_per_channel():
+    rng = np.random.default_rng(83)
+    x = rng.standard_normal((8, 128)).astype(np.float32)
+    w = (rng.standard_normal((24, 128)) * 0.02).astype(np.float32)
+    q, S, Z = O.quantize_weight_int8_grouped(w, 128)
+    b = rng.standard_normal(24).astype(np.float32)
+    y, _ = O.linear_int8_grouped(x, q, S, Z, 128, bias=b)
+    q1, s1, z1 = O.quantize_weight_int8_asym(w)
+    y1, _ = O.linear_int8(x, q1, s1, z1, bias=b)
+    np.testing.assert_allclose(y, y1, rtol=1e-14, atol=0)
+
+
+def test_grouped_linear_equals_dequantized_product():
+    """The grouped identity must equal the plain product of the dequantized
+    operands, (S_x q_x) . (S_j (q_w - Z_j))^T, computed by one float64 matmul
+    with the parameters expanded column by column: a dropped zero-point term,
+    a wrong sign, or a parameter from the wrong group or row fails it."""
+    rng = np.random.default_rng(84)
+    for (M, N, K, g) in [(5, 40, 512, 128), (3, 17, 384, 64)]:
+        x = rng.standard_normal((M, K)).astype(np.float32)
+        w = _grouped_weights(rng, N, K, g)
+        q, S, Z = O.quantize_weight_int8_grouped(w, g)
+        y, inter = O.linear_int8_grouped(x, q, S, Z, g)
+        xs = inter["x_scale"].astype(np.float64)[:, None] * inter["xq"].astype(np.float64)
+        Se = np.repeat(S.T, g, axis=1).astype(np.float64)
+        Ze = np.repeat(Z.T, g, axis=1).astype(np.float64)
+        ref = xs @ (Se * (q.astype(np.float64) - Ze)).T
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_grouped_linear_brute_force():
+    """Pure-Python loop with exact rationals over
+    y[m,n] = S_x[m] Sum_k S[k // g, n] (q_w[n,k] - Z[k // g, n]) q_x[m,k], and
+    the group code sums by hand."""
+    rng = np.random.default_rng(85)
+    M, N, K, g = 2, 3, 16, 4
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = _grouped_weights(rng, N, K, g)
+    q, S, Z = O.quantize_weight_int8_grouped(w, g)
+    y, inter = O.linear_int8_grouped(x, q, S, Z, g)
+    xq, xs = inter["xq"], inter["x_scale"]
+    for j in range(K // g):
+        for m in range(M):
+            assert inter["gsum"][j, m] == sum(int(xq[m, k]) for k in range(j * g, (j + 1) * g))
+    for m in range(M):
+        for n in range(N):
+            ref = Fraction(0)
+            for k in range(K):
+                ref += Fraction(float(S[k // g, n])) * (int(q[n, k]) - int(Z[k // g, n])) * int(xq[m, k])
+            ref *= Fraction(float(xs[m]))
+            assert abs(y[m, n] - float(ref)) <= 1e-13 * max(abs(float(ref)), 1e-30)
