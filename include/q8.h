@@ -66,7 +66,9 @@ typedef enum q8_format {
   Q8_FP8_E4M3 = 2   /* weights or activations: per-row OCP e4m3fn, r = S q    */
 } q8_format;
 
-typedef enum q8_op { Q8_OP_LINEAR = 0, Q8_OP_DECOMP = 1, Q8_OP_FP8 = 2, Q8_OP_STATIC = 3 } q8_op;
+typedef enum q8_op {
+  Q8_OP_LINEAR = 0, Q8_OP_DECOMP = 1, Q8_OP_FP8 = 2, Q8_OP_STATIC = 3, Q8_OP_GROUPED = 4
+} q8_op;
 
 /*
  * q8_quantize_weight -- per-output-channel weight quantization (done once,
@@ -274,6 +276,41 @@ q8_status q8_linear_w8a16(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
                           const int8_t* wq, const float* w_scale, const float* w_zp,
                           int64_t N, const float* bias, void* y, q8_dtype y_dtype,
                           void* stream);
+
+/*
+ * q8_quantize_weight_grouped -- per-group asymmetric INT8 weights ("大模型量化
+ * 技术概述" §2.2, granularity: groups of 64 to 128 parameters, each with its
+ * own parameters; lecture notes' granularity passage: per-group blocks with
+ * their own scale and zero point).  Group j of row n is w[n, j g .. j g + g-1];
+ * each group is quantized as Q8_INT8_ASYM quantizes a row:
+ *     lo = min(0, min w), hi = max(0, max w), S = max((hi - lo)/255, 1e-8),
+ *     Z = -128 - rne(lo / S),  q = clamp(rne(w / S) + Z, -128, 127)
+ * w: [N, K] of w_dtype; group: 64 or 128 and K a multiple of it (else
+ * Q8_ERR_BAD_SHAPE); wq: int8 [N, K]; w_scale, w_zp: float [K/group, N],
+ * group-major (w_scale[j * N + n] belongs to group j of row n; w_zp holds the
+ * integer Z).
+ */
+q8_status q8_quantize_weight_grouped(const void* w, q8_dtype w_dtype, int64_t N, int64_t K,
+                                     int64_t group, int8_t* wq, float* w_scale, float* w_zp,
+                                     void* stream);
+
+/*
+ * q8_linear_grouped -- W8A8 linear with per-group weights: the activations are
+ * quantized per token as q8_quantize_act(Q8_INT8_SYM) does, and the
+ * quantized-matmul identity is taken group by group ([OV] §2.1 with r = S (q - Z)):
+ *     C_j[m,n] = sum_{k in j} xq[m,k] wq[n,k] - Z[j,n] sum_{k in j} xq[m,k]   (exact)
+ *     y[m,n]   = S_x[m] sum_j S[j,n] C_j[m,n]  (+ bias[n])                    (fp32)
+ * x: [M, K] of x_dtype; wq/w_scale/w_zp from q8_quantize_weight_grouped with
+ * the same group; bias: float [N] or NULL; y: [M, N] of y_dtype.  workspace:
+ * q8_workspace_bytes(Q8_OP_GROUPED, M, N, K) bytes (codes, scales and group
+ * code sums, sized for group 64).  Errors: Q8_ERR_BAD_SHAPE for a group other
+ * than 64 or 128 or a K that is not a multiple of it.
+ */
+q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
+                            const int8_t* wq, const float* w_scale, const float* w_zp,
+                            int64_t group, int64_t N, const float* bias, void* y,
+                            q8_dtype y_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Bytes of workspace the call `op` needs at this shape (0 if none); returns 0
  * for invalid shapes as well, which the call itself then rejects. */

@@ -32,7 +32,7 @@ def test_header_declares_the_five_calls_and_helpers():
     names = declared_functions()
     for f in ["q8_quantize_weight", "q8_quantize_act", "q8_linear", "q8_linear_int8_decomp",
               "q8_linear_fp8", "q8_linear_w8a16", "q8_quantize_act_static", "q8_linear_static",
-              "q8_linear_fp8_grouped",
+              "q8_linear_fp8_grouped", "q8_quantize_weight_grouped", "q8_linear_grouped",
               "q8_workspace_bytes", "q8_status_str"]:
         assert f in names
     assert set(names) == set(_lib.SIGNATURES)
@@ -68,6 +68,9 @@ def test_workspace_sizes():
     # static path: codes, per-row scale copy and code sums at every M
     assert ws(_lib.Q8_OP_STATIC, 1, 4096, 4096) == 4096 + 2 * 256
     assert ws(_lib.Q8_OP_STATIC, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192
+    # per-group path: codes, scales and group code sums sized for groups of 64
+    assert ws(_lib.Q8_OP_GROUPED, 1, 4096, 4096) == 4096 + 256 + 256
+    assert ws(_lib.Q8_OP_GROUPED, 2048, 14336, 4096) == 2048 * 4096 + 8192 + 2048 * 64 * 4
     # invalid shapes give 0
     assert ws(_lib.Q8_OP_LINEAR, 0, 16, 16) == 0
     assert ws(_lib.Q8_OP_LINEAR, 16, 16, 24) == 0
@@ -216,3 +219,31 @@ def test_fp8_grouped_validation():
     assert call(ub=0.0) == 5
     assert call(w=None) == 7
     assert call(y=MIS) == 6
+
+
+def test_grouped_validation():
+    E = _lib
+    q = _lib.lib().q8_quantize_weight_grouped
+    assert q(P, E.Q8_BF16, 64, 256, 32, P, P, P, None) == 2             # group 64 or 128 only
+    assert q(P, E.Q8_BF16, 64, 192, 128, P, P, P, None) == 2            # K a multiple of the group
+    assert q(P, 7, 64, 256, 128, P, P, P, None) == 3
+    assert q(P, E.Q8_BF16, 64, 256, 128, P, P, None, None) == 1
+    assert q(P, E.Q8_BF16, 64, 256, 128, P, MIS, P, None) == 6
+    f = _lib.lib().q8_linear_grouped
+    ok = dict(x=P, xd=E.Q8_BF16, M=64, K=256, wq=P, ws=P, wz=P, g=128, N=64, b=None, y=P, yd=E.Q8_BF16,
+              w=P2, wb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["xd"], a["M"], a["K"], a["wq"], a["ws"], a["wz"], a["g"], a["N"], a["b"], a["y"],
+                 a["yd"], a["w"], a["wb"], None)
+
+    assert call(g=96) == 2
+    assert call(K=320) == 2                  # not a multiple of 128
+    assert call(K=320, g=64, w=None) == 7    # a multiple of 64 passes the shape check
+    assert call(xd=9) == 3
+    assert call(wz=None) == 1
+    assert call(w=None) == 7
+    assert call(M=1, wb=100) == 7            # the grouped path always needs its workspace
+    assert call(y=MIS) == 6
+    assert call(ws=MIS) == 6

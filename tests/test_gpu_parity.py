@@ -554,3 +554,117 @@ def test_fp8_grouped_ragged(counts, N, K):
     x = inputs.random_matrix(180 + sum(counts), (max(int(offsets[-1]), 1), K), 1.0, torch.bfloat16)
     w = inputs.random_matrix(190 + N, (E, N, K), 0.02, torch.float32)
     run_grouped_case(x[:int(offsets[-1])], w, offsets, what="moe ragged")
+
+
+# ---------------------------------------------------------------- per-group weights (q8_linear_grouped)
+def varied_groups(w, group, seed):
+    """The same weights with every group scaled by 10^u (u in -1..1) and the
+    first two groups of every row made one-signed (Z = -128 and Z = 127), so a
+    parameter taken from the wrong group or row changes the output."""
+    a = w.float().numpy().copy()
+    N, K = a.shape
+    rng = np.random.default_rng(seed)
+    a *= (10.0 ** rng.integers(-1, 2, (N, K // group))).repeat(group, axis=1).astype(np.float32)
+    a[:, :group] = np.abs(a[:, :group])
+    if K >= 2 * group:
+        a[:, group:2 * group] = -np.abs(a[:, group:2 * group])
+    return torch.from_numpy(a).to(w.dtype)
+
+
+def check_grouped_weights(w, group, what=""):
+    wq, ws, wz = q8.q8_quantize_weight_grouped(g(w), group)
+    rq, rs, rz = O.quantize_weight_int8_grouped(w, group)
+    assert_equal(host(wq), rq, f"{what} grouped weight codes")
+    assert_equal(f32_bits(host(ws)), f32_bits(rs), f"{what} grouped scale bits")
+    assert_equal(host(wz), rz, f"{what} grouped zero points")
+    return (wq, ws, wz), (rq, rs, rz)
+
+
+def run_grouped_linear_case(x, w, group, out_dtype, rows=None, cols=None, bias=None, what=""):
+    """GPU q8_linear_grouped on the full problem; oracle O15 on `rows` x `cols`."""
+    (wq, ws, wz), (rq, rs, rz) = check_grouped_weights(w, group, what)
+    b = g(bias) if bias is not None else None
+    y = q8.q8_linear_grouped(g(x), wq, ws, wz, group, bias=b, out_dtype=out_dtype)
+    xr = x if rows is None else x[rows]
+    br = bias
+    if cols is not None:
+        rq, rs, rz = rq[cols], rs[:, cols], rz[:, cols]
+        br = None if bias is None else bias[cols]
+    y_ref, _ = O.linear_int8_grouped(xr, rq, rs, rz, group, bias=br)
+    yg = out_f64(y)
+    if rows is not None:
+        yg = yg[rows]
+    if cols is not None:
+        yg = yg[:, cols]
+    check_close(yg, y_ref, f"{what} output")
+    return y
+
+
+@pytest.mark.parametrize("name,N,K,group,dt,seed", [("f32_256x256_g128", 256, 256, 128, torch.float32, 90),
+                                                    ("f32_37x192_g64", 37, 192, 64, torch.float32, 91),
+                                                    ("bf16_65x4224_g128", 65, 4224, 128, torch.bfloat16, 92),
+                                                    ("f16_9x8256_g64", 9, 8256, 64, torch.float16, 93)])
+def test_quantize_weight_grouped(name, N, K, group, dt, seed):
+    log(f"[grouped] weight quantization {name}")
+    w = inputs.random_matrix(seed, (N, K), 0.02, dt)
+    check_grouped_weights(w, group, name)
+    check_grouped_weights(varied_groups(w, group, seed), group, name + " varied")
+
+
+def test_quantize_weight_grouped_edge_groups():
+    log("[grouped] weight quantization: zero, constant and one-signed groups")
+    w = inputs.random_matrix(94, (8, 512), 0.02, torch.float32).numpy().copy()
+    w[0, :64] = 0.0                 # all-zero group: S = eps, Z = -128, codes -128
+    w[1, 64:128] = 0.37             # constant positive group
+    w[2, 128:192] = -1e-3           # constant negative group
+    w[3, :] = np.abs(w[3, :])
+    w[4, :] = -np.abs(w[4, :])
+    check_grouped_weights(torch.from_numpy(w), 64, "edge")
+
+
+@pytest.mark.parametrize("group", [64, 128])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_linear_grouped_decode_qproj_full_size(M, group):
+    log(f"[grouped] decode q_proj M={M} N=K=4096 group={group} bf16")
+    wl = inputs.decode_qproj(M=M)
+    cols = np.sort(np.random.default_rng(M + group).choice(4096, 384, replace=False))
+    cols = np.unique(np.r_[cols, [0, 15, 16, 4095]])
+    run_grouped_linear_case(wl.x, wl.w, group, torch.bfloat16, cols=cols, what="decode")
+
+
+@pytest.mark.parametrize("M,N,K,group,dt", [(3, 100, 4224, 128, torch.bfloat16),   # decode: partial 2nd segment, N tail
+                                            (16, 37, 8256, 64, torch.float16),     # decode: 3 segments, N tail
+                                            (1, 1, 128, 128, torch.float32),       # one output, one group
+                                            (13, 50, 64, 64, torch.bfloat16),      # one group of 64
+                                            (17, 64, 128, 128, torch.bfloat16),    # just above the decode path
+                                            (300, 520, 1024, 64, torch.bfloat16),  # GEMM: ragged M and N
+                                            (1000, 3000, 256, 128, torch.float16), # GEMM: few groups
+                                            (130, 4100, 4224, 128, torch.float32), # GEMM: odd group count
+                                            (257, 300, 192, 64, torch.bfloat16)])  # GEMM: 3 stages, 3 groups
+def test_linear_grouped_ragged(M, N, K, group, dt):
+    log(f"[grouped] ragged M={M} N={N} K={K} group={group} {dt}")
+    x = inputs.random_matrix(100 + M, (M, K), 1.0, dt)
+    w = varied_groups(inputs.random_matrix(110 + N, (N, K), 0.02, torch.float32), group, N)
+    rows = None if M * N * K <= 2e8 else sample_rows(M, 10, seed=M, extra=(127, 128, 255, 256))
+    run_grouped_linear_case(x, w, group, torch.float32, rows=rows, what="ragged")
+
+
+def test_linear_grouped_prefill_full_size_sampled():
+    log("[grouped] prefill FFN-up 2048x14336x4096 group=128 bf16, sampled rows")
+    wl = inputs.prefill_ffn_up()
+    rows = sample_rows(2048, 6, seed=8, extra=(127, 128, 1024))
+    y = run_grouped_linear_case(wl.x, wl.w, 128, torch.bfloat16, rows=rows, what="prefill")
+    wq, ws, wz = q8.q8_quantize_weight_grouped(g(wl.w), 128)
+    y2 = q8.q8_linear_grouped(g(wl.x), wq, ws, wz, 128, out_dtype=torch.bfloat16)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "second call differs"
+
+
+@pytest.mark.parametrize("M", [5, 200])
+def test_linear_grouped_bias_and_dtypes(M):
+    log(f"[grouped] bias + input/output dtypes M={M}")
+    w = varied_groups(inputs.random_matrix(120, (96, 512), 0.02, torch.float32), 128, 7)
+    bias = inputs.random_matrix(121, (96,), 0.5, torch.float32)
+    for xd in (torch.float32, torch.float16, torch.bfloat16):
+        x = inputs.random_matrix(122, (M, 512), 1.0, xd)
+        for od in (torch.float32, torch.float16, torch.bfloat16):
+            run_grouped_linear_case(x, w, 128, od, bias=bias, what=f"x {xd} y {od}")

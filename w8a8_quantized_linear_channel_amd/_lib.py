@@ -19,7 +19,7 @@ STATUS_NAMES = {
 }
 Q8_F32, Q8_F16, Q8_BF16 = 0, 1, 2
 Q8_INT8_ASYM, Q8_INT8_SYM, Q8_FP8_E4M3 = 0, 1, 2
-Q8_OP_LINEAR, Q8_OP_DECOMP, Q8_OP_FP8, Q8_OP_STATIC = 0, 1, 2, 3
+Q8_OP_LINEAR, Q8_OP_DECOMP, Q8_OP_FP8, Q8_OP_STATIC, Q8_OP_GROUPED = 0, 1, 2, 3, 4
 
 # every symbol include/q8.h declares, with (restype, argtypes)
 _P = ctypes.c_void_p
@@ -40,6 +40,8 @@ SIGNATURES = {
     "q8_linear_fp8_grouped": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P, _I64, _F, _P, _P, _SZ, _P]),
     "q8_quantize_act_static": (_INT, [_P, _INT, _I64, _I64, _F, _P, _P, _P]),
     "q8_linear_static": (_INT, [_P, _INT, _I64, _I64, _F, _P, _P, _P, _I64, _P, _F, _P, _P, _SZ, _P]),
+    "q8_quantize_weight_grouped": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "q8_linear_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _INT, _P, _SZ, _P]),
     "q8_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     "q8_status_str": (ctypes.c_char_p, [_INT]),
 }

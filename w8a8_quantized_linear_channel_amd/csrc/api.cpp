@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "q8_group.hpp"
 #include "q8_kernels.hpp"
 
 namespace {
@@ -96,6 +97,20 @@ LinearWs linear_ws(int64_t M, int64_t K) {
   w.total = c.off;
   return w;
 }
+
+// Per-group path: codes, scales and the group code sums [K / group, M], sized
+// for the smallest group (64).
+struct GroupedWs { size_t xq, xs, gs, total; };
+GroupedWs grouped_ws(int64_t M, int64_t K) {
+  Carve c;
+  GroupedWs w;
+  w.xq = c.take((size_t)M * K);
+  w.xs = c.take((size_t)M * 4);
+  w.gs = c.take((size_t)M * (K / 64) * 4);
+  w.total = c.off;
+  return w;
+}
+bool valid_group(int64_t group, int64_t K) { return (group == 64 || group == 128) && K % group == 0; }
 
 struct DecompWs { size_t xq, xs, rs, flags, idx, cnt, total; };
 DecompWs decomp_ws(int64_t M, int64_t K) {
@@ -215,6 +230,7 @@ size_t q8_workspace_bytes(q8_op op, int64_t M, int64_t N, int64_t K) {
     case Q8_OP_DECOMP: return decomp_ws(M, K).total;
     case Q8_OP_FP8: return fp8_ws(M, K).total;
     case Q8_OP_STATIC: return static_ws(M, K).total;
+    case Q8_OP_GROUPED: return grouped_ws(M, K).total;
   }
   return 0;
 }
@@ -477,6 +493,44 @@ q8_status q8_linear_w8a16(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y}));
   return launched(q8::launch_gemv_w8a16(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, st));
+}
+
+q8_status q8_quantize_weight_grouped(const void* w, q8_dtype w_dtype, int64_t N, int64_t K, int64_t group,
+                                     int8_t* wq, float* w_scale, float* w_zp, void* stream) {
+  if (!valid_dtype(w_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mk(N, K));
+  if (!valid_group(group, K)) return Q8_ERR_BAD_SHAPE;
+  if (!w || !wq || !w_scale || !w_zp) return Q8_ERR_NULL_PTR;
+  if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp)) return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {w, wq, w_scale, w_zp}));
+  return launched(q8::launch_quant_weight_grouped(w, w_dtype, N, K, group, wq, w_scale, w_zp, st));
+}
+
+q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const int8_t* wq,
+                            const float* w_scale, const float* w_zp, int64_t group, int64_t N, const float* bias,
+                            void* y, q8_dtype y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mnk(M, N, K));
+  if (!valid_group(group, K)) return Q8_ERR_BAD_SHAPE;
+  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  const GroupedWs ws = grouped_ws(M, K);
+  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || !aligned16(workspace))
+    return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace}));
+  char* base = static_cast<char*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
+  float* xs = reinterpret_cast<float*>(base + ws.xs);
+  int32_t* gs = reinterpret_cast<int32_t*>(base + ws.gs);
+  Q8_TRY(launched(q8::launch_quant_act_i8_groups(x, x_dtype, M, K, group, xq, xs, gs, st)));
+  if (M <= q8::kGroupGemvMaxM)
+    return launched(q8::launch_gemv_group(xq, xs, gs, M, K, wq, w_scale, w_zp, group, N, bias, y, y_dtype, st));
+  return launched(q8::launch_gemm_group(xq, xs, gs, M, K, wq, w_scale, w_zp, group, N, bias, y, y_dtype, st));
 }
 
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,

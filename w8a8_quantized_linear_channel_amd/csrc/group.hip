@@ -1,0 +1,554 @@
+// Per-group asymmetric INT8 weights ("大模型量化技术概述" §2.2, granularity:
+// groups of 64 to 128 parameters with their own scale and zero point; the
+// lecture notes' granularity passage: per-group blocks).  Group j of row n is
+// columns [j g, (j+1) g) of W; its scale S[j, n] and zero point Z[j, n] are
+// stored group-major.  With per-token activation codes q_x, the layer is
+//     y[m,n] = S_x[m] Sum_j S[j,n] (acc_j[m,n] - Z[j,n] gsum[j,m])  (+ b[n])
+// where acc_j is the exact INT32 product over the group's columns and
+// gsum[j, m] the sum of the activation codes over them.
+//
+//   k_quant_weight_grouped  one workgroup per row; the g/E lanes holding a
+//                           group's 16-byte chunks take its min / max by
+//                           lane shuffles, then every lane codes its chunk
+//   k_gemv_group            decode (M <= 16): the on-codes decode layout
+//                           (16 weight rows per workgroup, 4 waves splitting
+//                           K, DMA of weight and code rows into LDS,
+//                           v_mfma_i32_16x16x64_i8); after each group the
+//                           INT32 tile is corrected by Z gsum exactly and
+//                           added into fp32 with the group's scale
+//   k_gemm_group            M > 16: a 128 x 128 tile of 8 waves (two per
+//                           SIMD, each 64 x 32) on v_mfma_i32_32x32x32_i8,
+//                           with the activations as the first operand so a
+//                           lane's accumulators share one output column and
+//                           one group scale.  Two accumulator sets alternate
+//                           by group: the fold of one group (convert, fma
+//                           with its scale into fp32) is interleaved with the
+//                           MFMAs of the next.  The zero-point term
+//                           -Sum_j S Z gsum is a rank-(K/g) fp32 product,
+//                           computed first with v_mfma_f32_32x32x2_f32 into
+//                           the fp32 accumulators.
+#include "q8_device.hpp"
+#include "q8_group.hpp"
+
+namespace q8 {
+namespace {
+
+// ------------------------------------------------------------------ weights
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_weight_grouped(const void* __restrict__ w, int64_t K, int64_t N,
+                                                              int glanes, int8_t* __restrict__ wq,
+                                                              float* __restrict__ w_scale,
+                                                              float* __restrict__ w_zp) {
+  constexpr int E = Chunk<DT>::kElems;
+  constexpr int esz = DT == DT_F32 ? 4 : 2;
+  const int64_t n = blockIdx.x;
+  const int nch = (int)(K / E);
+  const int64_t row = n * K;
+  // chunk c is in group c / glanes; a group's chunks are glanes consecutive
+  // lanes of one wave, all inside or all outside the row (K is a multiple of
+  // the group size), so every lane of a group runs each iteration
+  for (int c = threadIdx.x; c < nch; c += 256) {
+    const v4i ch = *(const v4i*)((const char*)w + (row + (int64_t)c * E) * esz);
+    float v[E];
+    Chunk<DT>::decode(ch, v);
+    float lo = 0.0f, hi = 0.0f;   // the range always contains 0
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      lo = fminf(lo, v[e]);
+      hi = fmaxf(hi, v[e]);
+    }
+    for (int o = 1; o < glanes; o <<= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    float s = (hi - lo) / 255.0f;
+    s = s < kEps ? kEps : s;
+    const float z = -128.0f - __builtin_rintf(lo / s);
+    uint32_t words[E / 4];
+#pragma unroll
+    for (int g = 0; g < E / 4; ++g) {
+      int q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float t = __builtin_rintf(v[4 * g + e] / s) + z;
+        t = fminf(fmaxf(t, -128.0f), 127.0f);
+        q[e] = (int)t;
+      }
+      words[g] = pack4_i8(q[0], q[1], q[2], q[3]);
+    }
+    if constexpr (E == 8) *(v2i*)(wq + row + (int64_t)c * E) = v2i{(int)words[0], (int)words[1]};
+    else *(uint32_t*)(wq + row + (int64_t)c * E) = words[0];
+    if ((c & (glanes - 1)) == 0) {
+      const int64_t j = c / glanes;
+      w_scale[j * N + n] = s;
+      w_zp[j * N + n] = z;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode
+constexpr int kRows = 16;              // weight rows per workgroup
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSeg = 4096;             // K columns per segment
+constexpr int kKW = kSeg / kWaves;     // columns of a segment per wave
+constexpr int kSteps = kKW / 64;       // 64-column MFMA k-steps per wave per segment
+constexpr int kWPitch = kKW + 16;      // LDS bytes per row of a wave's share (16-byte pad)
+
+template <int YDT, int GS>
+__global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __restrict__ xq,
+                                                            const float* __restrict__ x_scale,
+                                                            const int32_t* __restrict__ gsum, int M, int K,
+                                                            const int8_t* __restrict__ wq,
+                                                            const float* __restrict__ w_scale,
+                                                            const float* __restrict__ w_zp, int N,
+                                                            const float* __restrict__ bias, void* __restrict__ y) {
+  constexpr int SPG = GS / 64;         // k-steps per group
+  constexpr int NG = kKW / GS;         // groups in a wave's share of a segment
+  __shared__ __attribute__((aligned(16))) uint8_t wsm[kWaves][kRows * kWPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t csm[kWaves][kRows * kWPitch];
+  __shared__ v4f part[kWaves][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * kRows;
+  const int G = K / GS;
+  // register r of lane (lr, lg) is D[n = n0 + 4 lg + r][m = lr]
+  const int m = lr;
+  const int mc = m < M ? m : M - 1;
+  int nc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) nc[r] = n0 + 4 * lg + r < N ? n0 + 4 * lg + r : N - 1;
+  uint8_t* const wl = wsm[wave];
+  uint8_t* const cl = csm[wave];
+  const int xr = lr < M ? lr : M - 1;    // code rows past M repeat the last: they feed unstored columns
+  v4f f = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < K; k0 += kSeg) {
+    const int seg = (K - k0) < kSeg ? (K - k0) : kSeg;
+    int c = wave * kKW + 16 * lane;
+    c = c < seg ? c : seg - 16;                          // clamped; its codes are masked below
+    if (k0 > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // this wave's reads of the last segment are done
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int n = n0 + i < N ? n0 + i : N - 1;
+      dma16((const uint8_t*)wq, (uint32_t)(n * K + k0 + c), wl + i * kWPitch);
+    }
+    const int mr = M < kRows ? M : kRows;
+    for (int i = 0; i < mr; ++i) dma16((const uint8_t*)xq, (uint32_t)(i * K + k0 + c), cl + i * kWPitch);
+    // the parameters of the share's groups, issued before the wait below so
+    // they arrive with the DMA (groups past K are clamped and not used)
+    float ps[NG][4], pz[NG][4];
+    int pg[NG];
+    const int g0 = (k0 + wave * kKW) / GS;
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+      const int gi = g0 + t < G ? g0 + t : G - 1;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ps[t][r] = w_scale[gi * N + nc[r]];
+        pz[t][r] = w_zp[gi * N + nc[r]];
+      }
+      pg[t] = gsum[gi * M + mc];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    v4i acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int o = s * 64 + lg * 16;
+      const v4i a = *(const v4i*)(wl + lr * kWPitch + o);
+      v4i b = *(const v4i*)(cl + xr * kWPitch + o);
+      if (seg != kSeg && wave * kKW + s * 64 + lg * 16 >= seg) b = v4i{0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+      if ((s + 1) % SPG == 0) {
+        const int t = s / SPG;
+        if (wave * kKW + t * GS < seg) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int cc = acc[r] - (int)pz[t][r] * pg[t];   // exact: |cc| < 2^24
+            f[r] = fmaf(ps[t][r], (float)cc, f[r]);
+          }
+        }
+        acc = v4i{0, 0, 0, 0};
+      }
+    }
+  }
+  part[wave][lane] = f;
+  __syncthreads();
+  if (wave == 0 && m < M) {
+    v4f t = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += part[w][lane];
+    const float sx = x_scale[m];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + lg * 4 + r;
+      if (n < N) {
+        float v = sx * t[r];
+        if (bias) v += bias[n];
+        store_out<YDT>(y, (size_t)m * N + n, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+namespace gg {
+constexpr int BM = 128, BN = 128;
+constexpr int NW = 8, NT = 64 * NW;             // 8 waves, two per SIMD
+constexpr int WN = 4;                           // wave grid 2 (M) x 4 (N)
+constexpr int TM = 64, TN = 32;                 // wave tile
+constexpr int FM = TM / 32, FN = TN / 32;       // 32 x 32 fragments per wave (2 x 1)
+constexpr int kBK = 64;                         // bytes of K per stage
+constexpr int KS = kBK / 32;                    // k-steps per stage
+constexpr int kStages = 4;
+constexpr int kStageBytes = (BM + BN) * kBK;
+constexpr int kMeta = 256;                      // per wave and stage: 64 lanes x 4 bytes of group scales
+constexpr int LOADS = 3;                        // DMA instructions per wave per stage: A rows, B rows, scales
+constexpr int kRowsPerDma = 16;                 // one 1 KB DMA = 16 rows of 64 bytes
+constexpr int kXcds = 8, kGroupM = 4;
+static_assert(BM * (kBK / 16) == NT && BN * (kBK / 16) == NT, "one A and one B DMA per thread and stage");
+}  // namespace gg
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * gg::kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// v_mfma_i32_32x32x32_i8 operand of lane l: row (base + l % 32), logical
+// 16-byte chunk 2 ks + l / 32 of the row, found at its swizzled position
+__device__ __forceinline__ int lane_off(int lane) { return ((lane >> 5) ^ ((lane >> 2) & 3)) << 4; }
+__device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// global_load_lds_dword: 64 lanes x 4 bytes from gbase + voff into 256 bytes
+// of LDS at `lds` (lane l at lds + 4 l), counted by vmcnt like dma16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const uint8_t* gbase, uint32_t voff, uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// XCD-contiguous renumbering, then kGroupM tile-rows per L2 group
+__device__ __forceinline__ void group_tile_coords(int ntm, int ntn, int& tm, int& tn) {
+  const int T = ntm * ntn;
+  const int b = blockIdx.x;
+  const int q = T / gg::kXcds, r = T % gg::kXcds;
+  const int x = b % gg::kXcds, i = b / gg::kXcds;
+  const int bp = x * q + (x < r ? x : r) + i;
+  const int per_group = gg::kGroupM * ntn;
+  const int group = bp / per_group;
+  const int first_m = group * gg::kGroupM;
+  const int gsize = (ntm - first_m) < gg::kGroupM ? (ntm - first_m) : gg::kGroupM;
+  const int inner = bp - group * per_group;
+  tm = first_m + inner % gsize;
+  tn = inner / gsize;
+}
+
+template <int YDT, int GS>
+__global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restrict__ xq,
+                                                         const float* __restrict__ x_scale,
+                                                         const int32_t* __restrict__ gsum, int M, int K,
+                                                         const int8_t* __restrict__ wq,
+                                                         const float* __restrict__ w_scale,
+                                                         const float* __restrict__ w_zp, int N,
+                                                         const float* __restrict__ bias, void* __restrict__ y) {
+  using namespace gg;
+  constexpr int SPG = GS / kBK;   // stages per group (1 or 2)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t meta[kStages * NW * kMeta];
+  __shared__ float f_sx[BM];
+  uint8_t* const sa0 = smem;
+  uint8_t* const sb0 = smem + BM * kBK;
+  uint8_t* const sa1 = smem + kStageBytes;
+  uint8_t* const sb1 = sa1 + BM * kBK;
+  uint8_t* const sa2 = smem + 2 * kStageBytes;
+  uint8_t* const sb2 = sa2 + BM * kBK;
+  uint8_t* const sa3 = smem + 3 * kStageBytes;
+  uint8_t* const sb3 = sa3 + BM * kBK;
+
+  int tm, tn;
+  group_tile_coords((M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int G = K / GS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave / WN, wn = wave % WN;
+  // the lane's output column (one per lane: the activations are the MFMA's
+  // first operand, so D[m][n] has n = l % 32)
+  const int ncol = n0 + wn * TN + (lane & 31);
+  const int nc = ncol < N ? ncol : N - 1;
+  const float bn = bias ? bias[nc] : 0.0f;
+  if (tid < BM) f_sx[tid] = x_scale[m0 + tid < M ? m0 + tid : M - 1];   // read after the main loop's barriers
+
+  // ---- DMA: lane l lands at row l / 4, physical chunk l % 4 of a 16-row
+  // block, which holds logical chunk (l % 4) ^ ((row >> 2) & 3); rows past M
+  // (or N) re-read the last row and only feed outputs that are not stored.
+  const int lrow = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  int gm = m0 + swave * kRowsPerDma + lrow;
+  gm = gm < M ? gm : M - 1;
+  int gn = n0 + swave * kRowsPerDma + lrow;
+  gn = gn < N ? gn : N - 1;
+  const uint32_t aoff = (uint32_t)(gm * K + lchunk * 16);
+  const uint32_t boff = (uint32_t)(gn * K + lchunk * 16);
+  // group scales: lane l fetches S[j, n0 + wn*32 + l % 32], the column its
+  // accumulators belong to, into this wave's own 256 bytes of the stage
+  const uint32_t moff = (uint32_t)nc * 4u;
+  const uint8_t* const sbase = (const uint8_t*)w_scale;
+  auto meta_at = [&](int s) { return meta + ((s & 3) * NW + swave) * kMeta; };
+  auto dma_one = [&](int k, uint8_t* sa, uint8_t* sb, int s) {
+    if (k == 0) dma16((const uint8_t*)xq + s * kBK, aoff, sa + swave * kRowsPerDma * kBK);
+    else if (k == 1) dma16((const uint8_t*)wq + s * kBK, boff, sb + swave * kRowsPerDma * kBK);
+    else dma4(sbase, moff + (uint32_t)((s / SPG) * N) * 4u, meta_at(s));
+  };
+  auto dma = [&](uint8_t* sa, uint8_t* sb, int s) {
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) dma_one(k, sa, sb, s);
+  };
+  const int nfull = K / kBK;   // K is a multiple of GS, hence of 64
+
+  // ---- zero-point term: f = -Sum_j (S Z)[j, n] gsum[j, m], two groups per
+  // v_mfma_f32_32x32x2_f32 (lane l: A[m = l % 32][k = l / 32], B[k][n = l % 32])
+  v16f f[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) f[i] = v16f{};
+  if (nfull > 0) dma(sa0, sb0, 0);
+  if (nfull > 1) dma(sa1, sb1, 1);
+  if (nfull > 2) dma(sa2, sb2, 2);
+  {
+    int mrow[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int mm = m0 + wm * TM + i * 32 + (lane & 31);
+      mrow[i] = mm < M ? mm : M - 1;
+    }
+    // 32 groups per pass: all their loads are in flight together (and, in
+    // the first pass, together with the DMA of the first stages)
+    constexpr int kPairs = 16;
+    for (int j0 = 0; j0 < G; j0 += 2 * kPairs) {
+      float pa[kPairs][FM], pp[kPairs];
+#pragma unroll
+      for (int u = 0; u < kPairs; ++u) {
+        const int j = j0 + 2 * u + (lane >> 5);
+        const bool in = j < G;
+        const int jc = in ? j : G - 1;
+        const float sv = w_scale[jc * N + nc], zv = w_zp[jc * N + nc];
+        pp[u] = in ? -(sv * zv) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int gv = gsum[jc * M + mrow[i]];
+          pa[u][i] = in ? (float)gv : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPairs; ++u)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) f[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[u][i], pp[u], f[i], 0, 0, 0);
+    }
+  }
+
+  using Acc = v16i;
+  Acc acc[2][FM];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[h][i] = Acc{};
+  float sgrp[2] = {0.0f, 0.0f};   // the scale of the group in each accumulator set
+
+  const int arow = (wm * TM + (lane & 31)) * kBK;
+  const int brow = (wn * TN + (lane & 31)) * kBK;
+  const int loff = lane_off(lane);
+  v4i fa[2][FM], fb[2][FN];
+  auto load_frag = [&](auto SET, int fi, const uint8_t* As, const uint8_t* Bs, int ks) {
+    constexpr int st = decltype(SET)::value;
+    if (fi < FM) fa[st][fi] = *(const v4i*)(As + arow + fi * 32 * kBK + (loff ^ (ks << 5)));
+    else fb[st][fi - FM] = *(const v4i*)(Bs + brow + (fi - FM) * 32 * kBK + (loff ^ (ks << 5)));
+  };
+  auto load_frags = [&](auto SET, const uint8_t* As, const uint8_t* Bs, int ks) {
+#pragma unroll
+    for (int fi = 0; fi < FM + FN; ++fi) load_frag(SET, fi, As, Bs, ks);
+  };
+  // fold part q (0 .. 2 FM - 1) of accumulator set H: 8 elements of fragment q / 2
+  auto fold = [&](auto HC, int q) {
+    constexpr int H = decltype(HC)::value;
+    const int i = q >> 1, r0 = (q & 1) * 8;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) f[i][r0 + r] = fmaf(sgrp[H], (float)acc[H][i][r0 + r], f[i][r0 + r]);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  // One k-step's MFMAs on fragment set CUR into accumulator set H, with the
+  // LDS reads of the next fragments (pf), DMA instructions of a later stage
+  // (dm) and fold parts of the other accumulator set (fl) spread between
+  // them; ZERO: the group's first k-step, whose MFMAs start from 0.
+  auto step = [&](auto CUR, auto NXT, auto HC, auto ZERO, bool fl, int fq, bool pf, bool dm, const uint8_t* xa,
+                  const uint8_t* xb, int xks, uint8_t* da, uint8_t* db, int ds) {
+    constexpr int cs = decltype(CUR)::value;
+    constexpr int H = decltype(HC)::value;
+    constexpr int NM = FM * FN, NF = FM + FN, NL = LOADS;
+#pragma unroll
+    for (int t = 0; t < NM; ++t) {
+      const int i = t / FN, jj = t % FN;
+      acc[H][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cs][i], fb[cs][jj], decltype(ZERO)::value ? Acc{} : acc[H][i],
+                                                        0, 0, 0);
+      if (fl) {
+        using O = std::integral_constant<int, H ^ 1>;
+        fold(O{}, fq + t);
+      }
+      if (pf) {
+#pragma unroll
+        for (int fi = (t * NF + NM - 1) / NM; fi < ((t + 1) * NF + NM - 1) / NM; ++fi) load_frag(NXT, fi, xa, xb, xks);
+      }
+      if (dm) {
+#pragma unroll
+        for (int k = (t * NL + NM - 1) / NM; k < ((t + 1) * NL + NM - 1) / NM; ++k) dma_one(k, da, db, ds);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto wait_stage = [&](int s, bool steady) {
+    const int later = steady || (nfull - 1 - s) >= 2 ? 2 : nfull - 1 - s;
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // One stage (KS = 2 k-steps) whose first k-step's fragments are in register
+  // set 0 (KS is even, so every stage starts in set 0).  HC: accumulator set
+  // of the stage's group; FIRST: the stage opens its group (its MFMAs start
+  // from 0, it reads the group's scale, and it folds the other set, which
+  // holds the previous group).
+  auto stage = [&](auto STEADY, auto HC, auto FIRST, int s, uint8_t* ca, uint8_t* cb, const uint8_t* xa,
+                   const uint8_t* xb) {
+    constexpr int H = decltype(HC)::value;
+    constexpr bool first = decltype(FIRST)::value;
+    constexpr bool steady = decltype(STEADY)::value;
+    if (first) sgrp[H] = *(const float*)(meta_at(s) + 4 * (lane & 31));
+    using Z = std::integral_constant<bool, first>;
+    step(S0{}, S1{}, HC, Z{}, first, 0, true, false, ca, cb, 1, ca, cb, 0);
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+    const bool nxt = steady || s + 1 < nfull;
+    const bool ahead = steady || s + 4 < nfull;
+    if (nxt) wait_stage(s + 1, steady);
+    step(S1{}, S0{}, HC, F{}, first, FM * FN, nxt, ahead, xa, xb, 0, ca, cb, s + 4);
+  };
+  // accumulator set and group opening of stage offset o in a 4-stage block
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, (1 / SPG) & 1>;
+  using H2 = std::integral_constant<int, (2 / SPG) & 1>;
+  using H3 = std::integral_constant<int, (3 / SPG) & 1>;
+  using F1 = std::integral_constant<bool, 1 % SPG == 0>;
+  using F3 = std::integral_constant<bool, 3 % SPG == 0>;
+  static_assert(FM * FN * KS * 2 >= 2 * FM, "fold parts fit the stage's MFMA slots");
+
+  if (nfull > 0) {
+    wait_stage(0, false);
+    if (nfull > 3) dma(sa3, sb3, 3);
+    load_frags(S0{}, sa0, sb0, 0);
+  }
+  int kt = 0;
+  for (; kt + 8 <= nfull; kt += 4) {
+    stage(T{}, H0{}, T{}, kt, sa0, sb0, sa1, sb1);
+    stage(T{}, H1{}, F1{}, kt + 1, sa1, sb1, sa2, sb2);
+    stage(T{}, H2{}, T{}, kt + 2, sa2, sb2, sa3, sb3);
+    stage(T{}, H3{}, F3{}, kt + 3, sa3, sb3, sa0, sb0);
+  }
+  if (kt + 4 <= nfull) {
+    stage(F{}, H0{}, T{}, kt, sa0, sb0, sa1, sb1);
+    stage(F{}, H1{}, F1{}, kt + 1, sa1, sb1, sa2, sb2);
+    stage(F{}, H2{}, T{}, kt + 2, sa2, sb2, sa3, sb3);
+    stage(F{}, H3{}, F3{}, kt + 3, sa3, sb3, sa0, sb0);
+    kt += 4;
+  }
+  if (kt < nfull) stage(F{}, H0{}, T{}, kt, sa0, sb0, sa1, sb1);
+  if (kt + 1 < nfull) stage(F{}, H1{}, F1{}, kt + 1, sa1, sb1, sa2, sb2);
+  if (kt + 2 < nfull) stage(F{}, H2{}, T{}, kt + 2, sa2, sb2, sa3, sb3);
+  // the last group's fold
+  if (((nfull / SPG - 1) & 1) == 0) {
+#pragma unroll
+    for (int q = 0; q < 2 * FM; ++q) fold(H0{}, q);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2 * FM; ++q) fold(S1{}, q);
+  }
+
+  // ---- epilogue: y = S_x[m] f (+ b[n]); lanes 0-31 and 32-63 each store 32
+  // consecutive outputs of one row
+  if (ncol < N) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = wm * TM + i * 32 + out_row(r, lane), m = m0 + ml;
+        if (m < M) {
+          float v = f_sx[ml] * f[i][r];
+          if (bias) v += bn;
+          store_out<YDT>(y, (size_t)m * N + ncol, v);
+        }
+      }
+  }
+}
+
+template <int GS>
+hipError_t gemv_gs(const int8_t* xq, const float* xs, const int32_t* gs, int64_t M, int64_t K, const int8_t* wq,
+                   const float* ws, const float* wz, int64_t N, const float* bias, void* y, int ydt, hipStream_t st) {
+  dim3 grid((unsigned)((N + kRows - 1) / kRows)), block(kThreads);
+  const int m = (int)M, k = (int)K, n = (int)N;
+  switch (ydt) {
+    case DT_F32: k_gemv_group<DT_F32, GS><<<grid, block, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+    case DT_F16: k_gemv_group<DT_F16, GS><<<grid, block, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+    default: k_gemv_group<DT_BF16, GS><<<grid, block, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+  }
+  return hipGetLastError();
+}
+
+template <int GS>
+hipError_t gemm_gs(const int8_t* xq, const float* xs, const int32_t* gs, int64_t M, int64_t K, const int8_t* wq,
+                   const float* ws, const float* wz, int64_t N, const float* bias, void* y, int ydt, hipStream_t st) {
+  const unsigned tiles = (unsigned)(((M + gg::BM - 1) / gg::BM) * ((N + gg::BN - 1) / gg::BN));
+  const int m = (int)M, k = (int)K, n = (int)N;
+  switch (ydt) {
+    case DT_F32: k_gemm_group<DT_F32, GS><<<tiles, gg::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+    case DT_F16: k_gemm_group<DT_F16, GS><<<tiles, gg::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+    default: k_gemm_group<DT_BF16, GS><<<tiles, gg::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_weight_grouped(const void* w, int dt, int64_t N, int64_t K, int64_t group, int8_t* wq,
+                                       float* w_scale, float* w_zp, hipStream_t st) {
+  dim3 grid((unsigned)N), block(256);
+  switch (dt) {
+    case DT_F32:
+      k_quant_weight_grouped<DT_F32><<<grid, block, 0, st>>>(w, K, N, (int)(group / 4), wq, w_scale, w_zp);
+      break;
+    case DT_F16:
+      k_quant_weight_grouped<DT_F16><<<grid, block, 0, st>>>(w, K, N, (int)(group / 8), wq, w_scale, w_zp);
+      break;
+    default:
+      k_quant_weight_grouped<DT_BF16><<<grid, block, 0, st>>>(w, K, N, (int)(group / 8), wq, w_scale, w_zp);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_group(const int8_t* xq, const float* x_scale, const int32_t* gsum, int64_t M, int64_t K,
+                             const int8_t* wq, const float* w_scale, const float* w_zp, int64_t group, int64_t N,
+                             const float* bias, void* y, int ydt, hipStream_t st) {
+  if (group == 64) return gemv_gs<64>(xq, x_scale, gsum, M, K, wq, w_scale, w_zp, N, bias, y, ydt, st);
+  return gemv_gs<128>(xq, x_scale, gsum, M, K, wq, w_scale, w_zp, N, bias, y, ydt, st);
+}
+
+hipError_t launch_gemm_group(const int8_t* xq, const float* x_scale, const int32_t* gsum, int64_t M, int64_t K,
+                             const int8_t* wq, const float* w_scale, const float* w_zp, int64_t group, int64_t N,
+                             const float* bias, void* y, int ydt, hipStream_t st) {
+  if (group == 64) return gemm_gs<64>(xq, x_scale, gsum, M, K, wq, w_scale, w_zp, N, bias, y, ydt, st);
+  return gemm_gs<128>(xq, x_scale, gsum, M, K, wq, w_scale, w_zp, N, bias, y, ydt, st);
+}
+
+}  // namespace q8

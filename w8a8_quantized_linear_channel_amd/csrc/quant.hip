@@ -117,6 +117,7 @@ enum RowMode : int {
   RM_I8_OUTLIER = 1, // as RM_I8 (fp16 only) with the flagged outlier columns read as 0
   RM_FP8 = 2,        // e4m3, S = min(absmax, bound) / 448
   RM_I8_STATIC = 3,  // INT8 symmetric with a given scale S = bound, codes clamped to +-127
+  RM_I8_GROUPS = 4,  // as RM_I8, plus the code sum of every group of glanes consecutive chunks
 };
 constexpr int kRowCache = 8;   // chunks per thread held in registers: 16-bit rows up to 16384 values
 
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
     const void* __restrict__ x, int64_t R, int64_t K, const uint8_t* __restrict__ flags, float bound,
     uint8_t* __restrict__ xq, float* __restrict__ x_scale, int32_t* __restrict__ x_rowsum,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int32_t* __restrict__ user_idx,
-    int32_t* __restrict__ user_cnt) {
+    int32_t* __restrict__ user_cnt, int32_t* __restrict__ gsum, int glanes) {
   constexpr int E = Chunk<DT>::kElems;
   __shared__ float redf[kWaves];
   __shared__ int redi[kWaves];
@@ -283,6 +284,16 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
       }
     }
     store_codes<E>(xq, row + (int64_t)c * E, words);
+    if constexpr (MODE == RM_I8_GROUPS) {
+      // chunk c belongs to group c / glanes; its glanes chunks sit in glanes
+      // consecutive lanes of one wave (chunk c is thread c % 256), all active
+      // together since K is a multiple of the group size
+      int cs = 0;
+#pragma unroll
+      for (int g = 0; g < E / 4; ++g) cs = sum_i8x4(words[g], cs);
+      for (int o = 1; o < glanes; o <<= 1) cs += __shfl_xor(cs, o, 64);
+      if ((c & (glanes - 1)) == 0) gsum[(int64_t)(c / glanes) * R + m] = cs;
+    }
   };
 #pragma unroll
   for (int j = 0; j < kRowCache; ++j) {
@@ -300,19 +311,19 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
 template <int MODE>
 void launch_rows(const void* x, int dt, int64_t R, int64_t K, const uint8_t* flags, float bound, uint8_t* xq,
                  float* x_scale, int32_t* x_rowsum, int32_t* idx, int32_t* cnt, int32_t* user_idx,
-                 int32_t* user_cnt, unsigned grid, hipStream_t st) {
+                 int32_t* user_cnt, unsigned grid, hipStream_t st, int32_t* gsum = nullptr, int glanes = 0) {
   switch (dt) {
     case DT_F32:
       k_quant_rows<MODE, DT_F32><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                            cnt, user_idx, user_cnt);
+                                                            cnt, user_idx, user_cnt, gsum, glanes);
       break;
     case DT_F16:
       k_quant_rows<MODE, DT_F16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                            cnt, user_idx, user_cnt);
+                                                            cnt, user_idx, user_cnt, gsum, glanes);
       break;
     default:
       k_quant_rows<MODE, DT_BF16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                             cnt, user_idx, user_cnt);
+                                                             cnt, user_idx, user_cnt, gsum, glanes);
       break;
   }
 }
@@ -351,13 +362,21 @@ hipError_t launch_quant_act_i8_static(const void* x, int dt, int64_t M, int64_t 
   return hipGetLastError();
 }
 
+hipError_t launch_quant_act_i8_groups(const void* x, int dt, int64_t M, int64_t K, int64_t group, int8_t* xq,
+                                      float* x_scale, int32_t* gsum, hipStream_t st) {
+  const int elems = dt == DT_F32 ? 4 : 8;   // values per 16-byte chunk
+  launch_rows<RM_I8_GROUPS>(x, dt, M, K, nullptr, 0.0f, (uint8_t*)xq, x_scale, nullptr, nullptr, nullptr, nullptr,
+                            nullptr, (unsigned)M, st, gsum, (int)(group / elems));
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act_f16_outliers(const uint16_t* x, int64_t M, int64_t K, const uint8_t* flags,
                                          int8_t* xq, float* x_scale, int32_t* x_rowsum, int32_t* idx,
                                          int32_t* cnt, int32_t* user_idx, int32_t* user_cnt,
                                          hipStream_t st) {
   // one workgroup per row, plus the compaction workgroup
   k_quant_rows<RM_I8_OUTLIER, DT_F16><<<(unsigned)(M + 1), kThreads, 0, st>>>(
-      x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt);
+      x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@ from . import _lib
 _DT = {torch.float32: _lib.Q8_F32, torch.float16: _lib.Q8_F16, torch.bfloat16: _lib.Q8_BF16}
 _FMT = {"int8_asym": _lib.Q8_INT8_ASYM, "int8_sym": _lib.Q8_INT8_SYM, "fp8_e4m3": _lib.Q8_FP8_E4M3}
 _OP = {"linear": _lib.Q8_OP_LINEAR, "decomp": _lib.Q8_OP_DECOMP, "fp8": _lib.Q8_OP_FP8,
-       "static": _lib.Q8_OP_STATIC}
+       "static": _lib.Q8_OP_STATIC, "grouped": _lib.Q8_OP_GROUPED}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -306,4 +306,47 @@ def q8_linear_fp8_grouped(x: torch.Tensor, expert_offsets: torch.Tensor, wq: tor
     st = _lib.lib().q8_linear_fp8_grouped(_ptr(x), T, K, _ptr(expert_offsets), E, _ptr(wq), _ptr(w_scale), N,
                                           float(scale_ub), _ptr(y), _ptr(ws), ws.numel(), _stream(dev))
     _lib.check("q8_linear_fp8_grouped", st)
+    return y
+
+
+def q8_quantize_weight_grouped(w: torch.Tensor, group: int = 128):
+    """Per-group asymmetric INT8 weights: returns (wq int8 [N, K], w_scale float32
+    [K/group, N], w_zp float32 [K/group, N]), the parameters group-major."""
+    dev = w.device
+    N, K = w.shape
+    if w.dtype not in _DT:
+        raise TypeError(f"q8_quantize_weight_grouped: unsupported dtype {w.dtype}")
+    _need(w, "w", w.dtype, (N, K), dev)
+    G = K // group if group > 0 else 0
+    wq = torch.empty(N, K, dtype=torch.int8, device=dev)
+    ws = torch.empty(max(G, 1), N, dtype=torch.float32, device=dev)
+    wz = torch.empty(max(G, 1), N, dtype=torch.float32, device=dev)
+    st = _lib.lib().q8_quantize_weight_grouped(_ptr(w), _DT[w.dtype], N, K, group, _ptr(wq), _ptr(ws), _ptr(wz),
+                                               _stream(dev))
+    _lib.check("q8_quantize_weight_grouped", st)
+    return wq, ws, wz
+
+
+def q8_linear_grouped(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, w_zp: torch.Tensor,
+                      group: int = 128, bias: Optional[torch.Tensor] = None,
+                      out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """W8A8 linear with per-group weights (from q8_quantize_weight_grouped with the
+    same group) and dynamic per-token INT8 activations."""
+    dev = x.device
+    M, K = x.shape
+    N = wq.shape[0]
+    G = K // group if group > 0 else 0
+    _need(x, "x", x.dtype, (M, K), dev)
+    _need(wq, "wq", torch.int8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (G, N), dev)
+    _need(w_zp, "w_zp", torch.float32, (G, N), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=dev)
+    _need(y, "y", out_dtype, (M, N), dev)
+    ws = workspace if workspace is not None else _workspace("grouped", M, N, K, dev)
+    st = _lib.lib().q8_linear_grouped(_ptr(x), _DT[x.dtype], M, K, _ptr(wq), _ptr(w_scale), _ptr(w_zp), group, N,
+                                      _ptr(bias), _ptr(y), _DT[out_dtype], _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check("q8_linear_grouped", st)
     return y
