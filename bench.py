@@ -172,22 +172,29 @@ def bench_prefill(dev, steps, warmup):
 
 
 # ------------------------------------------------------------------ decode
-def bench_decode(dev, M, replays, copies=32, weight_only=False):
+def bench_decode(dev, M, replays, copies=32, mode="w8a8", group=128):
+    """Decode q_proj calls in graph replay over `copies` weight sets (beyond
+    the caches).  mode: "w8a8" (q8_linear), "w8a16" (q8_linear_w8a16) or
+    "grouped" (q8_linear_grouped with per-group weights)."""
     wl = inputs.decode_qproj(M=16)
     N, K = wl.w.shape
     x = wl.x[:M].contiguous().to(dev)
     weights = []
     for c in range(copies):
-        w = wl.w if c == 0 else inputs.decode_weight_copy(c, N, K)
-        weights.append(q8.q8_quantize_weight(w.to(dev), "int8_asym"))
+        w = (wl.w if c == 0 else inputs.decode_weight_copy(c, N, K)).to(dev)
+        weights.append(q8.q8_quantize_weight_grouped(w, group) if mode == "grouped"
+                       else q8.q8_quantize_weight(w, "int8_asym"))
     ys = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
-    wsp = torch.empty(max(1, q8.q8_workspace_bytes("linear", M, N, K)), dtype=torch.uint8, device=dev)
+    op = "grouped" if mode == "grouped" else "linear"
+    wsp = torch.empty(max(1, q8.q8_workspace_bytes(op, M, N, K)), dtype=torch.uint8, device=dev)
 
     def one_pass():
         for c in range(copies):
             wq, wsc, wz = weights[c]
-            if weight_only:
+            if mode == "w8a16":
                 q8.q8_linear_w8a16(x, wq, wsc, wz, out_dtype=torch.bfloat16, out=ys[c])
+            elif mode == "grouped":
+                q8.q8_linear_grouped(x, wq, wsc, wz, group, out_dtype=torch.bfloat16, out=ys[c], workspace=wsp)
             else:
                 q8.q8_linear(x, wq, wsc, wz, out_dtype=torch.bfloat16, out=ys[c], workspace=wsp)
 
@@ -208,7 +215,8 @@ def bench_decode(dev, M, replays, copies=32, weight_only=False):
     t1.record()
     torch.cuda.synchronize()
     per_call_us = t0.elapsed_time(t1) * 1e3 / (replays * copies)
-    nbytes = N * K + 8 * N + M * K * 2 + M * N * 2
+    params = 8 * N * (K // group) if mode == "grouped" else 8 * N
+    nbytes = N * K + params + M * K * 2 + M * N * 2
     return {
         "M": M, "N": N, "K": K,
         "us_per_call": per_call_us,
@@ -317,6 +325,25 @@ def bench_static(dev, steps, warmup):
     return {"ms_per_step": ms, "tops": ops / (ms * 1e-3) / 1e12}
 
 
+def bench_grouped(dev, steps, warmup, group=128):
+    """Prefill FFN-up shape with per-group weights: q8_linear_grouped (row
+    quantizer with group code sums + grouped GEMM)."""
+    wl = inputs.prefill_ffn_up()
+    M, K = wl.x.shape
+    N = wl.w.shape[0]
+    x = wl.x.to(dev)
+    wq, ws, wz = q8.q8_quantize_weight_grouped(wl.w.to(dev), group)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    wsp = torch.empty(q8.q8_workspace_bytes("grouped", M, N, K), dtype=torch.uint8, device=dev)
+
+    def step(i, pair):
+        q8.q8_linear_grouped(x, wq, ws, wz, group, out=y, workspace=wsp)
+
+    ms, _, _ = timed_steps(step, steps, warmup, None)
+    ops = 2.0 * M * N * K
+    return {"ms_per_step": ms, "tops": ops / (ms * 1e-3) / 1e12}
+
+
 # ------------------------------------------------------------------ measured ceilings
 def bench_ceilings(dev, steps):
     """What this machine reaches with plain device copies and with the vendor
@@ -394,7 +421,7 @@ def main():
                     help="minimum warm-up steps per leg (each leg also warms up for %g ms)" % WARM_MS)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "grouped", "copy"], default=None,
                     help="run one workload (for profiling); 'copy' runs a plain 256 MiB device copy, "
                          "the known-size kernel that scales the HBM byte counters")
     ap.add_argument("--warm-ms", type=float, default=WARM_MS,
@@ -452,7 +479,7 @@ def main():
                          **dec}
         wo = {}
         for M in (16, 1):
-            d = bench_decode(dev, M, replays=max(4, args.steps // 4), weight_only=True)
+            d = bench_decode(dev, M, replays=max(4, args.steps // 4), mode="w8a16")
             wo[f"M{M}"] = {"us_per_call": round(d["us_per_call"], 3), "GB/s": round(d["gbs"], 1),
                            "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS,
                                         "unit": "GB/s", "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
@@ -485,6 +512,21 @@ def main():
                                   "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
                                   "frac_of_int8_peak": round(d["tops"] / PEAK_INT8_TOPS, 4)}
         out["ceilings"] = bench_ceilings(dev, args.steps)
+    if args.only in (None, "grouped"):
+        d = bench_grouped(dev, args.steps, args.warmup)
+        out["grouped_prefill"] = {"workload": "prefill FFN-up 2048x14336x4096, per-group weights (group 128), "
+                                              "q8_linear_grouped: row quantizer with group code sums + grouped GEMM",
+                                  "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
+                                  "frac_of_int8_peak": round(d["tops"] / PEAK_INT8_TOPS, 4)}
+        gd = {}
+        for M in (16, 1):
+            d = bench_decode(dev, M, replays=max(4, args.steps // 4), mode="grouped")
+            gd[f"M{M}"] = {"us_per_call": round(d["us_per_call"], 3), "GB/s": round(d["gbs"], 1),
+                           "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS,
+                                        "unit": "GB/s", "frac": round(d["gbs"] / PEAK_HBM_GBS, 4),
+                                        "bytes_per_call": d["bytes_per_call"]}}
+        out["grouped_decode"] = {"workload": "q8_linear_grouped decode q_proj, N = K = 4096, group 128, bf16, "
+                                             "32 rotating weight sets", **gd}
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(*pf["host_inputs"], args.cpu_seconds)
     print(json.dumps(out), flush=True)

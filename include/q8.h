@@ -302,9 +302,10 @@ q8_status q8_quantize_weight_grouped(const void* w, q8_dtype w_dtype, int64_t N,
  *     y[m,n]   = S_x[m] sum_j S[j,n] C_j[m,n]  (+ bias[n])                    (fp32)
  * x: [M, K] of x_dtype; wq/w_scale/w_zp from q8_quantize_weight_grouped with
  * the same group; bias: float [N] or NULL; y: [M, N] of y_dtype.  workspace:
- * q8_workspace_bytes(Q8_OP_GROUPED, M, N, K) bytes (codes, scales and group
- * code sums, sized for group 64).  Errors: Q8_ERR_BAD_SHAPE for a group other
- * than 64 or 128 or a K that is not a multiple of it.
+ * q8_workspace_bytes(Q8_OP_GROUPED, M, N, K) bytes: none up to 10 tokens
+ * (the quantization is fused into the decode kernel), else codes, scales and
+ * group code sums, sized for group 64.  Errors: Q8_ERR_BAD_SHAPE for a group
+ * other than 64 or 128 or a K that is not a multiple of it.
  */
 q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
                             const int8_t* wq, const float* w_scale, const float* w_zp,

@@ -69,7 +69,8 @@ def test_workspace_sizes():
     assert ws(_lib.Q8_OP_STATIC, 1, 4096, 4096) == 4096 + 2 * 256
     assert ws(_lib.Q8_OP_STATIC, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192
     # per-group path: codes, scales and group code sums sized for groups of 64
-    assert ws(_lib.Q8_OP_GROUPED, 1, 4096, 4096) == 4096 + 256 + 256
+    assert ws(_lib.Q8_OP_GROUPED, 10, 4096, 4096) == 0        # fused decode
+    assert ws(_lib.Q8_OP_GROUPED, 11, 4096, 4096) == 11 * 4096 + 256 + 11 * 64 * 4
     assert ws(_lib.Q8_OP_GROUPED, 2048, 14336, 4096) == 2048 * 4096 + 8192 + 2048 * 64 * 4
     # invalid shapes give 0
     assert ws(_lib.Q8_OP_LINEAR, 0, 16, 16) == 0
@@ -244,6 +245,6 @@ def test_grouped_validation():
     assert call(xd=9) == 3
     assert call(wz=None) == 1
     assert call(w=None) == 7
-    assert call(M=1, wb=100) == 7            # the grouped path always needs its workspace
+    assert call(M=11, wb=100) == 7           # above the fused decode path the workspace is needed
     assert call(y=MIS) == 6
     assert call(ws=MIS) == 6

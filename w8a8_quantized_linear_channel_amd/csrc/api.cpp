@@ -99,11 +99,12 @@ LinearWs linear_ws(int64_t M, int64_t K) {
 }
 
 // Per-group path: codes, scales and the group code sums [K / group, M], sized
-// for the smallest group (64).
+// for the smallest group (64); none for the fused decode path.
 struct GroupedWs { size_t xq, xs, gs, total; };
 GroupedWs grouped_ws(int64_t M, int64_t K) {
+  GroupedWs w{0, 0, 0, 0};
+  if (M <= q8::kGemvFusedMaxM) return w;
   Carve c;
-  GroupedWs w;
   w.xq = c.take((size_t)M * K);
   w.xs = c.take((size_t)M * 4);
   w.gs = c.take((size_t)M * (K / 64) * 4);
@@ -516,13 +517,15 @@ q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t 
   if (!valid_group(group, K)) return Q8_ERR_BAD_SHAPE;
   if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
   const GroupedWs ws = grouped_ws(M, K);
-  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
-      (bias && !aligned16(bias)) || !aligned16(workspace))
+      (bias && !aligned16(bias)) || (ws.total > 0 && !aligned16(workspace)))
     return Q8_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace}));
+  if (M <= q8::kGemvFusedMaxM)
+    return launched(q8::launch_gemv_i8_grouped(x, x_dtype, M, K, wq, w_scale, w_zp, group, N, bias, y, y_dtype, st));
   char* base = static_cast<char*>(workspace);
   int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
   float* xs = reinterpret_cast<float*>(base + ws.xs);

@@ -28,6 +28,7 @@
 // nothing.  Code rows m >= M hold stale bytes: they only feed MFMA output
 // columns that are not stored.
 #include "q8_device.hpp"
+#include "q8_group.hpp"
 #include "q8_kernels.hpp"
 
 namespace q8 {
@@ -46,8 +47,13 @@ constexpr int kArea = 2 * kKW + 16;
 
 
 // ONE: K <= 4096, a single segment (the host picks the instantiation, so each
-// kernel has one straight path and the compiler's wait insertion sees it alone)
-template <int DT, int YDT, bool ONE>
+// kernel has one straight path and the compiler's wait insertion sees it alone).
+// GS > 0: per-group weights (groups of GS columns; w_scale / w_zp are
+// group-major [K / GS, N]).  Each k-step also runs an MFMA of all-ones
+// weights against the codes, which gives sum_k q_x over the step in the
+// accumulator's own layout; after each group the INT32 tile is corrected by
+// Z times that sum, exactly, and added into fp32 with the group's scale.
+template <int DT, int YDT, bool ONE, int GS = 0>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict__ x, int M, int K,
                                                          const int8_t* __restrict__ wq,
                                                          const float* __restrict__ w_scale,
@@ -157,6 +163,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   auto add_int = [](int a, int b) { return a + b; };
   auto row_scale = [&](int m) { return rscale[m]; };
   v4i acc = {0, 0, 0, 0};
+  // per-group weights: the group code sums and the fp32 sum over groups
+  v4i accs = {0, 0, 0, 0};
+  v4f fsum = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int NG = GS > 0 ? kKW / GS : 1;   // groups in a wave's share of a segment
+  float gsc[NG][4], gzp[NG][4];
+  // the parameters of this wave's groups in segment k0 (groups past K are
+  // clamped and their fold is skipped)
+  auto load_groups = [&](int k0) {
+    if constexpr (GS > 0) {
+      const int G = K / GS, g0 = (k0 + wave * kKW) / GS;
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        const int gi = g0 + t < G ? g0 + t : G - 1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + 4 * lg + r;
+          const int nc = n < N ? n : N - 1;
+          gsc[t][r] = w_scale[gi * N + nc];
+          gzp[t][r] = w_zp[gi * N + nc];
+        }
+      }
+    }
+  };
 
   // ---- pass 1 over one segment: per-row partial absmax
   auto pass1 = [&](int sg, int k0, int seg) {
@@ -172,7 +201,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     }
     // issued after the wait, so X does not wait for them; they have the
     // whole coding and MFMA phase to arrive
-    if (sg == 0 && wave == 0) load_factors();
+    if constexpr (GS > 0) {
+      if (sg == 0 && wave == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + 4 * lg + r;
+          fbi[r] = bias ? bias[n < N ? n : N - 1] : 0.0f;
+        }
+      }
+      if (sg == 0) load_groups(k0);
+    } else {
+      if (sg == 0 && wave == 0) load_factors();
+    }
 #pragma unroll 4
     for (int m = 0; m < M; ++m) {
       float v[16];
@@ -237,10 +277,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
       *(v2i*)(area + 512 + 8 * lane) = v2i{(int)words[2], (int)words[3]};
       ((int*)lred[m])[tid] = sg == 0 ? q : ((int*)lred[m])[tid] + q;
     }
+    if constexpr (GS == 0) {
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const v4i xv = *(const v4i*)(xw + lr * kArea + s * 64 + lg * 16);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[s], xv, acc, 0, 0, 0);
+      for (int s = 0; s < kSteps; ++s) {
+        const v4i xv = *(const v4i*)(xw + lr * kArea + s * 64 + lg * 16);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[s], xv, acc, 0, 0, 0);
+      }
+    } else {
+      if (sg > 0) load_groups(k0);   // pass 1 loaded segment 0's groups
+      const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const v4i xv = *(const v4i*)(xw + lr * kArea + s * 64 + lg * 16);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[s], xv, acc, 0, 0, 0);
+        accs = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, xv, accs, 0, 0, 0);
+        if ((s + 1) % (GS / 64) == 0) {
+          const int t = s / (GS / 64);
+          if (wave * kKW + t * GS < seg) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int c = acc[r] - (int)gzp[t][r] * accs[r];   // exact: |c| < 2^24
+              fsum[r] = fmaf(gsc[t][r], (float)c, fsum[r]);
+            }
+          }
+          acc = v4i{0, 0, 0, 0};
+          accs = v4i{0, 0, 0, 0};
+        }
+      }
     }
   };
 
@@ -255,6 +318,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     for (int sg = 0; sg < nseg; ++sg) pass2(sg, sg * kSeg, seg_len(sg), true);
   }
 
+  if constexpr (GS > 0) {
+    // the four fp32 partial tiles meet in LDS; wave 0 scales by S_x
+    part[wave][lane] = __builtin_bit_cast(v4i, fsum);
+    __syncthreads();
+    if (wave == 0) {
+      v4f t = __builtin_bit_cast(v4f, part[0][lane]);
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) t += __builtin_bit_cast(v4f, part[w][lane]);
+      const int m = lr;
+      if (m < M) {
+        const float s_m = row_scale(m);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + lg * 4 + r;
+          if (n < N) {
+            float v = s_m * t[r];
+            if (bias) v += fbi[r];
+            store_out<YDT>(y, (size_t)m * N + n, v);
+          }
+        }
+      }
+    }
+    return;
+  }
   // ---- partial tiles and code sums meet in LDS; wave 0 applies the epilogue
   part[wave][lane] = acc;
   __syncthreads();
@@ -429,6 +516,41 @@ hipError_t launch_gemv_q8(const int8_t* xq, const float* x_scale, const int32_t*
   }
 #undef Q8_GEMV_Q8
   return hipGetLastError();
+}
+
+template <int DT, int GS>
+hipError_t launch_grouped_dt(const void* x, int64_t M, int64_t K, const int8_t* wq, const float* ws,
+                             const float* wz, int64_t N, const float* bias, void* y, int ydt, hipStream_t st) {
+  dim3 grid((unsigned)((N + kRows - 1) / kRows)), block(kThreads);
+  const int m = (int)M, k = (int)K, n = (int)N;
+  const bool one = K <= kSeg;
+#define Q8_GEMV_G(YT)                                                                                          \
+  (one ? (k_gemv_i8<DT, YT, true, GS><<<grid, block, 0, st>>>(x, m, k, wq, ws, wz, n, bias, y, nullptr))       \
+       : (k_gemv_i8<DT, YT, false, GS><<<grid, block, 0, st>>>(x, m, k, wq, ws, wz, n, bias, y, nullptr)))
+  switch (ydt) {
+    case DT_F32: Q8_GEMV_G(DT_F32); break;
+    case DT_F16: Q8_GEMV_G(DT_F16); break;
+    default: Q8_GEMV_G(DT_BF16); break;
+  }
+#undef Q8_GEMV_G
+  return hipGetLastError();
+}
+
+template <int GS>
+hipError_t launch_grouped_gs(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq, const float* ws,
+                             const float* wz, int64_t N, const float* bias, void* y, int ydt, hipStream_t st) {
+  switch (xdt) {
+    case DT_F32: return launch_grouped_dt<DT_F32, GS>(x, M, K, wq, ws, wz, N, bias, y, ydt, st);
+    case DT_F16: return launch_grouped_dt<DT_F16, GS>(x, M, K, wq, ws, wz, N, bias, y, ydt, st);
+    default: return launch_grouped_dt<DT_BF16, GS>(x, M, K, wq, ws, wz, N, bias, y, ydt, st);
+  }
+}
+
+hipError_t launch_gemv_i8_grouped(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq,
+                                  const float* w_scale, const float* w_zp, int64_t group, int64_t N,
+                                  const float* bias, void* y, int ydt, hipStream_t st) {
+  if (group == 64) return launch_grouped_gs<64>(x, xdt, M, K, wq, w_scale, w_zp, N, bias, y, ydt, st);
+  return launch_grouped_gs<128>(x, xdt, M, K, wq, w_scale, w_zp, N, bias, y, ydt, st);
 }
 
 hipError_t launch_gemv_i8(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq,

@@ -12,6 +12,11 @@ namespace q8 {
 // group.hip
 hipError_t launch_quant_weight_grouped(const void* w, int dt, int64_t N, int64_t K, int64_t group, int8_t* wq,
                                        float* w_scale, float* w_zp, hipStream_t st);
+// gemv.hip: decode up to kGemvFusedMaxM tokens in one launch, the activation
+// quantization fused in (no workspace).
+hipError_t launch_gemv_i8_grouped(const void* x, int xdt, int64_t M, int64_t K, const int8_t* wq,
+                                  const float* w_scale, const float* w_zp, int64_t group, int64_t N,
+                                  const float* bias, void* y, int ydt, hipStream_t st);
 // Decode-sized M (<= kGroupGemvMaxM) on codes, scales and group code sums.
 hipError_t launch_gemv_group(const int8_t* xq, const float* x_scale, const int32_t* gsum, int64_t M, int64_t K,
                              const int8_t* wq, const float* w_scale, const float* w_zp, int64_t group, int64_t N,
