@@ -193,21 +193,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
 
 // ------------------------------------------------------------------ GEMM
 namespace gg {
-constexpr int BM = 128, BN = 128;
-constexpr int NW = 8, NT = 64 * NW;             // 8 waves, two per SIMD
-constexpr int WN = 4;                           // wave grid 2 (M) x 4 (N)
-constexpr int TM = 64, TN = 32;                 // wave tile
-constexpr int FM = TM / 32, FN = TN / 32;       // 32 x 32 fragments per wave (2 x 1)
 constexpr int kBK = 64;                         // bytes of K per stage
 constexpr int KS = kBK / 32;                    // k-steps per stage
 constexpr int kStages = 4;
-constexpr int kStageBytes = (BM + BN) * kBK;
-constexpr int kMeta = 256;                      // per wave and stage: 64 lanes x 4 bytes of group scales
-constexpr int LOADS = 3;                        // DMA instructions per wave per stage: A rows, B rows, scales
+constexpr int kMeta = 512;                      // per wave and stage: two 256-byte DMAs of group parameters
 constexpr int kRowsPerDma = 16;                 // one 1 KB DMA = 16 rows of 64 bytes
 constexpr int kXcds = 8, kGroupM = 4;
-static_assert(BM * (kBK / 16) == NT && BN * (kBK / 16) == NT, "one A and one B DMA per thread and stage");
 }  // namespace gg
+
+// A BM x BN tile of NW waves in a (NW / WN) x WN grid, 32 x 32 fragments.
+// DB: two accumulator sets (the fold of a group overlaps the next group's
+// MFMAs); else one set, folded between the groups.
+template <int BM_, int BN_, int NW_, int WN_, bool DB_ = true>
+struct GTile {
+  static constexpr bool DB = DB_;
+  static constexpr int BM = BM_, BN = BN_, NW = NW_, NT = 64 * NW_, WN = WN_, WM = NW_ / WN_;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int ALOADS = BM * (gg::kBK / 16) / NT, BLOADS = BN * (gg::kBK / 16) / NT;
+  // DMA per wave and stage: A rows, B rows, the group's scales and zero
+  // points of the wave's columns, the group's code sums of the wave's rows
+  static constexpr int LOADS = ALOADS + BLOADS + 2;
+  static constexpr int kStageBytes = (BM + BN) * gg::kBK;
+  static_assert(ALOADS >= 1 && BLOADS >= 1 && FM >= 1 && FN >= 1 && (TN == 32 || TN == 64), "tile shape");
+};
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * gg::kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 // v_mfma_i32_32x32x32_i8 operand of lane l: row (base + l % 32), logical
@@ -224,6 +233,14 @@ __device__ __forceinline__ void dma4(const uint8_t* gbase, uint32_t voff, uint8_
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(m0), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+// The same with a per-lane 64-bit address (lanes may read different arrays).
+__device__ __forceinline__ void dma4v(const uint8_t* addr, uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(m0), "v"(addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -244,8 +261,8 @@ __device__ __forceinline__ void group_tile_coords(int ntm, int ntn, int& tm, int
   tn = inner / gsize;
 }
 
-template <int YDT, int GS>
-__global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restrict__ xq,
+template <class TL, int YDT, int GS>
+__global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restrict__ xq,
                                                          const float* __restrict__ x_scale,
                                                          const int32_t* __restrict__ gsum, int M, int K,
                                                          const int8_t* __restrict__ wq,
@@ -253,6 +270,10 @@ __global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restri
                                                          const float* __restrict__ w_zp, int N,
                                                          const float* __restrict__ bias, void* __restrict__ y) {
   using namespace gg;
+  constexpr int BM = TL::BM, BN = TL::BN, NW = TL::NW, NT = TL::NT, WN = TL::WN;
+  constexpr int TM = TL::TM, TN = TL::TN, FM = TL::FM, FN = TL::FN;
+  constexpr int ALOADS = TL::ALOADS, BLOADS = TL::BLOADS, LOADS = TL::LOADS;
+  constexpr int kStageBytes = TL::kStageBytes;
   constexpr int SPG = GS / kBK;   // stages per group (1 or 2)
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t meta[kStages * NW * kMeta];
@@ -273,129 +294,142 @@ __global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restri
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int swave = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave / WN, wn = wave % WN;
-  // the lane's output column (one per lane: the activations are the MFMA's
-  // first operand, so D[m][n] has n = l % 32)
-  const int ncol = n0 + wn * TN + (lane & 31);
-  const int nc = ncol < N ? ncol : N - 1;
-  const float bn = bias ? bias[nc] : 0.0f;
-  if (tid < BM) f_sx[tid] = x_scale[m0 + tid < M ? m0 + tid : M - 1];   // read after the main loop's barriers
+  // the lane's output column in fragment column jj (one per lane: the
+  // activations are the MFMA's first operand, so D[m][n] has n = l % 32)
+  int ncol[FN], ncl[FN];
+  float bn[FN];
+#pragma unroll
+  for (int jj = 0; jj < FN; ++jj) {
+    ncol[jj] = n0 + wn * TN + jj * 32 + (lane & 31);
+    ncl[jj] = ncol[jj] < N ? ncol[jj] : N - 1;
+    bn[jj] = bias ? bias[ncl[jj]] : 0.0f;
+  }
+  // row scales, read after the main loop's barriers
+#pragma unroll
+  for (int u = 0; u < (BM + NT - 1) / NT; ++u) {
+    const int t = tid + u * NT;
+    if (t < BM) f_sx[t] = x_scale[m0 + t < M ? m0 + t : M - 1];
+  }
 
   // ---- DMA: lane l lands at row l / 4, physical chunk l % 4 of a 16-row
   // block, which holds logical chunk (l % 4) ^ ((row >> 2) & 3); rows past M
   // (or N) re-read the last row and only feed outputs that are not stored.
   const int lrow = lane >> 2;
   const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
-  int gm = m0 + swave * kRowsPerDma + lrow;
-  gm = gm < M ? gm : M - 1;
-  int gn = n0 + swave * kRowsPerDma + lrow;
-  gn = gn < N ? gn : N - 1;
-  const uint32_t aoff = (uint32_t)(gm * K + lchunk * 16);
-  const uint32_t boff = (uint32_t)(gn * K + lchunk * 16);
-  // group scales: lane l fetches S[j, n0 + wn*32 + l % 32], the column its
-  // accumulators belong to, into this wave's own 256 bytes of the stage
-  const uint32_t moff = (uint32_t)nc * 4u;
-  const uint8_t* const sbase = (const uint8_t*)w_scale;
-  auto meta_at = [&](int s) { return meta + ((s & 3) * NW + swave) * kMeta; };
-  auto dma_one = [&](int k, uint8_t* sa, uint8_t* sb, int s) {
-    if (k == 0) dma16((const uint8_t*)xq + s * kBK, aoff, sa + swave * kRowsPerDma * kBK);
-    else if (k == 1) dma16((const uint8_t*)wq + s * kBK, boff, sb + swave * kRowsPerDma * kBK);
-    else dma4(sbase, moff + (uint32_t)((s / SPG) * N) * 4u, meta_at(s));
+  uint32_t aoff[ALOADS], boff[BLOADS];
+#pragma unroll
+  for (int j = 0; j < ALOADS; ++j) {
+    int gm = m0 + (j * NW + swave) * kRowsPerDma + lrow;
+    gm = gm < M ? gm : M - 1;
+    aoff[j] = (uint32_t)(gm * K + lchunk * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < BLOADS; ++j) {
+    int gn = n0 + (j * NW + swave) * kRowsPerDma + lrow;
+    gn = gn < N ? gn : N - 1;
+    boff[j] = (uint32_t)(gn * K + lchunk * 16);
+  }
+  // group parameters, into the wave's own 512 bytes of the stage: lane l
+  // fetches S[j, n] (l < 32) or Z[j, n] (l >= 32) of its column
+  // n = n0 + wn TN + l % 32, then the code sum gsum[j, m] of row
+  // m = m0 + wm TM + l of the wave tile
+  static_assert(TN == 32 && TM == 64 && TL::DB, "one column of scales per lane, one row of code sums per lane");
+  const uint8_t* const szbase = (const uint8_t*)(lane < 32 ? w_scale : w_zp) + (size_t)ncl[0] * 4;
+  int grow = m0 + wm * TM + lane;
+  grow = grow < M ? grow : M - 1;
+  const uint32_t goff = (uint32_t)grow * 4u;
+  auto meta_at = [&](int s) __attribute__((always_inline)) { return meta + ((s & 3) * NW + swave) * kMeta; };
+  auto dma_one = [&](int k, uint8_t* sa, uint8_t* sb, int s) __attribute__((always_inline)) {
+    if (k < ALOADS)
+      dma16((const uint8_t*)xq + s * kBK, aoff[k], sa + (k * NW + swave) * kRowsPerDma * kBK);
+    else if (k < ALOADS + BLOADS)
+      dma16((const uint8_t*)wq + s * kBK, boff[k - ALOADS], sb + ((k - ALOADS) * NW + swave) * kRowsPerDma * kBK);
+    else if (k == ALOADS + BLOADS)
+      dma4v(szbase + (size_t)(s / SPG) * N * 4, meta_at(s));
+    else
+      dma4((const uint8_t*)gsum, goff + (uint32_t)((s / SPG) * M) * 4u, meta_at(s) + 256);
   };
-  auto dma = [&](uint8_t* sa, uint8_t* sb, int s) {
+  auto dma = [&](uint8_t* sa, uint8_t* sb, int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) dma_one(k, sa, sb, s);
   };
   const int nfull = K / kBK;   // K is a multiple of GS, hence of 64
 
-  // ---- zero-point term: f = -Sum_j (S Z)[j, n] gsum[j, m], two groups per
-  // v_mfma_f32_32x32x2_f32 (lane l: A[m = l % 32][k = l / 32], B[k][n = l % 32])
-  v16f f[FM];
+  // fp32 accumulators; the zero-point term -Sum_j (S Z)[j, n] gsum[j, m]
+  // enters in the main loop, two groups per v_mfma_f32_32x32x2_f32 (lane l:
+  // A[m = l % 32][k = l / 32], B[k][n = l % 32]), k = 0 the earlier group
+  v16f f[FM][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) f[i] = v16f{};
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) f[i][jj] = v16f{};
   if (nfull > 0) dma(sa0, sb0, 0);
   if (nfull > 1) dma(sa1, sb1, 1);
   if (nfull > 2) dma(sa2, sb2, 2);
-  {
-    int mrow[FM];
+  // the earlier group of the current pair: its code sums and -S Z
+  float gprev[FM], pprev = 0.0f;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int mm = m0 + wm * TM + i * 32 + (lane & 31);
-      mrow[i] = mm < M ? mm : M - 1;
-    }
-    // 32 groups per pass: all their loads are in flight together (and, in
-    // the first pass, together with the DMA of the first stages)
-    constexpr int kPairs = 16;
-    for (int j0 = 0; j0 < G; j0 += 2 * kPairs) {
-      float pa[kPairs][FM], pp[kPairs];
-#pragma unroll
-      for (int u = 0; u < kPairs; ++u) {
-        const int j = j0 + 2 * u + (lane >> 5);
-        const bool in = j < G;
-        const int jc = in ? j : G - 1;
-        const float sv = w_scale[jc * N + nc], zv = w_zp[jc * N + nc];
-        pp[u] = in ? -(sv * zv) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int gv = gsum[jc * M + mrow[i]];
-          pa[u][i] = in ? (float)gv : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kPairs; ++u)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) f[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[u][i], pp[u], f[i], 0, 0, 0);
-    }
-  }
+  for (int i = 0; i < FM; ++i) gprev[i] = 0.0f;
 
   using Acc = v16i;
-  Acc acc[2][FM];
+  constexpr int NSET = TL::DB ? 2 : 1;
+  Acc acc[NSET][FM][FN];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < NSET; ++h)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) acc[h][i] = Acc{};
-  float sgrp[2] = {0.0f, 0.0f};   // the scale of the group in each accumulator set
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) acc[h][i][jj] = Acc{};
+  float sgrp[2][FN];   // the scales of the group in each accumulator set
+#pragma unroll
+  for (int jj = 0; jj < FN; ++jj) sgrp[0][jj] = sgrp[1][jj] = 0.0f;
 
   const int arow = (wm * TM + (lane & 31)) * kBK;
   const int brow = (wn * TN + (lane & 31)) * kBK;
   const int loff = lane_off(lane);
   v4i fa[2][FM], fb[2][FN];
-  auto load_frag = [&](auto SET, int fi, const uint8_t* As, const uint8_t* Bs, int ks) {
+  auto load_frag = [&](auto SET, int fi, const uint8_t* As, const uint8_t* Bs, int ks) __attribute__((always_inline)) {
     constexpr int st = decltype(SET)::value;
     if (fi < FM) fa[st][fi] = *(const v4i*)(As + arow + fi * 32 * kBK + (loff ^ (ks << 5)));
     else fb[st][fi - FM] = *(const v4i*)(Bs + brow + (fi - FM) * 32 * kBK + (loff ^ (ks << 5)));
   };
-  auto load_frags = [&](auto SET, const uint8_t* As, const uint8_t* Bs, int ks) {
+  auto load_frags = [&](auto SET, const uint8_t* As, const uint8_t* Bs, int ks) __attribute__((always_inline)) {
 #pragma unroll
     for (int fi = 0; fi < FM + FN; ++fi) load_frag(SET, fi, As, Bs, ks);
   };
-  // fold part q (0 .. 2 FM - 1) of accumulator set H: 8 elements of fragment q / 2
-  auto fold = [&](auto HC, int q) {
+  // fold part q (0 .. 2 FM FN - 1) of accumulator set H: 8 elements of
+  // fragment q / 2
+  auto fold = [&](auto HC, int q) __attribute__((always_inline)) {
     constexpr int H = decltype(HC)::value;
-    const int i = q >> 1, r0 = (q & 1) * 8;
+    const int fi = q >> 1, i = fi / FN, jj = fi % FN, r0 = (q & 1) * 8;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) f[i][r0 + r] = fmaf(sgrp[H], (float)acc[H][i][r0 + r], f[i][r0 + r]);
+    for (int r = 0; r < 8; ++r)
+      f[i][jj][r0 + r] = fmaf(sgrp[H][jj], (float)acc[H][i][jj][r0 + r], f[i][jj][r0 + r]);
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using T = std::true_type;
   using F = std::false_type;
+  constexpr int NM = FM * FN;   // MFMAs per k-step; a stage (KS = 2) has 2 NM slots for 2 NM fold parts
   // One k-step's MFMAs on fragment set CUR into accumulator set H, with the
   // LDS reads of the next fragments (pf), DMA instructions of a later stage
   // (dm) and fold parts of the other accumulator set (fl) spread between
   // them; ZERO: the group's first k-step, whose MFMAs start from 0.
   auto step = [&](auto CUR, auto NXT, auto HC, auto ZERO, bool fl, int fq, bool pf, bool dm, const uint8_t* xa,
-                  const uint8_t* xb, int xks, uint8_t* da, uint8_t* db, int ds) {
+                  const uint8_t* xb, int xks, uint8_t* da, uint8_t* db, int ds) __attribute__((always_inline)) {
     constexpr int cs = decltype(CUR)::value;
     constexpr int H = decltype(HC)::value;
-    constexpr int NM = FM * FN, NF = FM + FN, NL = LOADS;
+    constexpr int NF = FM + FN, NL = LOADS;
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
       const int i = t / FN, jj = t % FN;
-      acc[H][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[cs][i], fb[cs][jj], decltype(ZERO)::value ? Acc{} : acc[H][i],
-                                                        0, 0, 0);
-      if (fl) {
-        using O = std::integral_constant<int, H ^ 1>;
-        fold(O{}, fq + t);
+      acc[H][i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+          fa[cs][i], fb[cs][jj], decltype(ZERO)::value ? Acc{} : acc[H][i][jj], 0, 0, 0);
+      if constexpr (TL::DB) {
+        if (fl) {
+          using O = std::integral_constant<int, H ^ 1>;
+          fold(O{}, fq + t);
+        }
       }
       if (pf) {
 #pragma unroll
@@ -408,7 +442,7 @@ __global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restri
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto wait_stage = [&](int s, bool steady) {
+  auto wait_stage = [&](int s, bool steady) __attribute__((always_inline)) {
     const int later = steady || (nfull - 1 - s) >= 2 ? 2 : nfull - 1 - s;
     if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
     else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
@@ -419,21 +453,51 @@ __global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restri
   // One stage (KS = 2 k-steps) whose first k-step's fragments are in register
   // set 0 (KS is even, so every stage starts in set 0).  HC: accumulator set
   // of the stage's group; FIRST: the stage opens its group (its MFMAs start
-  // from 0, it reads the group's scale, and it folds the other set, which
+  // from 0, it reads the group's scales, and it folds the other set, which
   // holds the previous group).
   auto stage = [&](auto STEADY, auto HC, auto FIRST, int s, uint8_t* ca, uint8_t* cb, const uint8_t* xa,
-                   const uint8_t* xb) {
-    constexpr int H = decltype(HC)::value;
+                   const uint8_t* xb) __attribute__((always_inline)) {
+    constexpr int H = TL::DB ? decltype(HC)::value : 0;
     constexpr bool first = decltype(FIRST)::value;
     constexpr bool steady = decltype(STEADY)::value;
-    if (first) sgrp[H] = *(const float*)(meta_at(s) + 4 * (lane & 31));
+    if constexpr (!TL::DB) {
+      // one accumulator set: fold the previous group before this one starts
+      if (first) {
+#pragma unroll
+        for (int q = 0; q < 2 * NM; ++q) fold(S0{}, q);
+      }
+    }
+    float zc = 0.0f, gc[FM];
+    if (first) {
+      const uint8_t* mt = meta_at(s);
+      sgrp[H][0] = *(const float*)(mt + 4 * (lane & 31));
+      zc = *(const float*)(mt + 128 + 4 * (lane & 31));
+#pragma unroll
+      for (int i = 0; i < FM; ++i) gc[i] = (float)*(const int*)(mt + 256 + 4 * (i * 32 + (lane & 31)));
+    }
+    using HS = std::integral_constant<int, H>;
     using Z = std::integral_constant<bool, first>;
-    step(S0{}, S1{}, HC, Z{}, first, 0, true, false, ca, cb, 1, ca, cb, 0);
+    step(S0{}, S1{}, HS{}, Z{}, first, 0, true, false, ca, cb, 1, ca, cb, 0);
     __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
     const bool nxt = steady || s + 1 < nfull;
     const bool ahead = steady || s + 4 < nfull;
     if (nxt) wait_stage(s + 1, steady);
-    step(S1{}, S0{}, HC, F{}, first, FM * FN, nxt, ahead, xa, xb, 0, ca, cb, s + 4);
+    step(S1{}, S0{}, HS{}, F{}, first, NM, nxt, ahead, xa, xb, 0, ca, cb, s + 4);
+    if (first) {
+      // the group's zero-point term, after this stage's fold parts: groups
+      // alternate between the two k of the MFMA (H is the group's parity)
+      const float pc = -(sgrp[H][0] * zc);
+      if constexpr (H == 1) {
+        const bool lo = lane < 32;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          f[i][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo ? gprev[i] : gc[i], lo ? pprev : pc, f[i][0], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) gprev[i] = gc[i];
+        pprev = pc;
+      }
+    }
   };
   // accumulator set and group opening of stage offset o in a 4-stage block
   using H0 = std::integral_constant<int, 0>;
@@ -442,7 +506,6 @@ __global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restri
   using H3 = std::integral_constant<int, (3 / SPG) & 1>;
   using F1 = std::integral_constant<bool, 1 % SPG == 0>;
   using F3 = std::integral_constant<bool, 3 % SPG == 0>;
-  static_assert(FM * FN * KS * 2 >= 2 * FM, "fold parts fit the stage's MFMA slots");
 
   if (nfull > 0) {
     wait_stage(0, false);
@@ -467,30 +530,79 @@ __global__ __launch_bounds__(gg::NT, 1) void k_gemm_group(const int8_t* __restri
   if (kt + 1 < nfull) stage(F{}, H1{}, F1{}, kt + 1, sa1, sb1, sa2, sb2);
   if (kt + 2 < nfull) stage(F{}, H2{}, T{}, kt + 2, sa2, sb2, sa3, sb3);
   // the last group's fold
-  if (((nfull / SPG - 1) & 1) == 0) {
+  if constexpr (TL::DB) {
+    if (((nfull / SPG - 1) & 1) == 0) {
 #pragma unroll
-    for (int q = 0; q < 2 * FM; ++q) fold(H0{}, q);
+      for (int q = 0; q < 2 * NM; ++q) fold(H0{}, q);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2 * NM; ++q) fold(S1{}, q);
+    }
   } else {
 #pragma unroll
-    for (int q = 0; q < 2 * FM; ++q) fold(S1{}, q);
+    for (int q = 0; q < 2 * NM; ++q) fold(H0{}, q);
   }
-
-  // ---- epilogue: y = S_x[m] f (+ b[n]); lanes 0-31 and 32-63 each store 32
-  // consecutive outputs of one row
-  if (ncol < N) {
+  if (G & 1) {   // the last group had no partner: k = 1 is zero
+    const bool lo = lane < 32;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
+      f[i][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo ? gprev[i] : 0.0f, lo ? pprev : 0.0f, f[i][0], 0, 0, 0);
+  }
+
+  // ---- epilogue: y = S_x[m] f (+ b[n]) in the output type, one 32-row slab
+  // of the wave tile at a time through LDS (the main loop's arena): a lane
+  // holds one column of 16 rows, the readback gives each lane 16 bytes of one
+  // row, which leave as one store.
+  constexpr int ES = YDT == DT_F32 ? 4 : 2;
+  constexpr int kRowB = TN * ES;                 // bytes of a wave-tile row
+  constexpr int kPitchE = kRowB + 16;            // the two half-waves' rows fall in different banks
+  constexpr int LPR = kRowB / 16;                // readback lanes per row
+  constexpr int RPI = 64 / LPR;                  // rows per readback instruction
+  static_assert(NW * 32 * kPitchE <= kStages * kStageBytes, "epilogue staging does not fit");
+  __syncthreads();                               // every wave's main-loop LDS reads are done
+  uint8_t* const stg = smem + wave * 32 * kPitchE;
+  const bool vec = (N % (16 / ES)) == 0;         // 16-byte groups of a row start aligned
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ml = wm * TM + i * 32 + out_row(r, lane), m = m0 + ml;
-        if (m < M) {
-          float v = f_sx[ml] * f[i][r];
-          if (bias) v += bn;
-          store_out<YDT>(y, (size_t)m * N + ncol, v);
+        const int rl = out_row(r, lane);
+        float v = f_sx[wm * TM + i * 32 + rl] * f[i][jj][r];
+        if (bias) v += bn[jj];
+        uint8_t* p = stg + rl * kPitchE + (jj * 32 + (lane & 31)) * ES;
+        if constexpr (YDT == DT_F32) *(float*)p = v;
+        else if constexpr (YDT == DT_F16) *(uint16_t*)p = f32_to_f16(v);
+        else *(uint16_t*)p = f32_to_bf16(v);
+      }
+    // the wave's own staging writes precede these reads (LDS is in order)
+#pragma unroll
+    for (int t = 0; t < 32 / RPI; ++t) {
+      const int row = t * RPI + lane / LPR;
+      const int cb = (lane % LPR) * 16;
+      const v4i val = *(const v4i*)(stg + row * kPitchE + cb);
+      const int m = m0 + wm * TM + i * 32 + row;
+      const int n = n0 + wn * TN + cb / ES;
+      if (m < M) {
+        uint8_t* dst = (uint8_t*)y + ((size_t)m * N + n) * ES;
+        if (vec && n + 16 / ES <= N) {
+          *(v4i*)dst = val;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16 / ES; ++e)
+            if (n + e < N) {
+              if constexpr (ES == 4) ((int*)dst)[e] = val[e];
+              else ((uint16_t*)dst)[e] = (uint16_t)((uint32_t)val[e >> 1] >> (16 * (e & 1)));
+            }
         }
       }
+    }
   }
 }
+
+// the tile the launcher uses
+using GemmTile = GTile<128, 128, 8, 4>;
 
 template <int GS>
 hipError_t gemv_gs(const int8_t* xq, const float* xs, const int32_t* gs, int64_t M, int64_t K, const int8_t* wq,
@@ -508,12 +620,13 @@ hipError_t gemv_gs(const int8_t* xq, const float* xs, const int32_t* gs, int64_t
 template <int GS>
 hipError_t gemm_gs(const int8_t* xq, const float* xs, const int32_t* gs, int64_t M, int64_t K, const int8_t* wq,
                    const float* ws, const float* wz, int64_t N, const float* bias, void* y, int ydt, hipStream_t st) {
-  const unsigned tiles = (unsigned)(((M + gg::BM - 1) / gg::BM) * ((N + gg::BN - 1) / gg::BN));
+  using TL = GemmTile;
+  const unsigned tiles = (unsigned)(((M + TL::BM - 1) / TL::BM) * ((N + TL::BN - 1) / TL::BN));
   const int m = (int)M, k = (int)K, n = (int)N;
   switch (ydt) {
-    case DT_F32: k_gemm_group<DT_F32, GS><<<tiles, gg::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
-    case DT_F16: k_gemm_group<DT_F16, GS><<<tiles, gg::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
-    default: k_gemm_group<DT_BF16, GS><<<tiles, gg::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+    case DT_F32: k_gemm_group<TL, DT_F32, GS><<<tiles, TL::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+    case DT_F16: k_gemm_group<TL, DT_F16, GS><<<tiles, TL::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
+    default: k_gemm_group<TL, DT_BF16, GS><<<tiles, TL::NT, 0, st>>>(xq, xs, gs, m, k, wq, ws, wz, n, bias, y); break;
   }
   return hipGetLastError();
 }
