@@ -196,7 +196,7 @@ namespace gg {
 constexpr int kBK = 64;                         // bytes of K per stage
 constexpr int KS = kBK / 32;                    // k-steps per stage
 constexpr int kStages = 4;
-constexpr int kMeta = 512;                      // per wave and stage: two 256-byte DMAs of group parameters
+constexpr int kMeta = 768;                      // per wave and stage: three 256-byte DMAs of group parameters
 constexpr int kRowsPerDma = 16;                 // one 1 KB DMA = 16 rows of 64 bytes
 constexpr int kXcds = 8, kGroupM = 4;
 }  // namespace gg
@@ -213,7 +213,7 @@ struct GTile {
   static constexpr int ALOADS = BM * (gg::kBK / 16) / NT, BLOADS = BN * (gg::kBK / 16) / NT;
   // DMA per wave and stage: A rows, B rows, the group's scales and zero
   // points of the wave's columns, the group's code sums of the wave's rows
-  static constexpr int LOADS = ALOADS + BLOADS + 2;
+  static constexpr int LOADS = ALOADS + BLOADS + 3;
   static constexpr int kStageBytes = (BM + BN) * gg::kBK;
   static_assert(ALOADS >= 1 && BLOADS >= 1 && FM >= 1 && FN >= 1 && (TN == 32 || TN == 64), "tile shape");
 };
@@ -233,14 +233,6 @@ __device__ __forceinline__ void dma4(const uint8_t* gbase, uint32_t voff, uint8_
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(m0), "v"(voff), "s"(gbase)
-               : "memory", "m0");
-}
-// The same with a per-lane 64-bit address (lanes may read different arrays).
-__device__ __forceinline__ void dma4v(const uint8_t* addr, uint8_t* lds) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :
-               : "s"(m0), "v"(addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -329,12 +321,13 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
     gn = gn < N ? gn : N - 1;
     boff[j] = (uint32_t)(gn * K + lchunk * 16);
   }
-  // group parameters, into the wave's own 512 bytes of the stage: lane l
-  // fetches S[j, n] (l < 32) or Z[j, n] (l >= 32) of its column
-  // n = n0 + wn TN + l % 32, then the code sum gsum[j, m] of row
-  // m = m0 + wm TM + l of the wave tile
-  static_assert(TN == 32 && TM == 64 && TL::DB, "one column of scales per lane, one row of code sums per lane");
-  const uint8_t* const szbase = (const uint8_t*)(lane < 32 ? w_scale : w_zp) + (size_t)ncl[0] * 4;
+  // group parameters, into the wave's own 768 bytes of the stage: S[j, n]
+  // and Z[j, n] of the wave's columns n = n0 + wn TN + l % TN, then the code
+  // sums gsum[j, m] of its rows m = m0 + wm TM + l
+  static_assert(TM == 64 && TL::DB, "one row of code sums per lane");
+  int pcol = n0 + wn * TN + (lane & (TN - 1));
+  pcol = pcol < N ? pcol : N - 1;
+  const uint32_t poff = (uint32_t)pcol * 4u;
   int grow = m0 + wm * TM + lane;
   grow = grow < M ? grow : M - 1;
   const uint32_t goff = (uint32_t)grow * 4u;
@@ -345,9 +338,11 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
     else if (k < ALOADS + BLOADS)
       dma16((const uint8_t*)wq + s * kBK, boff[k - ALOADS], sb + ((k - ALOADS) * NW + swave) * kRowsPerDma * kBK);
     else if (k == ALOADS + BLOADS)
-      dma4v(szbase + (size_t)(s / SPG) * N * 4, meta_at(s));
+      dma4((const uint8_t*)w_scale, poff + (uint32_t)((s / SPG) * N) * 4u, meta_at(s));
+    else if (k == ALOADS + BLOADS + 1)
+      dma4((const uint8_t*)w_zp, poff + (uint32_t)((s / SPG) * N) * 4u, meta_at(s) + 256);
     else
-      dma4((const uint8_t*)gsum, goff + (uint32_t)((s / SPG) * M) * 4u, meta_at(s) + 256);
+      dma4((const uint8_t*)gsum, goff + (uint32_t)((s / SPG) * M) * 4u, meta_at(s) + 512);
   };
   auto dma = [&](uint8_t* sa, uint8_t* sb, int s) __attribute__((always_inline)) {
 #pragma unroll
@@ -367,9 +362,11 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
   if (nfull > 1) dma(sa1, sb1, 1);
   if (nfull > 2) dma(sa2, sb2, 2);
   // the earlier group of the current pair: its code sums and -S Z
-  float gprev[FM], pprev = 0.0f;
+  float gprev[FM], pprev[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) gprev[i] = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < FN; ++jj) pprev[jj] = 0.0f;
 
   using Acc = v16i;
   constexpr int NSET = TL::DB ? 2 : 1;
@@ -467,13 +464,16 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
         for (int q = 0; q < 2 * NM; ++q) fold(S0{}, q);
       }
     }
-    float zc = 0.0f, gc[FM];
+    float zc[FN], gc[FM];
     if (first) {
       const uint8_t* mt = meta_at(s);
-      sgrp[H][0] = *(const float*)(mt + 4 * (lane & 31));
-      zc = *(const float*)(mt + 128 + 4 * (lane & 31));
 #pragma unroll
-      for (int i = 0; i < FM; ++i) gc[i] = (float)*(const int*)(mt + 256 + 4 * (i * 32 + (lane & 31)));
+      for (int jj = 0; jj < FN; ++jj) {
+        sgrp[H][jj] = *(const float*)(mt + 4 * (jj * 32 + (lane & 31)));
+        zc[jj] = *(const float*)(mt + 256 + 4 * (jj * 32 + (lane & 31)));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) gc[i] = (float)*(const int*)(mt + 512 + 4 * (i * 32 + (lane & 31)));
     }
     using HS = std::integral_constant<int, H>;
     using Z = std::integral_constant<bool, first>;
@@ -486,16 +486,22 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
     if (first) {
       // the group's zero-point term, after this stage's fold parts: groups
       // alternate between the two k of the MFMA (H is the group's parity)
-      const float pc = -(sgrp[H][0] * zc);
+      float pc[FN];
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) pc[jj] = -(sgrp[H][jj] * zc[jj]);
       if constexpr (H == 1) {
         const bool lo = lane < 32;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          f[i][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo ? gprev[i] : gc[i], lo ? pprev : pc, f[i][0], 0, 0, 0);
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj)
+            f[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo ? gprev[i] : gc[i], lo ? pprev[jj] : pc[jj], f[i][jj],
+                                                            0, 0, 0);
       } else {
 #pragma unroll
         for (int i = 0; i < FM; ++i) gprev[i] = gc[i];
-        pprev = pc;
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) pprev[jj] = pc[jj];
       }
     }
   };
@@ -546,7 +552,9 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
     const bool lo = lane < 32;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      f[i][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo ? gprev[i] : 0.0f, lo ? pprev : 0.0f, f[i][0], 0, 0, 0);
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj)
+        f[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(lo ? gprev[i] : 0.0f, lo ? pprev[jj] : 0.0f, f[i][jj], 0, 0, 0);
   }
 
   // ---- epilogue: y = S_x[m] f (+ b[n]) in the output type, one 32-row slab
