@@ -388,6 +388,13 @@ def bench_ceilings(dev, steps):
                                                        "TFLOPS": round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)}
     except Exception as e:
         out["lib_fp8_rowwise_gemm_4096x4096x14336"] = f"unavailable: {str(e)[:80]}"
+    # register-only MFMA loops (include/q8_bench.h): the matrix-core rate with
+    # no memory traffic, 512 workgroups (two waves per SIMD)
+    sink = torch.empty(512 * 256, dtype=torch.int32, device=dev)
+    for fmt, name, per in (("int8_sym", "mfma_loop_int8_TOPS", 65536), ("fp8_e4m3", "mfma_loop_fp8_TFLOPS", 131072)):
+        iters = 4000
+        ms = t_ms(lambda: q8.q8_bench_mfma_loop(fmt, iters, 512, sink))
+        out[name] = round(512 * 4 * iters * 4 * per / (ms * 1e-3) / 1e12, 1)
     return out
 
 

@@ -12,6 +12,7 @@ from w8a8_quantized_linear_channel_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "q8.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "q8_bench.h")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libq8.so not built")
 
@@ -23,7 +24,7 @@ NAN = float("nan")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = open(HEADER).read() + open(BENCH_HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(q8_[a-z0-9_]+)\s*\(", text)))
 
@@ -248,3 +249,14 @@ def test_grouped_validation():
     assert call(M=11, wb=100) == 7           # above the fused decode path the workspace is needed
     assert call(y=MIS) == 6
     assert call(ws=MIS) == 6
+
+
+def test_bench_mfma_loop_validation():
+    f = _lib.lib().q8_bench_mfma_loop
+    E = _lib
+    assert f(E.Q8_INT8_ASYM, 10, 8, P, None) == 4
+    assert f(E.Q8_INT8_SYM, 0, 8, P, None) == 5
+    assert f(E.Q8_INT8_SYM, 10, 0, P, None) == 5
+    assert f(E.Q8_FP8_E4M3, 10, 65537, P, None) == 5
+    assert f(E.Q8_INT8_SYM, 10, 8, None, None) == 1
+    assert f(E.Q8_INT8_SYM, 10, 8, MIS, None) == 6

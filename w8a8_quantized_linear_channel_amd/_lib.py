@@ -1,4 +1,5 @@
-"""ctypes loader for libq8.so (the C ABI declared in include/q8.h).
+"""ctypes loader for libq8.so (the C ABI declared in include/q8.h, and the
+measurement helper of include/q8_bench.h).
 
 Argument marshalling only: this module never computes anything itself.  If
 the library has not been built the loader raises; there is no fallback.
@@ -43,6 +44,8 @@ SIGNATURES = {
     "q8_quantize_weight_grouped": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P]),
     "q8_linear_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _INT, _P, _SZ, _P]),
     "q8_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
+    # include/q8_bench.h
+    "q8_bench_mfma_loop": (_INT, [_INT, _I64, _I64, _P, _P]),
     "q8_status_str": (ctypes.c_char_p, [_INT]),
 }
 

@@ -3,6 +3,7 @@
 // reported before any HIP call (and can be exercised on a machine without a
 // GPU); then the device of the stream is checked once per device and cached.
 #include "q8.h"
+#include "q8_bench.h"
 
 #include <hip/hip_runtime.h>
 
@@ -11,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "q8_bench_kernels.hpp"
 #include "q8_group.hpp"
 #include "q8_kernels.hpp"
 
@@ -534,6 +536,17 @@ q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t 
   if (M <= q8::kGroupGemvMaxM)
     return launched(q8::launch_gemv_group(xq, xs, gs, M, K, wq, w_scale, w_zp, group, N, bias, y, y_dtype, st));
   return launched(q8::launch_gemm_group(xq, xs, gs, M, K, wq, w_scale, w_zp, group, N, bias, y, y_dtype, st));
+}
+
+q8_status q8_bench_mfma_loop(q8_format fmt, int64_t iters, int64_t workgroups, int32_t* sink, void* stream) {
+  if (fmt != Q8_INT8_SYM && fmt != Q8_FP8_E4M3) return Q8_ERR_BAD_FORMAT;
+  if (iters < 1 || iters > kMaxRows || workgroups < 1 || workgroups > 65536) return Q8_ERR_BAD_ARG;
+  if (!sink) return Q8_ERR_NULL_PTR;
+  if (!aligned16(sink)) return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {sink}));
+  return launched(q8::launch_mfma_loop(fmt == Q8_INT8_SYM ? 0 : 2, iters, workgroups, sink, st));
 }
 
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,

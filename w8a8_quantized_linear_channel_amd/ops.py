@@ -350,3 +350,13 @@ def q8_linear_grouped(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, 
                                       _ptr(bias), _ptr(y), _DT[out_dtype], _ptr(ws), ws.numel(), _stream(dev))
     _lib.check("q8_linear_grouped", st)
     return y
+
+
+def q8_bench_mfma_loop(fmt: str, iters: int, workgroups: int, sink: torch.Tensor) -> None:
+    """Measurement helper (include/q8_bench.h): a register-only MFMA loop,
+    fmt "int8_sym" (int8 32x32x32) or "fp8_e4m3" (fp8 32x32x64); sink is a
+    device int32 tensor of workgroups * 256 elements."""
+    dev = sink.device
+    _need(sink, "sink", torch.int32, (workgroups * 256,), dev)
+    st = _lib.lib().q8_bench_mfma_loop(_FMT[fmt], iters, workgroups, _ptr(sink), _stream(dev))
+    _lib.check("q8_bench_mfma_loop", st)
