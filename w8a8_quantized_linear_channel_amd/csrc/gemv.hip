@@ -76,15 +76,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   const uint8_t* xb = (const uint8_t*)x;
   uint8_t* const xw = xs[wave];
   const int nseg = (K + kSeg - 1) / kSeg;
-  auto seg_len = [&](int sg) { return (K - sg * kSeg) < kSeg ? (K - sg * kSeg) : kSeg; };
+  auto seg_len = [&](int sg) __attribute__((always_inline)) { return (K - sg * kSeg) < kSeg ? (K - sg * kSeg) : kSeg; };
 
   // The lane's columns inside the wave's 1024: chunk j (0, 1) is columns
   // [512 j + 8 lane, 512 j + 8 lane + 8); a chunk lies wholly inside or
   // wholly outside the segment (both are multiples of 8 or 16).
-  auto col = [&](int j) { return wave * kKW + 512 * j + 8 * lane; };
+  auto col = [&](int j) __attribute__((always_inline)) { return wave * kKW + 512 * j + 8 * lane; };
 
   // ---- X of one segment into LDS, 16-bit inputs: two 1 KB DMA per row
-  auto dma_x = [&](int k0, int seg) {
+  auto dma_x = [&](int k0, int seg) __attribute__((always_inline)) {
     for (int m = 0; m < M; ++m) {
       const uint8_t* base = xb + ((size_t)m * K + k0) * 2;
 #pragma unroll
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     }
   };
   // the lane's 16 values of row m: from LDS (16-bit) or from global (fp32)
-  auto get_x = [&](int m, int k0, int seg, float* v) {
+  auto get_x = [&](int m, int k0, int seg, float* v) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const bool ok = col(j) < seg;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   v4i wv[kSteps];
   const int wrow = (n0 + lr < N ? n0 + lr : N - 1);
   const __amdgpu_buffer_rsrc_t wres = byte_buffer(wq, (uint32_t)N * (uint32_t)K);
-  auto load_w = [&](int k0) {
+  auto load_w = [&](int k0) __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(wrow * K + k0 + wave * kKW + lg * 16);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) wv[s] = load16_nt(wres, base + s * 64);
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   // epilogue factors (wave 0): acc register r of lane (lr, lg) is
   // D[n = 4 lg + r][m = lr].
   float fsc[4] = {0, 0, 0, 0}, fzp[4] = {0, 0, 0, 0}, fbi[4] = {0, 0, 0, 0};
-  auto load_factors = [&]() {
+  auto load_factors = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = n0 + 4 * lg + r;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   // Block-wide reduction of lred over the 256 threads, all rows at once:
   // thread t takes row t/16 and 16 of its partials, then the 16 threads of
   // the row (one DPP row) combine theirs; every one of them gets the result.
-  auto reduce_rows = [&](auto op) {
+  auto reduce_rows = [&](auto op) __attribute__((always_inline)) {
     const int m = tid >> 4, sub = tid & 15;
     const v4i* src = (const v4i*)&lred[m][sub * 16];
     int r = 0;
@@ -159,9 +159,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     }
     return dpp_row_reduce(r, op);
   };
-  auto fmax_bits = [](int a, int b) { return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b))); };
-  auto add_int = [](int a, int b) { return a + b; };
-  auto row_scale = [&](int m) { return rscale[m]; };
+  auto fmax_bits = [](int a, int b) __attribute__((always_inline)) { return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b))); };
+  auto add_int = [](int a, int b) __attribute__((always_inline)) { return a + b; };
+  auto row_scale = [&](int m) __attribute__((always_inline)) { return rscale[m]; };
   v4i acc = {0, 0, 0, 0};
   // per-group weights: the group code sums and the fp32 sum over groups
   v4i accs = {0, 0, 0, 0};
@@ -170,25 +170,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   float gsc[NG][4], gzp[NG][4];
   // the parameters of this wave's groups in segment k0 (groups past K are
   // clamped and their fold is skipped)
-  auto load_groups = [&](int k0) {
+  auto load_groups = [&](int k0) __attribute__((always_inline)) {
     if constexpr (GS > 0) {
       const int G = K / GS, g0 = (k0 + wave * kKW) / GS;
+      // N a multiple of 4: the lane's columns are one aligned 16-byte quad
+      // (clamped to the last quad past N; those outputs are not stored)
+      const bool quad = (N & 3) == 0;
+      const int q0 = n0 + 4 * lg < N ? n0 + 4 * lg : N - 4;
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
         const int gi = g0 + t < G ? g0 + t : G - 1;
+        if (quad) {
+          const v4f sv = *(const v4f*)(w_scale + gi * N + q0), zv = *(const v4f*)(w_zp + gi * N + q0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = n0 + 4 * lg + r;
-          const int nc = n < N ? n : N - 1;
-          gsc[t][r] = w_scale[gi * N + nc];
-          gzp[t][r] = w_zp[gi * N + nc];
+          for (int r = 0; r < 4; ++r) {
+            gsc[t][r] = sv[r];
+            gzp[t][r] = zv[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 4 * lg + r;
+            const int nc = n < N ? n : N - 1;
+            gsc[t][r] = w_scale[gi * N + nc];
+            gzp[t][r] = w_zp[gi * N + nc];
+          }
         }
       }
     }
   };
 
   // ---- pass 1 over one segment: per-row partial absmax
-  auto pass1 = [&](int sg, int k0, int seg) {
+  auto pass1 = [&](int sg, int k0, int seg) __attribute__((always_inline)) {
     if constexpr (DT != DT_F32) {
       if (sg > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // reads of the last segment are done
       dma_x(k0, seg);
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     }
   };
   // row scales from the partial absmax of every thread
-  auto finish_scales = [&]() {
+  auto finish_scales = [&]() __attribute__((always_inline)) {
     __syncthreads();   // every thread's partial absmax is in LDS
     const int r = reduce_rows(fmax_bits);
     if ((tid & 15) == 0 && (tid >> 4) < M) {
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   };
   // ---- pass 2 over one segment: codes, then the MFMAs on them.  reload:
   // X (and, past the first segment, W) must be fetched again.
-  auto pass2 = [&](int sg, int k0, int seg, bool reload) {
+  auto pass2 = [&](int sg, int k0, int seg, bool reload) __attribute__((always_inline)) {
     if (reload) {
       if constexpr (DT != DT_F32) {
         __builtin_amdgcn_s_waitcnt(kLgkmcnt0);

@@ -119,6 +119,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
   int nc[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) nc[r] = n0 + 4 * lg + r < N ? n0 + 4 * lg + r : N - 1;
+  // N a multiple of 4: the lane's columns n0 + 4 lg .. + 3 are one aligned
+  // quad (clamped to the last quad past N; those outputs are not stored)
+  const bool quad = (N & 3) == 0;
+  const int q0 = n0 + 4 * lg < N ? n0 + 4 * lg : N - 4;
   uint8_t* const wl = wsm[wave];
   uint8_t* const cl = csm[wave];
   const int xr = lr < M ? lr : M - 1;    // code rows past M repeat the last: they feed unstored columns
@@ -143,10 +147,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
 #pragma unroll
     for (int t = 0; t < NG; ++t) {
       const int gi = g0 + t < G ? g0 + t : G - 1;
+      if (quad) {   // the lane's four columns are one aligned 16-byte quad
+        const v4f sv = *(const v4f*)(w_scale + gi * N + q0), zv = *(const v4f*)(w_zp + gi * N + q0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ps[t][r] = w_scale[gi * N + nc[r]];
-        pz[t][r] = w_zp[gi * N + nc[r]];
+        for (int r = 0; r < 4; ++r) {
+          ps[t][r] = sv[r];
+          pz[t][r] = zv[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ps[t][r] = w_scale[gi * N + nc[r]];
+          pz[t][r] = w_zp[gi * N + nc[r]];
+        }
       }
       pg[t] = gsum[gi * M + mc];
     }
