@@ -337,7 +337,7 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
   // group parameters, into the wave's own 768 bytes of the stage: S[j, n]
   // and Z[j, n] of the wave's columns n = n0 + wn TN + l % TN, then the code
   // sums gsum[j, m] of its rows m = m0 + wm TM + l
-  static_assert(TM == 64 && TL::DB, "one row of code sums per lane");
+  static_assert(TM == 64, "one row of code sums per lane");
   int pcol = n0 + wn * TN + (lane & (TN - 1));
   pcol = pcol < N ? pcol : N - 1;
   const uint32_t poff = (uint32_t)pcol * 4u;
@@ -467,7 +467,8 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
   // holds the previous group).
   auto stage = [&](auto STEADY, auto HC, auto FIRST, int s, uint8_t* ca, uint8_t* cb, const uint8_t* xa,
                    const uint8_t* xb) __attribute__((always_inline)) {
-    constexpr int H = TL::DB ? decltype(HC)::value : 0;
+    constexpr int PAR = decltype(HC)::value;   // the group's parity
+    constexpr int H = TL::DB ? PAR : 0;        // its accumulator set
     constexpr bool first = decltype(FIRST)::value;
     constexpr bool steady = decltype(STEADY)::value;
     if constexpr (!TL::DB) {
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
       float pc[FN];
 #pragma unroll
       for (int jj = 0; jj < FN; ++jj) pc[jj] = -(sgrp[H][jj] * zc[jj]);
-      if constexpr (H == 1) {
+      if constexpr (PAR == 1) {
         const bool lo = lane < 32;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
