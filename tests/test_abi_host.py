@@ -260,3 +260,11 @@ def test_bench_mfma_loop_validation():
     assert f(E.Q8_FP8_E4M3, 10, 65537, P, None) == 5
     assert f(E.Q8_INT8_SYM, 10, 8, None, None) == 1
     assert f(E.Q8_INT8_SYM, 10, 8, MIS, None) == 6
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without libq8.so every call raises (there is no CPU path)."""
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libq8.so"))
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
