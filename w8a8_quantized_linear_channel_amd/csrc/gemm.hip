@@ -608,7 +608,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
                                       (v4i*)((uint16_t*)g.y + o));
         }
       } else {
-        for (int e = 0; e < 8 && n + e < N; ++e) store_out<YDT>(g.y, o + e, v[e]);
+        if constexpr (YDT != DT_I8)   // (the INT8 output left above)
+          for (int e = 0; e < 8 && n + e < N; ++e) store_out<YDT>(g.y, o + e, v[e]);
       }
     }
   }
