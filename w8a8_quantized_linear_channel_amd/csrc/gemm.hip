@@ -520,6 +520,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   const float csb[8] = {csb0[0], csb0[1], csb0[2], csb0[3], csb1[0], csb1[1], csb1[2], csb1[3]};
   const float cbb[8] = {cbb0[0], cbb0[1], cbb0[2], cbb0[3], cbb1[0], cbb1[1], cbb1[2], cbb1[3]};
   const int czi[8] = {czi0[0], czi0[1], czi0[2], czi0[3], czi1[0], czi1[1], czi1[2], czi1[3]};
+  // acc - Z rowsum as one full-rate 24-bit multiply-add: |Z| <= 128 and
+  // |rowsum| <= 127 K < 2^23 (K <= 65536), and the product fits 32 bits
+  // (a full 32-bit multiply issues at a quarter of the rate)
+  auto zcorr = [](int acc, int z, int rs) { return acc + __mul24(-z, rs); };
   constexpr int ES = YDT == DT_F32 ? 4 : 2;
   const bool vec = (N & 7) == 0;                        // 8-column groups start 16-byte aligned
 #pragma unroll
@@ -570,7 +574,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
         if (!ok) continue;
         int qv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = requant_i8(sx, csb[e], a[e] - czi[e] * rrs[t], cbb[e], g.y_inv);
+        for (int e = 0; e < 8; ++e) qv[e] = requant_i8(sx, csb[e], zcorr(a[e], czi[e], rrs[t]), cbb[e], g.y_inv);
         int8_t* yq = (int8_t*)g.y + o;
         if (vec) {
           *(v2i*)yq = v2i{(int)pack_lo_bytes(qv[0], qv[1], qv[2], qv[3]), (int)pack_lo_bytes(qv[4], qv[5], qv[6], qv[7])};
@@ -583,7 +587,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if constexpr (KIND == GEMM_INT8) {
-          v[e] = (sx * csb[e]) * (float)(a[e] - czi[e] * rrs[t]) + cbb[e];
+          v[e] = (sx * csb[e]) * (float)zcorr(a[e], czi[e], rrs[t]) + cbb[e];
         } else if constexpr (KIND == GEMM_FP8) {
           v[e] = __int_as_float(a[e]) * (sx * csb[e]) + cbb[e];
         } else {
