@@ -421,6 +421,7 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
   using T = std::true_type;
   using F = std::false_type;
   constexpr int NM = FM * FN;   // MFMAs per k-step; a stage (KS = 2) has 2 NM slots for 2 NM fold parts
+  static_assert(KS == 2, "a stage is two k-steps of the 32x32x32 MFMA");
   // One k-step's MFMAs on fragment set CUR into accumulator set H, with the
   // LDS reads of the next fragments (pf), DMA instructions of a later stage
   // (dm) and fold parts of the other accumulator set (fl) spread between
