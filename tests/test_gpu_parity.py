@@ -328,6 +328,34 @@ def test_decomp_llm_int8_full_size():
     assert O.outlier_columns(wl.x, 6.0).tolist() == wl.extra["outlier_cols"].tolist()
 
 
+@pytest.mark.parametrize("M,N,K,seed", [(512, 4096, 4096, 31),   # the LLM.int8 shape, other seeds
+                                        (512, 4096, 8192, 32),   # two K segments of the outlier list
+                                        (300, 3000, 1024, 33),   # ragged M and N
+                                        (200, 1000, 512, 34)])
+def test_decomp_whole_accumulator(M, N, K, seed):
+    """Every tile: the whole INT32 accumulator against the exact product of
+    the oracle's codes (a float64 matmul of integers below 2^53 is exact), the
+    output on sampled rows, and a second call giving the same bits.  (Seed 31
+    has an outlier weight S (q - Z) next to a tie of fp16, where a fused
+    single-rounding conversion differs from the two roundings.)"""
+    log(f"[decomp] whole accumulator: M={M} N={N} K={K}")
+    wl = inputs.llm_int8_outliers(seed=seed, M=M, K=K, N=N, n_outlier_cols=5)
+    rows = sample_rows(M, 8, seed=seed, extra=(127, 128, 255, 256))
+    y = run_decomp_case(wl.x, wl.w, 6.0, rows=rows, what="whole")
+    wq, ws, wz = q8.q8_quantize_weight(g(wl.w), "int8_asym")
+    y1, _, _, acc = q8.q8_linear_int8_decomp(g(wl.x), wq, ws, wz, threshold=6.0, return_outliers=True, acc_out=True)
+    y2 = q8.q8_linear_int8_decomp(g(wl.x), wq, ws, wz, threshold=6.0)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "second call differs"
+    assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), "acc_out changes the output"
+    cols = O.outlier_columns(wl.x, 6.0)
+    xm = O.to_f32(wl.x).copy()
+    xm[:, cols] = 0
+    rq_x, _, _ = O.quantize_act_int8_sym(xm)
+    rq, _, _ = oracle_weights(wl.w)
+    acc_ref = rq_x.astype(np.float64) @ rq.astype(np.float64).T
+    assert_equal(host(acc), acc_ref.astype(np.int64).astype(np.int32), "whole INT32 accumulator")
+
+
 @pytest.mark.parametrize("tau", [6.0, 0.0, -1.0, 1e-30])
 def test_decomp_thresholds(tau):
     log(f"[decomp] threshold {tau}")

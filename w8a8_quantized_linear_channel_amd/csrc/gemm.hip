@@ -53,6 +53,19 @@ constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
+// Outlier weight of the LLM.int8 flow: fp16(fp32(S (q - Z))), the product
+// rounded to fp32 before the conversion to fp16, as the dequantized fp32
+// weights are cast to fp16.  Left alone, the compiler fuses the multiply and
+// the conversion into one v_fma_mixlo_f16 (even with contraction off), which
+// rounds the exact product to fp16 once and differs from the two roundings
+// next to a tie of fp16; the empty asm makes the fp32 product a value of its
+// own.
+__device__ __forceinline__ _Float16 outlier_weight_f16(float s, int q, float z) {
+  float p = s * ((float)q - z);
+  asm volatile("" : "+v"(p));
+  return (_Float16)p;
+}
+
 // One MFMA shape.  A fragment row is (base multiple of 32) + lane % 32, so
 // ((row >> 2) & 3) == ((lane >> 2) & 3) and the swizzled byte offset of the
 // lane's operand inside its LDS row is lane_off(lane) XOR a per-k-step constant.
@@ -485,11 +498,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
         const bool nok = n < N;
         const float sb = f_sb[nl], zb = (float)f_zi[nl];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float wv = 0.0f;
-          if (col[e] >= 0 && nok) wv = sb * ((float)(int8_t)g.b[n * K + col[e]] - zb);
-          wo[j][e] = (_Float16)wv;
-        }
+        for (int e = 0; e < 8; ++e)
+          wo[j][e] = (col[e] >= 0 && nok) ? outlier_weight_f16(sb, (int8_t)g.b[n * K + col[e]], zb) : (_Float16)0.0f;
       }
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
