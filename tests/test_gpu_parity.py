@@ -696,3 +696,59 @@ def test_linear_grouped_bias_and_dtypes(M):
         x = inputs.random_matrix(122, (M, 512), 1.0, xd)
         for od in (torch.float32, torch.float16, torch.bfloat16):
             run_grouped_linear_case(x, w, 128, od, bias=bias, what=f"x {xd} y {od}")
+
+
+# ---------------------------------------------------------------- graph capture
+def test_graph_capture_replays_match_eager():
+    """Every call is asynchronous on the caller's stream and allocates nothing,
+    so it can be captured in a HIP graph.  Each captured call is replayed three
+    times, with eager work and synchronizations between the replays, and every
+    replay must give the eager result bit for bit (no memset nodes, no state
+    kept between calls)."""
+    log("[graph] capture and replay: decode (fused, on codes), GEMM, LLM.int8, FP8, per-group")
+    wl = inputs.decode_qproj(M=16)
+    w = g(wl.w[:512, :1024].contiguous())
+    wq, ws, wz = q8.q8_quantize_weight(w, "int8_asym")
+    gq, gs, gz = q8.q8_quantize_weight_grouped(w, 128)
+    fq, fs = q8.q8_quantize_weight(w, "fp8_e4m3")[:2]
+    xs = {M: g(inputs.random_matrix(200 + M, (M, 1024), 1.0, torch.bfloat16)) for M in (1, 16, 96)}
+    d = inputs.llm_int8_outliers(seed=9, M=96, K=1024, N=512, n_outlier_cols=3)
+    dq, ds, dz = q8.q8_quantize_weight(g(d.w), "int8_asym")
+    xd = g(d.x)
+    calls = []
+    for M, x in xs.items():
+        y = torch.empty(M, 512, dtype=torch.bfloat16, device=DEV)
+        wsp = torch.empty(max(1, q8.q8_workspace_bytes("linear", M, 512, 1024)), dtype=torch.uint8, device=DEV)
+        calls.append((f"linear M={M}", y, lambda x=x, y=y, wsp=wsp: q8.q8_linear(x, wq, ws, wz, out=y, workspace=wsp)))
+        yg_ = torch.empty(M, 512, dtype=torch.bfloat16, device=DEV)
+        wg = torch.empty(max(1, q8.q8_workspace_bytes("grouped", M, 512, 1024)), dtype=torch.uint8, device=DEV)
+        calls.append((f"grouped M={M}", yg_,
+                      lambda x=x, y=yg_, wg=wg: q8.q8_linear_grouped(x, gq, gs, gz, 128, out=y, workspace=wg)))
+    yd = torch.empty(96, 512, dtype=torch.float16, device=DEV)
+    wd = torch.empty(q8.q8_workspace_bytes("decomp", 96, 512, 1024), dtype=torch.uint8, device=DEV)
+    calls.append(("llm.int8", yd, lambda: q8.q8_linear_int8_decomp(xd, dq, ds, dz, 6.0, out=yd, workspace=wd)))
+    yf = torch.empty(96, 512, dtype=torch.bfloat16, device=DEV)
+    wf = torch.empty(q8.q8_workspace_bytes("fp8", 96, 512, 1024), dtype=torch.uint8, device=DEV)
+    calls.append(("fp8", yf, lambda: q8.q8_linear_fp8(xs[96], fq, fs, out=yf, workspace=wf)))
+
+    eager = {}
+    for name, y, fn in calls:
+        fn()
+        torch.cuda.synchronize()
+        eager[name] = y.clone()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for _, _, fn in calls:
+                fn()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for _, y, _ in calls:
+            y.fill_(0)                      # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, y, _ in calls:
+            assert torch.equal(y.view(torch.int16), eager[name].view(torch.int16)), f"replay {rep}: {name} differs"
