@@ -209,7 +209,7 @@ namespace gg {
 constexpr int kBK = 64;                         // bytes of K per stage
 constexpr int KS = kBK / 32;                    // k-steps per stage
 constexpr int kStages = 4;
-constexpr int kMeta = 768;                      // per wave and stage: three 256-byte DMAs of group parameters
+constexpr int kMetaSlot = 2048;                 // per stage: the group's S, Z (128 columns), code sums (128 rows), spare
 constexpr int kRowsPerDma = 16;                 // one 1 KB DMA = 16 rows of 64 bytes
 constexpr int kXcds = 8, kGroupM = 4;
 }  // namespace gg
@@ -224,9 +224,9 @@ struct GTile {
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int ALOADS = BM * (gg::kBK / 16) / NT, BLOADS = BN * (gg::kBK / 16) / NT;
-  // DMA per wave and stage: A rows, B rows, the group's scales and zero
-  // points of the wave's columns, the group's code sums of the wave's rows
-  static constexpr int LOADS = ALOADS + BLOADS + 3;
+  // DMA per wave and stage: A rows and B rows; the first stage of a group
+  // adds one DMA of the group's parameters
+  static constexpr int AB = ALOADS + BLOADS;
   static constexpr int kStageBytes = (BM + BN) * gg::kBK;
   static_assert(ALOADS >= 1 && BLOADS >= 1 && FM >= 1 && FN >= 1 && (TN == 32 || TN == 64), "tile shape");
 };
@@ -249,6 +249,17 @@ __device__ __forceinline__ void dma4(const uint8_t* gbase, uint32_t voff, uint8_
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) for a uniform n in 0..N (the count must be an immediate)
+template <int N>
+__device__ __forceinline__ void vm_wait_upto(int n) {
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    else vm_wait_upto<N - 1>(n);
+  }
+}
 
 // XCD-contiguous renumbering, then kGroupM tile-rows per L2 group
 __device__ __forceinline__ void group_tile_coords(int ntm, int ntn, int& tm, int& tn) {
@@ -277,11 +288,11 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
   using namespace gg;
   constexpr int BM = TL::BM, BN = TL::BN, NW = TL::NW, NT = TL::NT, WN = TL::WN;
   constexpr int TM = TL::TM, TN = TL::TN, FM = TL::FM, FN = TL::FN;
-  constexpr int ALOADS = TL::ALOADS, BLOADS = TL::BLOADS, LOADS = TL::LOADS;
+  constexpr int ALOADS = TL::ALOADS, BLOADS = TL::BLOADS, AB = TL::AB;
   constexpr int kStageBytes = TL::kStageBytes;
   constexpr int SPG = GS / kBK;   // stages per group (1 or 2)
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t meta[kStages * NW * kMeta];
+  __shared__ __attribute__((aligned(16))) uint8_t meta[kStages * kMetaSlot];
   __shared__ float f_sx[BM];
   uint8_t* const sa0 = smem;
   uint8_t* const sb0 = smem + BM * kBK;
@@ -334,34 +345,46 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
     gn = gn < N ? gn : N - 1;
     boff[j] = (uint32_t)(gn * K + lchunk * 16);
   }
-  // group parameters, into the wave's own 768 bytes of the stage: S[j, n]
-  // and Z[j, n] of the wave's columns n = n0 + wn TN + l % TN, then the code
-  // sums gsum[j, m] of its rows m = m0 + wm TM + l
-  static_assert(TM == 64, "one row of code sums per lane");
-  int pcol = n0 + wn * TN + (lane & (TN - 1));
-  pcol = pcol < N ? pcol : N - 1;
-  const uint32_t poff = (uint32_t)pcol * 4u;
-  int grow = m0 + wm * TM + lane;
-  grow = grow < M ? grow : M - 1;
-  const uint32_t goff = (uint32_t)grow * 4u;
-  auto meta_at = [&](int s) __attribute__((always_inline)) { return meta + ((s & 3) * NW + swave) * kMeta; };
+  const int nfull = K / kBK;   // K is a multiple of GS, hence of 64
+  // The group's parameters for the whole tile, once per group, into the
+  // stage's meta slot: one 256-byte DMA per wave.  Waves 0, 1: S[j, n] of the
+  // tile's 128 columns (bytes 0..511 of the slot); 2, 3: Z[j, n] (512..1023);
+  // 4, 5: the code sums gsum[j, m] of its 128 rows (1024..1535); 6, 7 a second
+  // copy of S into the spare bytes, so that every wave issues the same number
+  // of DMAs and one vmcnt fits all.
+  static_assert(BM == 128 && BN == 128 && NW == 8, "eight 64-entry parameter DMAs per group");
+  const int mk = swave >> 1, mh = swave & 1;
+  const uint8_t* mbase;
+  int mstride, mlds, mix;
+  if (mk == 2) {
+    mix = m0 + mh * 64 + lane;
+    mix = mix < M ? mix : M - 1;
+    mbase = (const uint8_t*)gsum;
+    mstride = M;
+  } else {
+    mix = n0 + mh * 64 + lane;
+    mix = mix < N ? mix : N - 1;
+    mbase = (const uint8_t*)(mk == 1 ? w_zp : w_scale);
+    mstride = N;
+  }
+  mlds = mk * 512 + mh * 256;
+  const uint32_t moff = (uint32_t)mix * 4u;
+  auto meta_at = [&](int s) __attribute__((always_inline)) { return meta + (s & (kStages - 1)) * kMetaSlot; };
   auto dma_one = [&](int k, uint8_t* sa, uint8_t* sb, int s) __attribute__((always_inline)) {
     if (k < ALOADS)
       dma16((const uint8_t*)xq + s * kBK, aoff[k], sa + (k * NW + swave) * kRowsPerDma * kBK);
-    else if (k < ALOADS + BLOADS)
+    else if (k < AB)
       dma16((const uint8_t*)wq + s * kBK, boff[k - ALOADS], sb + ((k - ALOADS) * NW + swave) * kRowsPerDma * kBK);
-    else if (k == ALOADS + BLOADS)
-      dma4((const uint8_t*)w_scale, poff + (uint32_t)((s / SPG) * N) * 4u, meta_at(s));
-    else if (k == ALOADS + BLOADS + 1)
-      dma4((const uint8_t*)w_zp, poff + (uint32_t)((s / SPG) * N) * 4u, meta_at(s) + 256);
     else
-      dma4((const uint8_t*)gsum, goff + (uint32_t)((s / SPG) * M) * 4u, meta_at(s) + 512);
+      dma4(mbase, moff + (uint32_t)((s / SPG) * mstride) * 4u, meta_at(s) + mlds);
   };
+  // DMA instructions of stage t (0 past the last stage)
+  auto loads_of = [&](int t) __attribute__((always_inline)) { return t < nfull ? AB + (t % SPG == 0) : 0; };
   auto dma = [&](uint8_t* sa, uint8_t* sb, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < LOADS; ++k) dma_one(k, sa, sb, s);
+    for (int k = 0; k < AB; ++k) dma_one(k, sa, sb, s);
+    if (s % SPG == 0) dma_one(AB, sa, sb, s);
   };
-  const int nfull = K / kBK;   // K is a multiple of GS, hence of 64
 
   // fp32 accumulators; the zero-point term -Sum_j (S Z)[j, n] gsum[j, m]
   // enters in the main loop, two groups per v_mfma_f32_32x32x2_f32 (lane l:
@@ -426,11 +449,12 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
   // LDS reads of the next fragments (pf), DMA instructions of a later stage
   // (dm) and fold parts of the other accumulator set (fl) spread between
   // them; ZERO: the group's first k-step, whose MFMAs start from 0.
-  auto step = [&](auto CUR, auto NXT, auto HC, auto ZERO, bool fl, int fq, bool pf, bool dm, const uint8_t* xa,
-                  const uint8_t* xb, int xks, uint8_t* da, uint8_t* db, int ds) __attribute__((always_inline)) {
+  auto step = [&](auto CUR, auto NXT, auto HC, auto ZERO, auto MD, bool fl, int fq, bool pf, bool dm,
+                  const uint8_t* xa, const uint8_t* xb, int xks, uint8_t* da, uint8_t* db,
+                  int ds) __attribute__((always_inline)) {
     constexpr int cs = decltype(CUR)::value;
     constexpr int H = decltype(HC)::value;
-    constexpr int NF = FM + FN, NL = LOADS;
+    constexpr int NF = FM + FN, NL = AB + (decltype(MD)::value ? 1 : 0);
 #pragma unroll
     for (int t = 0; t < NM; ++t) {
       const int i = t / FN, jj = t % FN;
@@ -453,11 +477,12 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Stage s complete: the DMAs of the (at most two) stages issued after it
+  // may still be in flight.  In the steady state one of every two
+  // consecutive stages opens a group when SPG = 2, both when SPG = 1.
   auto wait_stage = [&](int s, bool steady) __attribute__((always_inline)) {
-    const int later = steady || (nfull - 1 - s) >= 2 ? 2 : nfull - 1 - s;
-    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (steady) vm_wait_upto<2 * AB + 2 / SPG>(2 * AB + 2 / SPG);
+    else vm_wait_upto<2 * AB + 2>(loads_of(s + 1) + loads_of(s + 2));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
@@ -484,20 +509,22 @@ __global__ __launch_bounds__(TL::NT, 1) void k_gemm_group(const int8_t* __restri
       const uint8_t* mt = meta_at(s);
 #pragma unroll
       for (int jj = 0; jj < FN; ++jj) {
-        sgrp[H][jj] = *(const float*)(mt + 4 * (jj * 32 + (lane & 31)));
-        zc[jj] = *(const float*)(mt + 256 + 4 * (jj * 32 + (lane & 31)));
+        const int c = wn * TN + jj * 32 + (lane & 31);
+        sgrp[H][jj] = *(const float*)(mt + 4 * c);
+        zc[jj] = *(const float*)(mt + 512 + 4 * c);
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) gc[i] = (float)*(const int*)(mt + 512 + 4 * (i * 32 + (lane & 31)));
+      for (int i = 0; i < FM; ++i) gc[i] = (float)*(const int*)(mt + 1024 + 4 * (wm * TM + i * 32 + (lane & 31)));
     }
     using HS = std::integral_constant<int, H>;
     using Z = std::integral_constant<bool, first>;
-    step(S0{}, S1{}, HS{}, Z{}, first, 0, true, false, ca, cb, 1, ca, cb, 0);
+    step(S0{}, S1{}, HS{}, Z{}, F{}, first, 0, true, false, ca, cb, 1, ca, cb, 0);
     __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
     const bool nxt = steady || s + 1 < nfull;
     const bool ahead = steady || s + 4 < nfull;
     if (nxt) wait_stage(s + 1, steady);
-    step(S1{}, S0{}, HS{}, F{}, first, NM, nxt, ahead, xa, xb, 0, ca, cb, s + 4);
+    // the stage DMA'd here, s + 4, opens a group exactly when s does
+    step(S1{}, S0{}, HS{}, F{}, FIRST, first, NM, nxt, ahead, xa, xb, 0, ca, cb, s + 4);
     if (first) {
       // the group's zero-point term, after this stage's fold parts: groups
       // alternate between the two k of the MFMA (H is the group's parity)
