@@ -26,7 +26,14 @@
  * - Every argument is checked on the host BEFORE anything is enqueued.  On a
  *   non-Q8_OK status nothing has been written.  Q8_ERR_LAUNCH reports a
  *   failed kernel launch (hipGetLastError) after validation passed.
- * - Preconditions checked for every call: M, N, K >= 1; K % 16 == 0;
+ * - Empty batches: every call that takes activations accepts M = 0 (T = 0
+ *   for q8_linear_fp8_grouped).  It checks its other arguments as usual; the
+ *   pointers to M-sized arrays (x, codes, scales, code sums, y, acc_out) may
+ *   then be NULL, no workspace is needed (q8_workspace_bytes returns 0), and
+ *   nothing is enqueued or written, except that q8_linear_int8_decomp writes
+ *   0 to n_outliers when it is given (the outlier set of no rows is empty).
+ * - Preconditions checked for every call: M >= 0 and N, K >= 1 (weight
+ *   quantization: N, K >= 1); K % 16 == 0;
  *   K <= 65536 (keeps the zero-point-corrected INT32 sums in range); every
  *   matrix (X, W, Y) has fewer than 2^31 elements; all pointers 16-byte
  *   aligned; the device running `stream` is gfx950.
@@ -48,7 +55,7 @@ extern "C" {
 typedef enum q8_status {
   Q8_OK = 0,
   Q8_ERR_NULL_PTR = 1,   /* a required pointer is NULL */
-  Q8_ERR_BAD_SHAPE = 2,  /* M, N or K < 1, or K % 16 != 0, or a size overflows */
+  Q8_ERR_BAD_SHAPE = 2,  /* M < 0, N or K < 1, K % 16 != 0, or a size overflows */
   Q8_ERR_BAD_DTYPE = 3,  /* unsupported element type for this argument */
   Q8_ERR_BAD_FORMAT = 4, /* unsupported quantization format for this call */
   Q8_ERR_BAD_ARG = 5,    /* NaN threshold/bound, or a pointer that must be NULL is not */

@@ -73,9 +73,13 @@ def test_workspace_sizes():
     assert ws(_lib.Q8_OP_GROUPED, 10, 4096, 4096) == 0        # fused decode
     assert ws(_lib.Q8_OP_GROUPED, 11, 4096, 4096) == 11 * 4096 + 256 + 11 * 64 * 4
     assert ws(_lib.Q8_OP_GROUPED, 2048, 14336, 4096) == 2048 * 4096 + 8192 + 2048 * 64 * 4
+    # an empty batch needs no workspace on any path
+    for op in (_lib.Q8_OP_LINEAR, _lib.Q8_OP_DECOMP, _lib.Q8_OP_FP8, _lib.Q8_OP_STATIC, _lib.Q8_OP_GROUPED):
+        assert ws(op, 0, 4096, 4096) == 0
     # invalid shapes give 0
-    assert ws(_lib.Q8_OP_LINEAR, 0, 16, 16) == 0
+    assert ws(_lib.Q8_OP_LINEAR, -1, 16, 16) == 0
     assert ws(_lib.Q8_OP_LINEAR, 16, 16, 24) == 0
+    assert ws(_lib.Q8_OP_DECOMP, 16, 0, 16) == 0
 
 
 def test_quantize_weight_validation():
@@ -147,6 +151,38 @@ def test_decomp_and_fp8_validation():
     assert g(None, 64, 64, P, P, 64, 1200.0, None, P, P2, 1 << 24, None) == 1
 
 
+def test_empty_batch_validation():
+    """M = 0 (an empty batch) is a valid shape: the pointers to M-sized
+    arrays may be NULL, and every other argument is still checked (each call
+    here fails before the device check, so no GPU work can start)."""
+    L = _lib.lib()
+    E = _lib
+    lin = L.q8_linear
+    # wq still required / K % 16 / N >= 1 / dtype / M < 0
+    assert lin(None, E.Q8_BF16, 0, 64, None, P, P, 64, None, None, E.Q8_BF16, None, 0, None, None) == 1
+    assert lin(None, E.Q8_BF16, 0, 40, P, P, P, 64, None, None, E.Q8_BF16, None, 0, None, None) == 2
+    assert lin(None, E.Q8_BF16, 0, 64, P, P, P, 0, None, None, E.Q8_BF16, None, 0, None, None) == 2
+    assert lin(None, 9, 0, 64, P, P, P, 64, None, None, E.Q8_BF16, None, 0, None, None) == 3
+    assert lin(None, E.Q8_BF16, -1, 64, P, P, P, 64, None, None, E.Q8_BF16, None, 0, None, None) == 2
+    # NaN threshold, misaligned bias, NaN scale bound: still rejected at M = 0
+    assert L.q8_linear_int8_decomp(None, 0, 64, P, P, P, 64, NAN, None, None, None, 0, None, None, None,
+                                   None) == 5
+    assert L.q8_linear_int8_decomp(None, 0, 64, P, P, P, 64, 6.0, MIS, None, None, 0, None, None, None,
+                                   None) == 6
+    assert L.q8_linear_fp8(None, 0, 64, P, P, 64, NAN, None, None, None, 0, None) == 5
+    assert L.q8_gemm_int8(None, None, None, 0, 64, None, P, P, 64, None, None, E.Q8_BF16, None, None) == 1
+    assert L.q8_gemm_fp8(None, None, 0, 40, P, P, 64, None, None, None) == 2
+    assert L.q8_quantize_act(E.Q8_FP8_E4M3, None, E.Q8_BF16, 0, 64, 0.0, None, None, None, None) == 5
+    assert L.q8_quantize_act_static(None, E.Q8_BF16, 0, 64, 0.0, None, None, None) == 5
+    assert L.q8_linear_static(None, E.Q8_BF16, 0, 64, 0.5, P, P, P, 64, None, NAN, None, None, 0, None) == 5
+    assert L.q8_linear_w8a16(None, E.Q8_F32, 0, 64, P, P, P, 64, None, None, E.Q8_BF16, None) == 3
+    assert L.q8_linear_grouped(None, E.Q8_BF16, 0, 64, P, P, P, 96, 64, None, None, E.Q8_BF16, None, 0,
+                               None) == 2
+    assert L.q8_linear_fp8_grouped(None, 0, 64, P, 0, P, P, 64, 1200.0, None, None, 0, None) == 2
+    # weights have no empty case: N = 0 stays a shape error
+    assert L.q8_quantize_weight(E.Q8_INT8_ASYM, P, E.Q8_F32, 0, 16, P, P, P, None) == 2
+
+
 def test_valid_arguments_without_a_device_report_device_error():
     """With every argument valid, the call reaches the device check, which
     fails cleanly when there is no GPU (the CPU test host).  Never run where a
@@ -156,6 +192,9 @@ def test_valid_arguments_without_a_device_report_device_error():
         pytest.skip("a GPU is visible; the no-device path is checked on CPU hosts only")
     E = _lib
     st = _lib.lib().q8_quantize_weight(E.Q8_INT8_ASYM, P, E.Q8_F32, 4, 16, P, P, P, None)
+    assert st == 8
+    # an empty batch with NULL activations and outputs passes every argument check
+    st = _lib.lib().q8_linear(None, E.Q8_BF16, 0, 64, P, P, P, 64, None, None, E.Q8_BF16, None, 0, None, None)
     assert st == 8
 
 

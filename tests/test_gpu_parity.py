@@ -698,6 +698,54 @@ def test_linear_grouped_bias_and_dtypes(M):
             run_grouped_linear_case(x, w, 128, od, bias=bias, what=f"x {xd} y {od}")
 
 
+# ---------------------------------------------------------------- empty batch
+def test_empty_batch_every_entry_point():
+    """An empty batch (M = 0 tokens) gives empty outputs from every call
+    that takes activations and enqueues nothing; the LLM.int8 call still
+    reports its outlier set as empty (count 0, list untouched).  A call on a
+    real batch before and after gives the same bits."""
+    from w8a8_quantized_linear_channel_amd import _lib
+    log("[empty] M = 0 through every activation entry point")
+    K, N = 256, 128
+    w = g(inputs.random_matrix(71, (N, K), 0.02, torch.float32))
+    wq, ws, wz = q8.q8_quantize_weight(w, "int8_asym")
+    fq, fs = q8.q8_quantize_weight(w, "fp8_e4m3")[:2]
+    gq, gs, gz = q8.q8_quantize_weight_grouped(w, 128)
+    x3 = g(inputs.random_matrix(72, (3, K), 1.0, torch.bfloat16))
+    before = q8.q8_linear(x3, wq, ws, wz)
+    xb = torch.empty(0, K, dtype=torch.bfloat16, device=DEV)
+    xh = torch.empty(0, K, dtype=torch.float16, device=DEV)
+    assert q8.q8_linear(xb, wq, ws, wz).shape == (0, N)
+    xq, xs, rs = q8.q8_quantize_act(xb)
+    assert xq.shape == (0, K) and xs.shape == (0,) and rs.shape == (0,)
+    fx, fxs, _ = q8.q8_quantize_act(xb, "fp8_e4m3", scale_ub=1200.0)
+    assert fx.shape == (0, K)
+    assert q8.q8_gemm_int8(xq, xs, rs, wq, ws, wz).shape == (0, N)
+    assert q8.q8_gemm_fp8(fx, fxs, fq, fs).shape == (0, N)
+    assert q8.q8_linear_fp8(xb, fq, fs).shape == (0, N)
+    assert q8.q8_linear_w8a16(xb, wq, ws, wz).shape == (0, N)
+    assert q8.q8_linear_grouped(xb, gq, gs, gz, 128).shape == (0, N)
+    sq, srs = q8.q8_quantize_act_static(xb, 0.05)
+    assert sq.shape == (0, K) and srs.shape == (0,)
+    assert q8.q8_linear_static(xb, 0.05, wq, ws, wz, 0.1).shape == (0, N)
+    eq, es = q8.q8_quantize_weight(w.repeat(3, 1), "fp8_e4m3")[:2]
+    off = torch.zeros(4, dtype=torch.int32, device=DEV)
+    assert q8.q8_linear_fp8_grouped(xb, off, eq.view(3, N, K), es.view(3, N)).shape == (0, N)
+    assert q8.q8_linear_int8_decomp(xh, wq, ws, wz, 6.0).shape == (0, N)
+    # the count is written even for no rows; the list is left alone
+    cnt = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    idx = torch.full((K,), -5, dtype=torch.int32, device=DEV)
+    st = _lib.lib().q8_linear_int8_decomp(None, 0, K, wq.data_ptr(), ws.data_ptr(), wz.data_ptr(), N, 6.0, None,
+                                          None, None, 0, idx.data_ptr(), cnt.data_ptr(), None,
+                                          torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 0 and bool((idx == -5).all())
+    after = q8.q8_linear(x3, wq, ws, wz)
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), after.view(torch.int16))
+
+
 # ---------------------------------------------------------------- graph capture
 def test_graph_capture_replays_match_eager():
     """Every call is asynchronous on the caller's stream and allocates nothing,

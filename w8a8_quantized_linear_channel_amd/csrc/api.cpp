@@ -27,14 +27,16 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_dtype(int d) { return d == Q8_F32 || d == Q8_F16 || d == Q8_BF16; }
 
-q8_status check_mk(int64_t M, int64_t K) {
-  if (M < 1 || K < 1 || M > kMaxRows) return Q8_ERR_BAD_SHAPE;
+// M rows of K; min_m = 0 admits an empty batch of activations
+q8_status check_mk(int64_t M, int64_t K, int64_t min_m = 1) {
+  if (M < min_m || K < 1 || M > kMaxRows) return Q8_ERR_BAD_SHAPE;
   if (K % 16 != 0 || K > kMaxK) return Q8_ERR_BAD_SHAPE;
   return Q8_OK;
 }
 
+// M activation rows (0: an empty batch), N weight rows, K features
 q8_status check_mnk(int64_t M, int64_t N, int64_t K) {
-  q8_status s = check_mk(M, K);
+  q8_status s = check_mk(M, K, 0);
   if (s != Q8_OK) return s;
   if (N < 1 || N > kMaxRows) return Q8_ERR_BAD_SHAPE;
   // the GEMM indexes its operands and output with 32-bit offsets
@@ -117,6 +119,7 @@ bool valid_group(int64_t group, int64_t K) { return (group == 64 || group == 128
 
 struct DecompWs { size_t xq, xs, rs, flags, idx, cnt, total; };
 DecompWs decomp_ws(int64_t M, int64_t K) {
+  if (M == 0) return DecompWs{};   // an empty batch needs no scratch
   Carve c;
   DecompWs w;
   w.xq = c.take((size_t)M * K);
@@ -262,8 +265,8 @@ q8_status q8_quantize_act(q8_format fmt, const void* x, q8_dtype x_dtype, int64_
                           float scale_ub, void* xq, float* x_scale, int32_t* x_rowsum, void* stream) {
   if (fmt != Q8_INT8_SYM && fmt != Q8_FP8_E4M3) return Q8_ERR_BAD_FORMAT;
   if (!valid_dtype(x_dtype)) return Q8_ERR_BAD_DTYPE;
-  Q8_TRY(check_mk(M, K));
-  if (!x || !xq || !x_scale) return Q8_ERR_NULL_PTR;
+  Q8_TRY(check_mk(M, K, 0));
+  if (M > 0 && (!x || !xq || !x_scale)) return Q8_ERR_NULL_PTR;
   if (fmt == Q8_FP8_E4M3) {
     if (x_rowsum) return Q8_ERR_BAD_ARG;
     if (std::isnan(scale_ub) || scale_ub <= 0.0f) return Q8_ERR_BAD_ARG;
@@ -273,6 +276,7 @@ q8_status q8_quantize_act(q8_format fmt, const void* x, q8_dtype x_dtype, int64_
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, xq, x_scale, x_rowsum}));
+  if (M == 0) return Q8_OK;
   if (fmt == Q8_INT8_SYM)
     return launched(q8::launch_quant_act_i8(x, x_dtype, M, K, static_cast<int8_t*>(xq),
                                             x_scale, x_rowsum, st));
@@ -286,7 +290,7 @@ q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const
                     void* stream) {
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
   Q8_TRY(check_mnk(M, N, K));
-  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
   const LinearWs ws = linear_ws(M, K);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
@@ -296,6 +300,7 @@ q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace, acc_out}));
+  if (M == 0) return Q8_OK;
 
   if (M <= q8::kGemvFusedMaxM)
     return launched(q8::launch_gemv_i8(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype,
@@ -315,10 +320,10 @@ q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_
                                 int32_t* outlier_idx, int32_t* n_outliers, int32_t* acc_out,
                                 void* stream) {
   Q8_TRY(check_mnk(M, N, K));
-  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
   if (std::isnan(threshold)) return Q8_ERR_BAD_ARG;
   const DecompWs ws = decomp_ws(M, K);
-  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
       !aligned16(workspace) || (bias && !aligned16(bias)) || (acc_out && !aligned16(acc_out)) ||
       (outlier_idx && !aligned16(outlier_idx)) || (n_outliers && !aligned16(n_outliers)))
@@ -326,6 +331,14 @@ q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace, outlier_idx, n_outliers, acc_out}));
+  if (M == 0) {
+    // the outlier set of an empty batch is empty: only the count is written,
+    // by the quantizer's compaction workgroup alone (no flags, no rows)
+    if (n_outliers)
+      return launched(q8::launch_quant_act_f16_outliers(nullptr, 0, K, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                        n_outliers, nullptr, nullptr, st));
+    return Q8_OK;
+  }
 
   char* base = static_cast<char*>(workspace);
   int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
@@ -364,16 +377,17 @@ q8_status q8_linear_fp8(const void* x, int64_t M, int64_t K, const uint8_t* wq, 
                         int64_t N, float scale_ub, const float* bias, void* y, void* workspace,
                         size_t workspace_bytes, void* stream) {
   Q8_TRY(check_mnk(M, N, K));
-  if (!x || !wq || !w_scale || !y) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
   if (std::isnan(scale_ub) || scale_ub <= 0.0f) return Q8_ERR_BAD_ARG;
   const Fp8Ws ws = fp8_ws(M, K);
-  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) || !aligned16(workspace) ||
       (bias && !aligned16(bias)))
     return Q8_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, bias, y, workspace}));
+  if (M == 0) return Q8_OK;
 
   char* base = static_cast<char*>(workspace);
   uint8_t* xq = reinterpret_cast<uint8_t*>(base + ws.xq);
@@ -397,16 +411,17 @@ q8_status q8_linear_fp8_grouped(const void* x, int64_t T, int64_t K, const int32
                                 void* workspace, size_t workspace_bytes, void* stream) {
   Q8_TRY(check_mnk(T, N, K));
   if (E < 1 || E > kMaxGroups || E * N > kMaxRows) return Q8_ERR_BAD_SHAPE;
-  if (!x || !expert_offsets || !wq || !w_scale || !y) return Q8_ERR_NULL_PTR;
+  if (!expert_offsets || !wq || !w_scale || (T > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
   if (std::isnan(scale_ub) || scale_ub <= 0.0f) return Q8_ERR_BAD_ARG;
   const Fp8Ws ws = fp8_ws(T, K);
-  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) || !aligned16(workspace) ||
       !aligned4(expert_offsets))
     return Q8_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, expert_offsets, wq, w_scale, y, workspace}));
+  if (T == 0) return Q8_OK;
 
   char* base = static_cast<char*>(workspace);
   uint8_t* xq = reinterpret_cast<uint8_t*>(base + ws.xq);
@@ -432,7 +447,7 @@ q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_
                        const float* bias, void* y, q8_dtype y_dtype, int32_t* acc_out, void* stream) {
   if (!valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
   Q8_TRY(check_mnk(M, N, K));
-  if (!xq || !x_scale || !x_rowsum || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || !w_zp || (M > 0 && (!xq || !x_scale || !x_rowsum || !y))) return Q8_ERR_NULL_PTR;
   if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(x_rowsum) || !aligned16(wq) ||
       !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) || (bias && !aligned16(bias)) ||
       (acc_out && !aligned16(acc_out)))
@@ -440,19 +455,21 @@ q8_status q8_gemm_int8(const int8_t* xq, const float* x_scale, const int32_t* x_
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {xq, x_scale, x_rowsum, wq, w_scale, w_zp, bias, y, acc_out}));
+  if (M == 0) return Q8_OK;
   return launched(int8_on_codes(xq, x_scale, x_rowsum, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st));
 }
 
 q8_status q8_quantize_act_static(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, float x_scale,
                                  int8_t* xq, int32_t* x_rowsum, void* stream) {
   if (!valid_dtype(x_dtype)) return Q8_ERR_BAD_DTYPE;
-  Q8_TRY(check_mk(M, K));
-  if (!x || !xq) return Q8_ERR_NULL_PTR;
+  Q8_TRY(check_mk(M, K, 0));
+  if (M > 0 && (!x || !xq)) return Q8_ERR_NULL_PTR;
   if (!std::isfinite(x_scale) || x_scale <= 0.0f) return Q8_ERR_BAD_ARG;
   if (!aligned16(x) || !aligned16(xq) || (x_rowsum && !aligned16(x_rowsum))) return Q8_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, xq, x_rowsum}));
+  if (M == 0) return Q8_OK;
   return launched(q8::launch_quant_act_i8_static(x, x_dtype, M, K, x_scale, xq, nullptr, x_rowsum, st));
 }
 
@@ -462,17 +479,18 @@ q8_status q8_linear_static(const void* x, q8_dtype x_dtype, int64_t M, int64_t K
                            size_t workspace_bytes, void* stream) {
   if (!valid_dtype(x_dtype)) return Q8_ERR_BAD_DTYPE;
   Q8_TRY(check_mnk(M, N, K));
-  if (!x || !wq || !w_scale || !w_zp || !yq) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !yq))) return Q8_ERR_NULL_PTR;
   if (!std::isfinite(x_scale) || x_scale <= 0.0f || !std::isfinite(y_scale) || y_scale <= 0.0f)
     return Q8_ERR_BAD_ARG;
   const LinearWs ws = static_ws(M, K);
-  if (!workspace || workspace_bytes < ws.total) return Q8_ERR_WORKSPACE;
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(yq) ||
       (bias && !aligned16(bias)) || !aligned16(workspace))
     return Q8_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, yq, workspace}));
+  if (M == 0) return Q8_OK;
   char* base = static_cast<char*>(workspace);
   int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
   float* xs = reinterpret_cast<float*>(base + ws.xs);
@@ -488,13 +506,14 @@ q8_status q8_linear_w8a16(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype) || x_dtype == Q8_F32) return Q8_ERR_BAD_DTYPE;
   Q8_TRY(check_mnk(M, N, K));
   if (M > q8::kW8A16MaxM) return Q8_ERR_BAD_SHAPE;
-  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
       (bias && !aligned16(bias)))
     return Q8_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y}));
+  if (M == 0) return Q8_OK;
   return launched(q8::launch_gemv_w8a16(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, st));
 }
 
@@ -517,7 +536,7 @@ q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t 
   if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
   Q8_TRY(check_mnk(M, N, K));
   if (!valid_group(group, K)) return Q8_ERR_BAD_SHAPE;
-  if (!x || !wq || !w_scale || !w_zp || !y) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
   const GroupedWs ws = grouped_ws(M, K);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
@@ -526,6 +545,7 @@ q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace}));
+  if (M == 0) return Q8_OK;
   if (M <= q8::kGemvFusedMaxM)
     return launched(q8::launch_gemv_i8_grouped(x, x_dtype, M, K, wq, w_scale, w_zp, group, N, bias, y, y_dtype, st));
   char* base = static_cast<char*>(workspace);
@@ -552,13 +572,14 @@ q8_status q8_bench_mfma_loop(q8_format fmt, int64_t iters, int64_t workgroups, i
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,
                       const float* w_scale, int64_t N, const float* bias, void* y, void* stream) {
   Q8_TRY(check_mnk(M, N, K));
-  if (!xq || !x_scale || !wq || !w_scale || !y) return Q8_ERR_NULL_PTR;
+  if (!wq || !w_scale || (M > 0 && (!xq || !x_scale || !y))) return Q8_ERR_NULL_PTR;
   if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
       (bias && !aligned16(bias)))
     return Q8_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Q8_TRY(check_device(st));
   Q8_TRY(check_ptrs(st, {xq, x_scale, wq, w_scale, bias, y}));
+  if (M == 0) return Q8_OK;
   q8::GemmArgs g{};
   g.a = xq;
   g.b = wq;
