@@ -698,6 +698,55 @@ def test_linear_grouped_bias_and_dtypes(M):
             run_grouped_linear_case(x, w, 128, od, bias=bias, what=f"x {xd} y {od}")
 
 
+# ---------------------------------------------------------------- maximum sizes
+@pytest.mark.parametrize("M", [1, 16, 33])
+def test_linear_max_k_extreme_accumulators(M):
+    """K = 65536, the largest accepted, with codes that drive the INT32 sums
+    to their extremes: acc = -16256 K and the zero-point-corrected sum
+    -32385 K = -2.12e9 (127 * 255 * K, within 1.3 % of the int32 limit), on
+    the fused decode (M = 1), the GEMV on codes (M = 16) and the GEMM (M = 33)."""
+    log(f"[linear] K = 65536 extreme codes, M={M}")
+    wl = inputs.extreme_codes(M=M)
+    rq, _, rz = oracle_weights(wl.w)
+    assert (rq[0::3] == -128).all() and (rz[0::3] == 127).all()
+    assert (rq[1::3] == 127).all() and (rz[1::3] == -128).all()
+    y, acc = run_linear_case(wl.x, wl.w, torch.bfloat16, what=f"K=65536 M={M}")
+    a = host(acc)
+    assert a[:, 0::3].min() == -16256 * 65536 and a[:, 1::3].max() == 16129 * 65536
+
+
+def test_linear_max_weight_elements_sampled():
+    """A weight matrix of N * K = 32767 * 65536 = 2^31 - 65536 elements, just
+    under the 2^31 limit of the 32-bit offsets (2 GB of int8 codes), through
+    the fused decode (M = 1) and the GEMM (M = 64); codes, scales and zero
+    points are bit-exact and outputs within tolerance on sampled rows up to
+    the last one."""
+    N, K = 32767, 65536
+    log(f"[linear] {N}x{K} weights (2^31 - 2^16 elements), sampled rows")
+    base, rows_of = inputs.tiled_rows(K=K)
+    bg = g(base)
+    w = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    for r0 in range(0, N, 4096):
+        r1 = min(N, r0 + 4096)
+        w[r0:r1] = rows_of(bg, torch.arange(r0, r1, device=DEV))
+    wq, ws, wz = q8.q8_quantize_weight(w, "int8_asym")
+    del w, bg
+    torch.cuda.empty_cache()
+    sel = np.array([0, 1, 256, 16383, 32511, 32640, 32765, N - 1])
+    w_sel = rows_of(base, torch.from_numpy(sel))
+    rq, rs, rz = O.quantize_weight_int8_asym(w_sel)
+    assert_equal(host(wq[torch.from_numpy(sel).to(DEV)]), rq, "codes of the sampled rows")
+    assert_equal(host(ws[torch.from_numpy(sel).to(DEV)]).view(np.uint32), rs.view(np.uint32), "scales")
+    assert_equal(host(wz[torch.from_numpy(sel).to(DEV)]), rz, "zero points")
+    x = inputs.random_matrix(82, (64, K), 1.0, torch.bfloat16)
+    for M in (1, 64):
+        y = q8.q8_linear(g(x[:M]), wq, ws, wz, out_dtype=torch.bfloat16)
+        y_ref, _ = O.linear_int8(x[:M], rq, rs, rz)
+        check_close(out_f64(y)[:, sel], y_ref, f"max weight elements M={M}")
+    del wq
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- empty batch
 def test_empty_batch_every_entry_point():
     """An empty batch (M = 0 tokens) gives empty outputs from every call

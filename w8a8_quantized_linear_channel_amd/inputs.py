@@ -136,3 +136,34 @@ def random_matrix(seed: int, shape, std: float = 1.0,
     """Generic N(0, std) matrix for ragged-shape parity cases."""
     rng = np.random.default_rng(seed)
     return _cast(normal(rng, shape, std), dtype)
+
+
+def extreme_codes(seed: int = 11, M: int = 33, N: int = 64, K: int = 65536) -> Workload:
+    """Largest accumulator magnitudes at the largest K: every activation row is
+    a positive constant (all its int8 codes are +127); weight rows n % 3 == 0
+    are a negative constant (codes -128, zero point 127), rows n % 3 == 1 a
+    positive constant (codes 127, zero point -128), the rest N(0, 0.02).  The
+    constants are multiples of 1/64 and 1/1024, exact in bf16 and fp32."""
+    rng = np.random.default_rng(seed)
+    x = np.repeat((0.5 + np.arange(M, dtype=np.float32) / 64)[:, None], K, axis=1)
+    w = normal(rng, (N, K), 0.02)
+    n = np.arange(N)
+    mag = (0.25 + n.astype(np.float32) / 1024).astype(np.float32)
+    w[n % 3 == 0] = -mag[n % 3 == 0][:, None]
+    w[n % 3 == 1] = mag[n % 3 == 1][:, None]
+    return Workload(f"extreme_codes_M{M}_N{N}_K{K}", _cast(x, torch.bfloat16), _cast(w, torch.float32),
+                    torch.bfloat16, {})
+
+
+def tiled_rows(seed: int = 12, B: int = 257, K: int = 65536):
+    """A weight matrix of any height from a small seeded base: row n is
+    base[n % B] * mult[n] with mult[n] = 1 + (n % 7) / 8 (exact), one float32
+    product per element.  Returns (base float32 [B, K], a function giving the
+    rows `rows` (an index tensor) on the device of `base`)."""
+    base = random_matrix(seed, (B, K), 0.02, torch.float32)
+
+    def rows_of(base_t: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:
+        mult = 1.0 + (rows % 7).to(torch.float32) / 8.0
+        return base_t[rows % B] * mult[:, None]
+
+    return base, rows_of
