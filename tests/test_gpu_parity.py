@@ -715,6 +715,31 @@ def test_linear_max_k_extreme_accumulators(M):
     assert a[:, 0::3].min() == -16256 * 65536 and a[:, 1::3].max() == 16129 * 65536
 
 
+@pytest.mark.parametrize("path,M", [("fp8", 1), ("fp8", 33), ("decomp", 40), ("w8a16", 1), ("w8a16", 16),
+                                    ("grouped128", 1), ("grouped64", 16), ("grouped128", 40), ("static", 33)])
+def test_other_paths_at_max_k(path, M):
+    """Every other product at K = 65536, the largest accepted (16 K segments
+    of the decode kernels, 1024 stages of the GEMM main loops, 512 or 1024
+    weight groups)."""
+    K, N = 65536, 64
+    log(f"[max K] {path} M={M} N={N} K={K}")
+    w = inputs.random_matrix(90 + M, (N, K), 0.02, torch.float32)
+    if path == "fp8":
+        run_fp8_case(inputs.random_matrix(91 + M, (M, K), 1.0, torch.bfloat16), w, 1200.0, what=f"fp8 K={K}")
+    elif path == "decomp":
+        d = inputs.llm_int8_outliers(seed=92, M=M, K=K, N=N, n_outlier_cols=5)
+        run_decomp_case(d.x, d.w, 6.0, what=f"decomp K={K}")
+    elif path == "w8a16":
+        run_w8a16_case(inputs.random_matrix(93 + M, (M, K), 1.0, torch.bfloat16), w, torch.bfloat16,
+                       what=f"w8a16 K={K}")
+    elif path == "static":
+        run_static_case(inputs.random_matrix(94 + M, (M, K), 1.0, torch.bfloat16), w, 0.02, what=f"static K={K}")
+    else:
+        group = int(path[len("grouped"):])
+        run_grouped_linear_case(inputs.random_matrix(95 + M, (M, K), 1.0, torch.bfloat16), w, group,
+                                torch.bfloat16, what=f"grouped g{group} K={K}")
+
+
 def test_linear_max_weight_elements_sampled():
     """A weight matrix of N * K = 32767 * 65536 = 2^31 - 65536 elements, just
     under the 2^31 limit of the 32-bit offsets (2 GB of int8 codes), through
