@@ -10,7 +10,9 @@
 //   k_quant_weight_grouped  one workgroup per row; the g/E lanes holding a
 //                           group's 16-byte chunks take its min / max by
 //                           lane shuffles, then every lane codes its chunk
-//   k_gemv_group            decode (M <= 16): the on-codes decode layout
+//   k_gemv_group            decode, 11 <= M <= 16 (up to 10 tokens the fused
+//                           decode kernel has a per-group mode): the on-codes
+//                           decode layout
 //                           (16 weight rows per workgroup, 4 waves splitting
 //                           K, DMA of weight and code rows into LDS,
 //                           v_mfma_i32_16x16x64_i8); after each group the
@@ -24,9 +26,11 @@
 //                           by group: the fold of one group (convert, fma
 //                           with its scale into fp32) is interleaved with the
 //                           MFMAs of the next.  The zero-point term
-//                           -Sum_j S Z gsum is a rank-(K/g) fp32 product,
-//                           computed first with v_mfma_f32_32x32x2_f32 into
-//                           the fp32 accumulators.
+//                           -Sum_j S Z gsum is a rank-(K/g) fp32 product: one
+//                           v_mfma_f32_32x32x2_f32 per pair of groups in the
+//                           main loop, into the fp32 accumulators.  A group's
+//                           S, Z and code sums for the whole tile come into
+//                           LDS once, one 256-byte DMA per wave.
 #include "q8_device.hpp"
 #include "q8_group.hpp"
 
