@@ -772,6 +772,45 @@ def test_linear_max_weight_elements_sampled():
     torch.cuda.empty_cache()
 
 
+# ---------------------------------------------------------------- pointer validation
+_VALIDATE_CHILD = '''
+import torch
+from w8a8_quantized_linear_channel_amd import _lib, ops as q8
+dev = "cuda:0"
+w = torch.randn(64, 64, device=dev)
+wq, ws, wz = q8.q8_quantize_weight(w, "int8_asym")
+x = torch.randn(4, 64, device=dev, dtype=torch.bfloat16)
+y = torch.empty(4, 64, device=dev, dtype=torch.bfloat16)
+xh = x.cpu().pin_memory()   # pinned: device-readable, so even an unchecked launch could not fault
+L = _lib.lib()
+st = torch.cuda.current_stream().cuda_stream
+host_x = L.q8_linear(xh.data_ptr(), _lib.Q8_BF16, 4, 64, wq.data_ptr(), ws.data_ptr(), wz.data_ptr(), 64,
+                     None, y.data_ptr(), _lib.Q8_BF16, None, 0, None, st)
+dev_x = L.q8_linear(x.data_ptr(), _lib.Q8_BF16, 4, 64, wq.data_ptr(), ws.data_ptr(), wz.data_ptr(), 64,
+                    None, y.data_ptr(), _lib.Q8_BF16, None, 0, None, st)
+torch.cuda.synchronize()
+print(host_x, dev_x, flush=True)
+'''
+
+
+def test_debug_pointer_validation():
+    """With Q8_DEBUG_VALIDATE=1 every pointer is checked to be device memory
+    of the stream's device: a (pinned) host buffer is Q8_ERR_BAD_ARG before
+    any launch, device buffers pass.  Run in a child process (the switch is
+    read once per process)."""
+    import os
+    import subprocess
+    import sys
+    log("[validate] Q8_DEBUG_VALIDATE=1: host pointer rejected, device pointers accepted")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, Q8_DEBUG_VALIDATE="1", PYTHONPATH=root)
+    r = subprocess.run([sys.executable, "-c", _VALIDATE_CHILD], env=env, cwd=root, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    host_st, dev_st = map(int, r.stdout.split()[-2:])
+    assert host_st == 5 and dev_st == 0, r.stdout
+
+
 # ---------------------------------------------------------------- empty batch
 def test_empty_batch_every_entry_point():
     """An empty batch (M = 0 tokens) gives empty outputs from every call
