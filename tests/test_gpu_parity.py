@@ -226,6 +226,21 @@ def test_linear_tiny_config():
     run_linear_case(wl.x, wl.w, torch.float32, what="tiny")
 
 
+def test_linear_every_small_m():
+    """M = 1 .. 17 one by one, across the three dispatch regimes (fused decode
+    up to 10 tokens, the GEMV on codes for 11 .. 16, the GEMM from 17), on a
+    ragged shape: N = 40 (not a multiple of 16 or 32), K = 272 (not a multiple
+    of 64), and on the per-group path with K = 384 (three groups of 128)."""
+    log("[linear] every M in 1..17, N=40 K=272; per-group N=40 K=384")
+    w = inputs.random_matrix(180, (40, 272), 0.02, torch.float32)
+    wg = inputs.random_matrix(181, (40, 384), 0.02, torch.float32)
+    for M in range(1, 18):
+        x = inputs.random_matrix(182 + M, (M, 272), 1.0, torch.bfloat16)
+        run_linear_case(x, w, torch.bfloat16, what=f"M={M}")
+        xg = inputs.random_matrix(200 + M, (M, 384), 1.0, torch.bfloat16)
+        run_grouped_linear_case(xg, wg, 128, torch.float32, what=f"grouped M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
 def test_linear_decode_qproj_full_size(M):
     log(f"[linear] decode q_proj M={M} N=K=4096 bf16")
