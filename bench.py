@@ -472,7 +472,7 @@ def main():
     args = ap.parse_args()
     set_warm_ms(args.warm_ms)
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
