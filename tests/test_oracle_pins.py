@@ -685,3 +685,50 @@ def test_grouped_linear_brute_force():
                 ref += Fraction(float(S[k // g, n])) * (int(q[n, k]) - int(Z[k // g, n])) * int(xq[m, k])
             ref *= Fraction(float(xs[m]))
             assert abs(y[m, n] - float(ref)) <= 1e-13 * max(abs(float(ref)), 1e-30)
+
+
+# ----------------------------------------------------------------- property tests over arbitrary rows
+from hypothesis import given, settings, strategies as st  # noqa: E402
+from hypothesis.extra.numpy import arrays  # noqa: E402
+
+# finite binary32 rows whose range stays well inside the normal numbers, so that
+# S = (hi - lo)/255 and the quotients w/S are ordinary binary32 values
+_rows = arrays(np.float32, st.tuples(st.integers(1, 6), st.integers(1, 40)),
+               elements=st.floats(-1e4, 1e4, width=32, allow_nan=False, allow_infinity=False))
+
+
+@settings(max_examples=300, deadline=None)
+@given(_rows)
+def test_property_asym_weight_quant(w):
+    """O2 on arbitrary rows: codes and zero points in [-128, 127], Z an
+    integer, zero exactly representable (0 maps to the code Z and back to 0),
+    and every weight within half a step (plus binary32 slack) of its
+    dequantized value, since the widened range [lo, hi] contains the row."""
+    q, s, z = O.quantize_weight_int8_asym(w)
+    assert q.dtype == np.int8 and np.all(z == np.rint(z)) and np.all((z >= -128) & (z <= 127))
+    assert np.all(s > 0)
+    zeros = (w == 0)
+    assert np.all(q[zeros] == np.broadcast_to(z[:, None], w.shape)[zeros])
+    r = O.dequantize_weight_int8(q, s, z)
+    assert np.all(r[zeros] == 0)
+    big = s.astype(np.float64) > 1e-7        # rows not held at the scale floor
+    err = np.abs(w.astype(np.float64) - r)
+    slack = s.astype(np.float64)[:, None] * (0.5 + 1e-4) + 1e-30
+    assert np.all(err[big] <= slack[big])
+
+
+@settings(max_examples=300, deadline=None)
+@given(_rows)
+def test_property_sym_act_quant(x):
+    """O3 on arbitrary rows: |q| <= 127, the row's largest magnitude codes to
+    +-127 (unless the row is held at the scale floor), every value within half
+    a step of S q, and the row sum is the exact sum of the codes."""
+    q, s, rs = O.quantize_act_int8_sym(x)
+    qi = q.astype(np.int64)
+    assert np.all(np.abs(qi) <= 127)
+    assert np.array_equal(rs.astype(np.int64), qi.sum(axis=1))
+    amax = np.abs(x).max(axis=1)
+    live = amax / 127 >= 1e-8
+    assert np.all(np.abs(qi).max(axis=1)[live] == 127)
+    err = np.abs(x.astype(np.float64) - s.astype(np.float64)[:, None] * qi)
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 1e-4))
