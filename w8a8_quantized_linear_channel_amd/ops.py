@@ -18,6 +18,17 @@ _OP = {"linear": _lib.Q8_OP_LINEAR, "decomp": _lib.Q8_OP_DECOMP, "fp8": _lib.Q8_
        "static": _lib.Q8_OP_STATIC, "grouped": _lib.Q8_OP_GROUPED}
 
 
+class _DtypeCodes(dict):
+    """torch dtype -> q8_dtype code; an unsupported dtype is a TypeError that
+    names the supported ones."""
+
+    def __missing__(self, key):
+        raise TypeError(f"unsupported dtype {key}: expected torch.float32, torch.float16 or torch.bfloat16")
+
+
+_DT = _DtypeCodes(_DT)
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
