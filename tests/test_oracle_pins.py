@@ -732,3 +732,23 @@ def test_property_sym_act_quant(x):
     assert np.all(np.abs(qi).max(axis=1)[live] == 127)
     err = np.abs(x.astype(np.float64) - s.astype(np.float64)[:, None] * qi)
     assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 1e-4))
+
+
+@settings(max_examples=300, deadline=None)
+@given(_rows, st.sampled_from([None, 1200.0, 3.0]))
+def test_property_fp8_rowwise_quant(x, ub):
+    """O8 on arbitrary rows, with and without a binding bound: every code is a
+    finite e4m3 value within 448; x/S inside the range lands within half an
+    e4m3 spacing of dec(q) (spacing 2^(e-3) in the binade [2^e, 2^(e+1)),
+    2^-9 below 2^-6); values past the bound saturate at +-448 with their sign."""
+    q, s = O.quantize_fp8_rowwise(x, ub)
+    d = O.e4m3_decode(q)
+    assert np.all(np.isfinite(d)) and np.all(np.abs(d) <= 448)
+    r = x.astype(np.float64) / s.astype(np.float64)[:, None]
+    inside = np.abs(r) <= 448 * (1 - 2.0 ** -20)
+    a = np.abs(r[inside])
+    e = np.maximum(np.floor(np.log2(np.maximum(a, 2.0 ** -30))), -6)
+    half = np.exp2(e - 3) / 2 * (1 + 1e-6)
+    assert np.all(np.abs(r[inside] - d[inside]) <= half + 2.0 ** -24 * a)
+    out = np.abs(r) > 448 * (1 + 2.0 ** -20)
+    assert np.all(np.abs(d[out]) == 448) and np.all(np.sign(d[out]) == np.sign(r[out]))
