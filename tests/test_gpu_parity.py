@@ -683,7 +683,9 @@ def test_linear_grouped_decode_qproj_full_size(M, group):
                                             (300, 520, 1024, 64, torch.bfloat16),  # GEMM: ragged M and N
                                             (1000, 3000, 256, 128, torch.float16), # GEMM: few groups
                                             (130, 4100, 4224, 128, torch.float32), # GEMM: odd group count
-                                            (257, 300, 192, 64, torch.bfloat16)])  # GEMM: 3 stages, 3 groups
+                                            (257, 300, 192, 64, torch.bfloat16),   # GEMM: 3 stages, 3 groups
+                                            (40, 70, 64, 64, torch.bfloat16),      # GEMM: one stage, one group
+                                            (33, 130, 128, 64, torch.float16)])    # GEMM: two stages, two groups
 def test_linear_grouped_ragged(M, N, K, group, dt):
     log(f"[grouped] ragged M={M} N={N} K={K} group={group} {dt}")
     x = inputs.random_matrix(100 + M, (M, K), 1.0, dt)
