@@ -757,6 +757,21 @@ def test_other_paths_at_max_k(path, M):
                                 torch.bfloat16, what=f"grouped g{group} K={K}")
 
 
+@pytest.mark.parametrize("K", [16, 48])
+def test_short_k_every_gemm(K):
+    """K below one 64-byte stage: the GEMMs run no DMA stage at all, only the
+    register-loaded partial stage (int8, FP8 and LLM.int8 tiles, M above the
+    decode sizes), and the decode kernels a single partial k-step."""
+    log(f"[short K] K={K}: int8 GEMM, FP8 GEMM, LLM.int8, decode")
+    w = inputs.random_matrix(120 + K, (70, K), 0.02, torch.float32)
+    for M in (3, 13, 40, 300):
+        run_linear_case(inputs.random_matrix(121 + M, (M, K), 1.0, torch.bfloat16), w, torch.bfloat16,
+                        what=f"int8 K={K} M={M}")
+    run_fp8_case(inputs.random_matrix(125, (300, K), 1.0, torch.bfloat16), w, 1200.0, what=f"fp8 K={K}")
+    d = inputs.llm_int8_outliers(seed=126, M=300, K=K, N=70, n_outlier_cols=2)
+    run_decomp_case(d.x, d.w, 6.0, what=f"decomp K={K}")
+
+
 def test_linear_max_weight_elements_sampled():
     """A weight matrix of N * K = 32767 * 65536 = 2^31 - 65536 elements, just
     under the 2^31 limit of the 32-bit offsets (2 GB of int8 codes), through
