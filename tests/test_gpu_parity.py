@@ -770,6 +770,10 @@ def test_short_k_every_gemm(K):
     run_fp8_case(inputs.random_matrix(125, (300, K), 1.0, torch.bfloat16), w, 1200.0, what=f"fp8 K={K}")
     d = inputs.llm_int8_outliers(seed=126, M=300, K=K, N=70, n_outlier_cols=2)
     run_decomp_case(d.x, d.w, 6.0, what=f"decomp K={K}")
+    for M in (1, 16):
+        run_w8a16_case(inputs.random_matrix(127 + M, (M, K), 1.0, torch.bfloat16), w, torch.bfloat16,
+                       what=f"w8a16 K={K} M={M}")
+    run_static_case(inputs.random_matrix(129, (300, K), 1.0, torch.bfloat16), w, 0.02, what=f"static K={K}")
 
 
 def test_linear_max_weight_elements_sampled():
@@ -841,6 +845,58 @@ def test_debug_pointer_validation():
     assert r.returncode == 0, r.stderr[-2000:]
     host_st, dev_st = map(int, r.stdout.split()[-2:])
     assert host_st == 5 and dev_st == 0, r.stdout
+
+
+# ---------------------------------------------------------------- concurrent streams
+def test_calls_on_two_streams_run_concurrently():
+    """The library keeps no state between calls, so calls enqueued on two
+    streams at once (each with its own workspace) give the same bits as the
+    same calls run one after the other."""
+    log("[streams] q8_linear, LLM.int8 and FP8 interleaved on two streams")
+    w = g(inputs.random_matrix(140, (512, 1024), 0.02, torch.float32))
+    wq, ws, wz = q8.q8_quantize_weight(w, "int8_asym")
+    fq, fs = q8.q8_quantize_weight(w, "fp8_e4m3")[:2]
+    d = inputs.llm_int8_outliers(seed=141, M=96, K=1024, N=512, n_outlier_cols=4)
+    dq, ds, dz = q8.q8_quantize_weight(g(d.w), "int8_asym")
+    xd = g(d.x)
+    xs = [g(inputs.random_matrix(142 + i, (M, 1024), 1.0, torch.bfloat16)) for i, M in enumerate((1, 16, 700, 300))]
+
+    def calls(i):
+        x = xs[i]
+        M = x.shape[0]
+        y = torch.empty(M, 512, dtype=torch.bfloat16, device=DEV)
+        wl = torch.empty(max(1, q8.q8_workspace_bytes("linear", M, 512, 1024)), dtype=torch.uint8, device=DEV)
+        yf = torch.empty(M, 512, dtype=torch.bfloat16, device=DEV)
+        wf = torch.empty(max(1, q8.q8_workspace_bytes("fp8", M, 512, 1024)), dtype=torch.uint8, device=DEV)
+        yd = torch.empty(96, 512, dtype=torch.float16, device=DEV)
+        wd = torch.empty(q8.q8_workspace_bytes("decomp", 96, 512, 1024), dtype=torch.uint8, device=DEV)
+
+        def run():
+            q8.q8_linear(x, wq, ws, wz, out=y, workspace=wl)
+            q8.q8_linear_fp8(x, fq, fs, out=yf, workspace=wf)
+            q8.q8_linear_int8_decomp(xd, dq, ds, dz, 6.0, out=yd, workspace=wd)
+        return run, (y, yf, yd)
+
+    jobs = [calls(i) for i in range(len(xs))]
+    ref = []
+    for run, outs in jobs:
+        run()
+        torch.cuda.synchronize()
+        ref.append([o.clone() for o in outs])
+        for o in outs:
+            o.fill_(0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for i, (run, _) in enumerate(jobs):
+            with torch.cuda.stream(streams[i % 2]):
+                run()
+        torch.cuda.synchronize()
+        for i, (_, outs) in enumerate(jobs):
+            for o, r in zip(outs, ref[i]):
+                assert torch.equal(o.view(torch.int16), r.view(torch.int16)), f"rep {rep}, job {i} differs"
+                o.fill_(0)
+        torch.cuda.synchronize()
 
 
 # ---------------------------------------------------------------- empty batch
