@@ -752,3 +752,152 @@ def test_property_fp8_rowwise_quant(x, ub):
     assert np.all(np.abs(r[inside] - d[inside]) <= half + 2.0 ** -24 * a)
     out = np.abs(r) > 448 * (1 + 2.0 ** -20)
     assert np.all(np.abs(d[out]) == 448) and np.all(np.sign(d[out]) == np.sign(r[out]))
+
+
+# ---------------------------------------------------------------- rounding of the outlier weights; bias placement
+def round_binary(fr: Fraction, p: int, emin: int) -> Fraction:
+    """Exact rational -> nearest value of a binary format with p significand
+    bits and smallest normal exponent emin, ties to even (subnormals
+    included).  Written from the IEEE 754 definition; binary32 is (24, -126),
+    binary16 is (11, -14)."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    ulp = Fraction(2) ** (e - (p - 1))
+    n = a / ulp
+    lo = math.floor(n)
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * ulp
+
+
+def test_outlier_weights_round_through_binary32_then_binary16():
+    """W_O = fp16(fp32(S (q - Z))): the dequantized weight is a binary32 value
+    first (the int8 weights are dequantized to fp32), then cast to fp16 for the
+    16-bit outlier product ([BNB] core idea: the outlier columns go through
+    fp16).  The cases are scales and code differences where the exact product
+    lies next to an fp16 tie and its binary32 rounding lands on the tie, so
+    one rounding of the exact product to fp16 gives the neighbouring value."""
+    cases = [  # (bits of S, q, Z)
+        (976103014, -118, -128),    # q - Z = 10
+        (974503705, 85, -128),      # 213
+        (970297745, -51, 0),        # -51
+        (975054530, 123, -128),     # 251
+        (981643349, 113, -128),     # 241
+        (973245523, 7, -128),       # 135
+    ]
+    N = len(cases)
+    wq = np.zeros((N, 4), np.int8)
+    ws = np.zeros(N, np.float32)
+    wz = np.zeros(N, np.float32)
+    for n, (bits, q, z) in enumerate(cases):
+        ws[n] = np.array([bits], np.uint32).view(np.float32)[0]
+        wq[n, 2] = q
+        wz[n] = z
+    w_o = O.outlier_weights_f16(wq, ws, wz, np.array([2]))
+    assert w_o.dtype == np.float16 and w_o.shape == (N, 1)
+    for n, (_, q, z) in enumerate(cases):
+        exact = Fraction(float(ws[n])) * (q - z)
+        two = round_binary(round_binary(exact, 24, -126), 11, -14)
+        one = round_binary(exact, 11, -14)
+        assert two != one                       # the case separates the two readings
+        assert Fraction(float(w_o[n, 0])) == two
+
+
+def _e4m3_rows_with_scale(rng, R, K, scale_pow2):
+    """Rows on the e4m3 grid times 2^scale_pow2, each with absmax 448 * 2^p, so
+    the rowwise FP8 quantizer returns S = 2^p and the codes of the grid values."""
+    codes = rng.integers(0, 0x7F, (R, K)).astype(np.uint8)        # finite, |v| < 448
+    codes[:, 0] = 0x7E                                              # 448
+    codes |= (rng.integers(0, 2, (R, K)) << 7).astype(np.uint8)   # random signs
+    return (O.e4m3_decode(codes) * 2.0 ** scale_pow2).astype(np.float32)
+
+
+def test_fp8_linear_bias_added_after_the_scales():
+    """[FB] §5.3: the rowwise FP8 product is scaled by both row scales, then the
+    fp32 bias is added.  With S_x = 2^-3 and S_w = 2^-5 (rows on the e4m3 grid)
+    the layer is the exact product X W^T plus b; a bias added before the scales
+    would come out multiplied by 2^-8."""
+    rng = np.random.default_rng(90)
+    x = _e4m3_rows_with_scale(rng, 3, 32, -3)
+    w = _e4m3_rows_with_scale(rng, 4, 32, -5)
+    wq, ws = O.quantize_fp8_rowwise(w)
+    assert np.all(ws == np.float32(2.0 ** -5))
+    b = np.array([0.5, -1.25, 3.0, -7.5], np.float32)
+    y, inter = O.linear_fp8(x, wq, ws, scale_ub=1200.0, bias=b)
+    assert np.all(inter["x_scale"] == np.float32(2.0 ** -3))
+    ref = x.astype(np.float64) @ w.astype(np.float64).T + b.astype(np.float64)
+    np.testing.assert_array_equal(y, ref)
+
+
+def _asym_rows_eighth(rng, K):
+    """Weight rows on a 1/8 grid spanning exactly 255 steps: S = 1/8 with Z = 0
+    (range [-16, 15.875]) and Z = -64 (range [-8, 23.875])."""
+    a = rng.integers(-128, 128, K).astype(np.float32) / 8
+    a[0], a[1] = -16.0, 15.875
+    b = rng.integers(-64, 192, K).astype(np.float32) / 8
+    b[0], b[1] = -8.0, 23.875
+    return np.stack([a, b])
+
+
+def test_w8a16_bias_added_after_the_scale():
+    """y = X (S_w (Wq - Z_w))^T + b: with S_w = 1/8 (Z_w = 0 and -64) and small
+    integer activations the layer is the exact product plus b; a bias added
+    inside the scaled sum would come out multiplied by 1/8."""
+    rng = np.random.default_rng(91)
+    K = 40
+    w = _asym_rows_eighth(rng, K)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    assert np.all(ws == np.float32(0.125)) and wz.tolist() == [0.0, -64.0]
+    x = rng.integers(-20, 21, (3, K)).astype(np.float32)
+    b = np.array([0.75, -2.5], np.float32)
+    y = O.linear_w8a16(torch.from_numpy(x).to(torch.bfloat16), wq, ws, wz, bias=b)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T + b.astype(np.float64)
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_decomp_bias_added_once_after_both_flows():
+    """LLM.int8 with a bias: the regular columns (|x| < 6, row absmax 127/32, so
+    S_x = 1/32) go through the int8 flow, two outlier columns (|x| >= 6)
+    through the fp16 flow, and S_w = 1/8 makes every dequantized weight exact
+    in fp16.  The layer is then the exact product X W^T plus b; a bias inside
+    either flow's scaling, or added twice, fails."""
+    rng = np.random.default_rng(92)
+    K = 48
+    w = _asym_rows_eighth(rng, K)
+    wq, ws, wz = O.quantize_weight_int8_asym(w)
+    M = 4
+    x = rng.integers(-127, 128, (M, K)).astype(np.float32) / 32
+    x[:, 5] = 127 / 32
+    x[:, [9, 30]] = np.array([[8.0, -20.5], [-6.0, 12.25], [7.5, 60.0], [-9.0, 6.0]], np.float32)
+    xh = x.astype(np.float16)
+    assert np.array_equal(xh.astype(np.float32), x)
+    b = np.array([1.5, -0.375], np.float32)
+    y, inter = O.linear_int8_decomp(xh, wq, ws, wz, tau=6.0, bias=b)
+    assert inter["cols"].tolist() == [9, 30]
+    assert np.all(inter["x_scale"] == np.float32(1 / 32))
+    ref = x.astype(np.float64) @ w.astype(np.float64).T + b.astype(np.float64)
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_max_rel_err_accumulation_floor():
+    """The optional floor abs_dot_frac * A_i of the FP8 comparison, worked by
+    hand: ref = [100, 1, 0.5], A = [100, 200, 1], frac 1/64 -> denominators
+    max(|ref|, 0.1, A/64) = [100, 3.125, 0.5]."""
+    ref = np.array([100.0, 1.0, 0.5])
+    a = np.array([100.0, 200.0, 1.0])
+    y = ref + np.array([0.0, 0.3125, 0.0])
+    assert abs(O.max_rel_err(y, ref) - 0.3125) < 1e-12                       # den 1
+    assert abs(O.max_rel_err(y, ref, abs_dot=a, abs_dot_frac=1 / 64) - 0.1) < 1e-12   # den 3.125
+    y = ref + np.array([0.0, 0.0, 0.01])                                      # A/64 < |ref| here
+    assert abs(O.max_rel_err(y, ref, abs_dot=a, abs_dot_frac=1 / 64) - 0.02) < 1e-12
+    y = ref + np.array([2.0, 0.0, 0.0])                                       # |ref| = A/64 * 64
+    assert abs(O.max_rel_err(y, ref, abs_dot=a, abs_dot_frac=1 / 64) - 0.02) < 1e-12
