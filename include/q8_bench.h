@@ -1,8 +1,11 @@
 /*
- * Measurement helper of libq8, outside the quantized layer itself: a
- * register-only MFMA loop that gives the matrix-core rate the chip sustains
- * with no memory traffic (the measured compute ceiling set beside the
- * published peak when the GEMM kernels are timed).
+ * Measurement helpers of libq8, outside the quantized layer itself:
+ * - a register-only MFMA loop that gives the matrix-core rate the chip
+ *   sustains with no memory traffic (the measured compute ceiling set beside
+ *   the published peak when the GEMM kernels are timed);
+ * - a probe that runs the FP8 GEMM's matrix instruction once on given
+ *   operands, so that the rounding of its internal sum can be measured
+ *   against exact sums (the FP8 parity tolerance rests on it).
  */
 #ifndef Q8_BENCH_H
 #define Q8_BENCH_H
@@ -27,6 +30,24 @@ extern "C" {
  */
 q8_status q8_bench_mfma_loop(q8_format fmt, int64_t iters, int64_t workgroups, int32_t* sink,
                              void* stream);
+
+/*
+ * q8_probe_fp8_mfma -- for each of `count` independent problems p, one wave
+ * runs one v_mfma_f32_32x32x64_f8f6f4 on e4m3 operands (the instruction and
+ * operand layout of the FP8 GEMM's main loop: the scaled form with zero scale
+ * operands, which the compiler emits as this unscaled instruction)
+ *     d[p][i][j] = c[p][i][j] + sum_{k<64} e4m3(a[p][i][k]) e4m3(b[p][j][k])
+ * a, b: uint8 e4m3fn codes [count, 32, 64] (row-major, k contiguous); c, d:
+ * float [count, 32, 32] (row-major).  The page's FP8 GEMM runs with fast
+ * accumulation ("Transformers FP8 (W8A8) 量化实战…" §5.3,
+ * use_fast_accum=True): the instruction's own sum is not exact, and this
+ * probe is how its error is measured.  Device memory, caller-owned, 16-byte
+ * aligned; asynchronous on `stream`.  Errors: Q8_ERR_BAD_ARG unless
+ * 1 <= count <= 65536; Q8_ERR_NULL_PTR, Q8_ERR_ALIGN, Q8_ERR_DEVICE as for
+ * every call.
+ */
+q8_status q8_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d,
+                            int64_t count, void* stream);
 
 #ifdef __cplusplus
 }

@@ -301,6 +301,15 @@ def test_bench_mfma_loop_validation():
     assert f(E.Q8_INT8_SYM, 10, 8, MIS, None) == 6
 
 
+def test_probe_fp8_mfma_validation():
+    f = _lib.lib().q8_probe_fp8_mfma
+    assert f(P, P, P, P2, 0, None) == 5
+    assert f(P, P, P, P2, 65537, None) == 5
+    assert f(None, P, P, P2, 1, None) == 1
+    assert f(P, P, P, None, 1, None) == 1
+    assert f(P, MIS, P, P2, 1, None) == 6
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """No fallback: without libq8.so every call raises (there is no CPU path)."""
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libq8.so"))

@@ -12,6 +12,8 @@ from oracle import q8_oracle as O
 from w8a8_quantized_linear_channel_amd import inputs
 from w8a8_quantized_linear_channel_amd import ops as q8
 
+import fp8_accum as F
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = 1e-2
@@ -47,22 +49,44 @@ def out_f64(y):
     return y.detach().float().cpu().numpy().astype(np.float64)
 
 
-# The FP8 MFMA of gfx950 (v_mfma_f32_16x16x128_f8f6f4) does not sum its
-# products exactly in fp32: a register-level probe of single instructions
-# measured errors up to 7.8e-5 of sum_k |x_k w_k| (the same for the older
-# 16x16x32 fp8 instruction), where an fp32 sum of the exact products stays
-# near 2e-8.  FP8 outputs are therefore compared with the relative error
-# floored at A/64, A = S_x S_w sum_k |x_k w_k|: the 1e-2 gate then admits an
-# absolute error of 1.6e-4 A, twice the measured per-instruction worst case.
-FP8_ABS_DOT_FRAC = 1.0 / 64
-
-
-def check_close(y_gpu, y_ref, what, abs_dot=None):
-    err = O.max_rel_err(y_gpu, y_ref, abs_dot=abs_dot,
-                        abs_dot_frac=FP8_ABS_DOT_FRAC if abs_dot is not None else 0.0)
-    plain = O.max_rel_err(y_gpu, y_ref)
-    log(f"  {what}: max rel err {err:.3e} (without the accumulation floor {plain:.3e})")
+def check_close(y_gpu, y_ref, what):
+    err = O.max_rel_err(y_gpu, y_ref)
+    log(f"  {what}: max rel err {err:.3e}")
     assert err <= TOL, (what, err)
+
+
+# The FP8 GEMM runs with the fast accumulation of the page's FP8 GEMM
+# ("Transformers FP8 (W8A8) 量化实战…" §5.3, use_fast_accum=True): its matrix
+# instruction cuts each product 13 bits below the largest of its group of
+# eight (tests/fp8_accum.py, pinned on the instruction by
+# test_gpu_fp8_accum.py).  An FP8 output passes if its error is within the
+# 1e-2 relative tolerance, or within that tolerance plus the bound B that the
+# instruction's cuts and the chain's binary32 roundings can add to the exact
+# sum (fp8_accum.gemm_bound, computed from the oracle's codes).
+def check_close_fp8(y_gpu, y_ref, x_rows, w, ub, what):
+    """y_gpu, y_ref [R, N] for the activation rows x_rows [R, K] (input
+    values) and weights w [N, K] (input values)."""
+    y_gpu = np.asarray(y_gpu, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    if y_ref.size == 0:
+        return
+    plain = O.max_rel_err(y_gpu, y_ref)
+    den = np.maximum(np.abs(y_ref), 1e-3 * np.abs(y_ref).max())
+    err = np.abs(y_gpu - y_ref)
+    over = np.argwhere(err > TOL * den)
+    worst = 0.0
+    if over.size:
+        xq, xs = O.quantize_fp8_rowwise(x_rows, ub)
+        wq, wsc = O.quantize_fp8_rowwise(w)
+        xv, wv = O.e4m3_decode(xq), O.e4m3_decode(wq)
+        for r in np.unique(over[:, 0]):
+            cols = over[over[:, 0] == r][:, 1]
+            b = F.gemm_bound(xv[r:r + 1], xs[r:r + 1], wv[cols], wsc[cols])[0]
+            excess = err[r, cols] - TOL * den[r, cols]
+            assert np.all(excess <= b), (what, int(r), int(cols[np.argmax(excess - b)]))
+            worst = max(worst, float(np.max(excess / b)))
+    log(f"  {what}: max rel err {plain:.3e}; {len(over)} of {y_ref.size} outputs beyond 1e-2, "
+        f"their excess at most {worst:.3f} of the fast-accumulation bound")
 
 
 def sample_rows(M, n=12, seed=0, extra=()):
@@ -401,9 +425,8 @@ def run_fp8_case(x, w, ub, rows=None, bias=None, what=""):
     assert_equal(host(wq), rq, f"{what} weight codes")
     xr = x if rows is None else x[rows]
     y_ref, _ = O.linear_fp8(xr, rq, rs, ub, bias)
-    a = O.fp8_abs_dot(xr, rq, rs, ub)
     y_g = out_f64(y) if rows is None else out_f64(y)[rows]
-    check_close(y_g, y_ref, f"{what} output", abs_dot=a)
+    check_close_fp8(y_g, y_ref, xr, w, ub, f"{what} output")
     # the two-step form (quantize, then the rowwise GEMM) gives the same bits
     xq, xs, _ = q8.q8_quantize_act(g(x), "fp8_e4m3", scale_ub=ub)
     y2 = q8.q8_gemm_fp8(xq, xs, wq, ws, bias=b)
@@ -559,7 +582,7 @@ def run_grouped_case(x, w, offsets, rows_per_expert=None, ub=1200.0, what=""):
     rq, rs = O.quantize_fp8_rowwise(w.reshape(E * N, K))
     rq, rs = rq.reshape(E, N, K), rs.reshape(E, N)
     y_g = out_f64(y)
-    rows, ref, a = [], [], []
+    rows = []
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
@@ -568,14 +591,12 @@ def run_grouped_case(x, w, offsets, rows_per_expert=None, ub=1200.0, what=""):
             np.unique(np.r_[lo, hi - 1, np.random.default_rng(e).integers(lo, hi, rows_per_expert)])
         yr, _ = O.linear_fp8(x[r], rq[e], rs[e], ub)
         rows.append(r)
-        ref.append(yr)
-        a.append(O.fp8_abs_dot(x[r], rq[e], rs[e], ub))
+        check_close_fp8(y_g[r], yr, x[r], w[e], ub, f"{what} expert {e} output ({len(r)} rows)")
         if hi - lo <= 600:
             # the same rows through the plain rowwise FP8 path give the same bits
             y1 = q8.q8_linear_fp8(g(x[lo:hi]), wq[e].contiguous(), ws[e].contiguous(), scale_ub=ub)
             assert torch.equal(y[lo:hi].view(torch.int16), y1.view(torch.int16)), f"{what}: expert {e} differs"
-    rows = np.concatenate(rows)
-    check_close(y_g[rows], np.concatenate(ref), f"{what} output ({len(rows)} rows)", abs_dot=np.concatenate(a))
+    assert sum(len(r) for r in rows) > 0 or int(offsets[-1]) == 0
 
 
 def test_fp8_grouped_moe_full_size():

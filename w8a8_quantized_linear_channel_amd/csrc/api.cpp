@@ -569,6 +569,17 @@ q8_status q8_bench_mfma_loop(q8_format fmt, int64_t iters, int64_t workgroups, i
   return launched(q8::launch_mfma_loop(fmt == Q8_INT8_SYM ? 0 : 2, iters, workgroups, sink, st));
 }
 
+q8_status q8_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int64_t count,
+                            void* stream) {
+  if (count < 1 || count > 65536) return Q8_ERR_BAD_ARG;
+  if (!a || !b || !c || !d) return Q8_ERR_NULL_PTR;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c) || !aligned16(d)) return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {a, b, c, d}));
+  return launched(q8::launch_probe_fp8_mfma(a, b, c, d, count, st));
+}
+
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,
                       const float* w_scale, int64_t N, const float* bias, void* y, void* stream) {
   Q8_TRY(check_mnk(M, N, K));

@@ -44,7 +44,40 @@ __global__ __launch_bounds__(256) void k_mfma_loop(int iters, int* __restrict__ 
   sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// One FP8 MFMA per wave on operands from memory.  Lane l supplies row l % 32
+// of both operands, bytes 32 (l / 32) .. +31 of its 64 (the mapping the GEMM's
+// fragments use); output register r of lane l is row 8 (r / 4) + 4 (l / 32) +
+// r % 4, column l % 32 (the 32 x 32 MFMA output layout).
+__global__ __launch_bounds__(64) void k_probe_fp8(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                  const float* __restrict__ c, float* __restrict__ d) {
+  const int lane = threadIdx.x, p = blockIdx.x;
+  const int row = lane & 31, kh = lane >> 5;
+  const v4i* pa = (const v4i*)(a + (size_t)p * 2048 + row * 64 + kh * 32);
+  const v4i* pb = (const v4i*)(b + (size_t)p * 2048 + row * 64 + kh * 32);
+  const v4i a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+  const v8i fa = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  const v8i fb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  v16f acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 8 * (r >> 2) + 4 * kh + (r & 3);
+    acc[r] = c[(size_t)p * 1024 + i * 32 + row];
+  }
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = 8 * (r >> 2) + 4 * kh + (r & 3);
+    d[(size_t)p * 1024 + i * 32 + row] = acc[r];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int64_t count,
+                                 hipStream_t st) {
+  k_probe_fp8<<<(unsigned)count, 64, 0, st>>>(a, b, c, d);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_loop(int kind, int64_t iters, int64_t workgroups, int* sink, hipStream_t st) {
   if (kind == 0) k_mfma_loop<0><<<(unsigned)workgroups, 256, 0, st>>>((int)iters, sink);

@@ -371,3 +371,18 @@ def q8_bench_mfma_loop(fmt: str, iters: int, workgroups: int, sink: torch.Tensor
     _need(sink, "sink", torch.int32, (workgroups * 256,), dev)
     st = _lib.lib().q8_bench_mfma_loop(_FMT[fmt], iters, workgroups, _ptr(sink), _stream(dev))
     _lib.check("q8_bench_mfma_loop", st)
+
+
+def q8_probe_fp8_mfma(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor) -> torch.Tensor:
+    """Measurement helper (include/q8_bench.h): d = c + a . b^T through one
+    FP8 MFMA per problem.  a, b: uint8 e4m3 codes [P, 32, 64]; c: float32
+    [P, 32, 32]; returns d float32 [P, 32, 32]."""
+    dev = a.device
+    P = a.shape[0]
+    _need(a, "a", torch.uint8, (P, 32, 64), dev)
+    _need(b, "b", torch.uint8, (P, 32, 64), dev)
+    _need(c, "c", torch.float32, (P, 32, 32), dev)
+    d = torch.empty(P, 32, 32, dtype=torch.float32, device=dev)
+    st = _lib.lib().q8_probe_fp8_mfma(_ptr(a), _ptr(b), _ptr(c), _ptr(d), P, _stream(dev))
+    _lib.check("q8_probe_fp8_mfma", st)
+    return d
