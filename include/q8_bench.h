@@ -5,7 +5,9 @@
  *   the published peak when the GEMM kernels are timed);
  * - a probe that runs the FP8 GEMM's matrix instruction once on given
  *   operands, so that the rounding of its internal sum can be measured
- *   against exact sums (the FP8 parity tolerance rests on it).
+ *   against exact sums (the FP8 parity tolerance rests on it);
+ * - a query of the GEMM tile a call picks for a shape, so that tests can
+ *   show which kernel instantiation a shape exercises.
  */
 #ifndef Q8_BENCH_H
 #define Q8_BENCH_H
@@ -48,6 +50,19 @@ q8_status q8_bench_mfma_loop(q8_format fmt, int64_t iters, int64_t workgroups, i
  */
 q8_status q8_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d,
                             int64_t count, void* stream);
+
+/*
+ * q8_gemm_tile -- the output tile (rows x columns of Y per workgroup) of the
+ * MFMA GEMM that a call of `op` runs for M activation rows and N output
+ * features: *bm x *bn is 256 x 256, 128 x 128, 64 x 128 or 64 x 64.  Writes
+ * 0 x 0 where no GEMM runs (Q8_OP_LINEAR and Q8_OP_STATIC up to 16 rows,
+ * which take the streaming decode kernels, and M = 0).  Q8_OP_LINEAR is
+ * q8_linear / q8_gemm_int8, Q8_OP_STATIC q8_linear_static, Q8_OP_DECOMP
+ * q8_linear_int8_decomp, Q8_OP_FP8 q8_linear_fp8 / q8_gemm_fp8.  Host only,
+ * nothing is launched.  Errors: Q8_ERR_BAD_ARG for another op;
+ * Q8_ERR_BAD_SHAPE for shapes the calls reject; Q8_ERR_NULL_PTR.
+ */
+q8_status q8_gemm_tile(q8_op op, int64_t M, int64_t N, int64_t K, int32_t* bm, int32_t* bn);
 
 #ifdef __cplusplus
 }

@@ -146,9 +146,17 @@ def quantize_act_int8_sym(x):
 # --------------------------------------------------------------------------
 def int_gemm(xq, wq) -> np.ndarray:
     """acc[m,n] = Sum_k xq[m,k] * wq[n,k], exact.  ([NOTE] "INT8 这么小的范围不会导致溢出吗？":
-    int8 x int8 products summed in an INT32 accumulator.)  Computed in int64 and
-    checked to fit int32."""
-    acc = xq.astype(np.int64) @ wq.astype(np.int64).T
+    int8 x int8 products summed in an INT32 accumulator.)
+
+    The matrix product is taken in float64 by the library routine: every
+    product and every partial sum, in whatever order the routine adds them,
+    is an integer of magnitude at most 128 * 128 * K, below 2^53 for any K up
+    to 2^39, so every float64 operation is exact and the result equals the
+    integer sum.  Returned as int64, checked to fit int32."""
+    xq = np.asarray(xq)
+    wq = np.asarray(wq)
+    assert 128 * 128 * xq.shape[1] < 2**53
+    acc = (xq.astype(np.float64) @ wq.astype(np.float64).T).astype(np.int64)
     assert acc.size == 0 or np.abs(acc).max() < 2**31
     return acc
 
@@ -430,7 +438,7 @@ def linear_int8_grouped(x, wq, S, Z, group: int, bias=None):
     t = np.zeros((M, N), dtype=np.float64)
     for j in range(G):
         cols = slice(j * group, (j + 1) * group)
-        acc = xq[:, cols].astype(np.int64) @ wq[:, cols].astype(np.int64).T
+        acc = int_gemm(xq[:, cols], wq[:, cols])
         c = acc - Z[j].astype(np.int64)[None, :] * gsum[j].astype(np.int64)[:, None]
         t += S[j].astype(np.float64)[None, :] * c.astype(np.float64)
     y = xs.astype(np.float64)[:, None] * t

@@ -310,6 +310,29 @@ def test_probe_fp8_mfma_validation():
     assert f(P, MIS, P, P2, 1, None) == 6
 
 
+def test_gemm_tile_query():
+    """The tile rule on the shapes the parity tests use for each tile (host
+    only: nothing is launched)."""
+    from w8a8_quantized_linear_channel_amd import ops
+    assert ops.q8_gemm_tile("linear", 2000, 6100, 208) == (256, 256)
+    assert ops.q8_gemm_tile("linear", 2048, 14336, 4096) == (256, 256)
+    assert ops.q8_gemm_tile("linear", 1000, 3000, 208) == (128, 128)
+    assert ops.q8_gemm_tile("linear", 500, 3000, 208) == (64, 128)
+    assert ops.q8_gemm_tile("linear", 512, 4096, 4096) == (64, 128)
+    assert ops.q8_gemm_tile("linear", 100, 500, 208) == (64, 64)
+    assert ops.q8_gemm_tile("linear", 16, 4096, 4096) == (0, 0)          # the decode kernels
+    assert ops.q8_gemm_tile("static", 17, 4096, 4096) == (64, 64)
+    assert ops.q8_gemm_tile("decomp", 2000, 6100, 208) == (128, 128)     # no 256 x 256 there
+    assert ops.q8_gemm_tile("decomp", 4, 64, 64) == (64, 64)
+    assert ops.q8_gemm_tile("fp8", 4096, 4096, 14336) == (256, 256)
+    assert ops.q8_gemm_tile("fp8", 1024, 4096, 4096) == (128, 128)
+    assert ops.q8_gemm_tile("fp8", 0, 4096, 4096) == (0, 0)
+    f = _lib.lib().q8_gemm_tile
+    assert f(_lib.Q8_OP_GROUPED, 100, 100, 64, P, P2) == 5
+    assert f(_lib.Q8_OP_LINEAR, 100, 100, 8, P, P2) == 2
+    assert f(_lib.Q8_OP_LINEAR, 100, 100, 64, None, P2) == 1
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """No fallback: without libq8.so every call raises (there is no CPU path)."""
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libq8.so"))

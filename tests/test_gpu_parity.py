@@ -295,23 +295,32 @@ def test_linear_decode_ragged(M, N, K, dt):
     run_linear_case(x, w, torch.float32, what="decode ragged")
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 64, 128),          # just above the decode path
-                                   (300, 520, 1040),       # 64x64 tiles, K tail of 16
-                                   (1000, 3000, 208),      # 128x128 tiles
-                                   (2040, 6200, 336)])     # 256x256 tiles, ragged M/N/K
-def test_linear_gemm_tiles(M, N, K):
-    log(f"[linear] GEMM M={M} N={N} K={K} bf16")
+# Shapes that the GEMM's tile rule sends to each tile (asserted through
+# q8_gemm_tile), with ragged M, N and K: every tile is compared on the whole
+# matrix (the whole INT32 accumulator and every output).
+GEMM_TILE_SHAPES = [((64, 64), 17, 64, 128),          # just above the decode path
+                    ((64, 64), 300, 520, 1040),       # K tail of 16
+                    ((64, 128), 500, 3000, 208),
+                    ((64, 128), 512, 4096, 4096),     # the LLM.int8 shape through the plain layer
+                    ((128, 128), 1000, 3000, 208),
+                    ((256, 256), 2040, 6200, 336)]
+
+
+@pytest.mark.parametrize("tile,M,N,K", GEMM_TILE_SHAPES)
+def test_linear_gemm_tiles(tile, M, N, K):
+    log(f"[linear] GEMM M={M} N={N} K={K} bf16, tile {tile}")
+    assert q8.q8_gemm_tile("linear", M, N, K) == tile
     x = inputs.random_matrix(50 + M, (M, K), 1.0, torch.bfloat16)
     w = inputs.random_matrix(60 + N, (N, K), 0.02, torch.float32)
-    rows = None if M * N * K <= 2e8 else sample_rows(M, 10, seed=M, extra=(255, 256, 127, 128, 63, 64))
-    run_linear_case(x, w, torch.bfloat16, rows=rows, what="gemm")
+    bias = inputs.random_matrix(61, (N,), 0.3, torch.float32)
+    run_linear_case(x, w, torch.bfloat16, bias=bias, what="gemm")
 
 
-def test_linear_prefill_full_size_sampled():
-    log("[linear] prefill FFN-up 2048x14336x4096 bf16, sampled rows")
+def test_linear_prefill_full_size():
+    log("[linear] prefill FFN-up 2048x14336x4096 bf16, whole matrix")
     wl = inputs.prefill_ffn_up()
-    rows = sample_rows(2048, 6, seed=7, extra=(255, 256, 1024))
-    y, acc = run_linear_case(wl.x, wl.w, torch.bfloat16, rows=rows, what="prefill")
+    assert q8.q8_gemm_tile("linear", 2048, 14336, 4096) == (256, 256)
+    y, acc = run_linear_case(wl.x, wl.w, torch.bfloat16, what="prefill")
     # determinism: a second call gives identical bits
     wq, ws, wz = q8.q8_quantize_weight(g(wl.w), "int8_asym")
     y2, acc2 = q8.q8_linear(g(wl.x), wq, ws, wz, out_dtype=torch.bfloat16, acc_out=True)
@@ -362,25 +371,25 @@ def run_decomp_case(x, w, tau, rows=None, bias=None, what=""):
 def test_decomp_llm_int8_full_size():
     log("[decomp] 512x4096x4096 fp16, 6 outlier columns, threshold 6.0")
     wl = inputs.llm_int8_outliers()
-    rows = sample_rows(512, 16, seed=3, extra=(63, 64, 127, 128))
-    run_decomp_case(wl.x, wl.w, 6.0, rows=rows, what="llm.int8")
+    run_decomp_case(wl.x, wl.w, 6.0, what="llm.int8")
     assert O.outlier_columns(wl.x, 6.0).tolist() == wl.extra["outlier_cols"].tolist()
 
 
-@pytest.mark.parametrize("M,N,K,seed", [(512, 4096, 4096, 31),   # the LLM.int8 shape, other seeds
-                                        (512, 4096, 8192, 32),   # two K segments of the outlier list
-                                        (300, 3000, 1024, 33),   # ragged M and N
-                                        (200, 1000, 512, 34)])
-def test_decomp_whole_accumulator(M, N, K, seed):
+@pytest.mark.parametrize("tile,M,N,K,seed", [((64, 128), 512, 4096, 4096, 31),   # the LLM.int8 shape, other seeds
+                                             ((64, 128), 512, 4096, 8192, 32),   # two K segments of the outlier list
+                                             ((128, 128), 1000, 3000, 208, 35),  # ragged
+                                             ((64, 64), 300, 3000, 1024, 33),    # ragged M and N
+                                             ((64, 64), 200, 1000, 512, 34)])
+def test_decomp_whole_accumulator(tile, M, N, K, seed):
     """Every tile: the whole INT32 accumulator against the exact product of
     the oracle's codes (a float64 matmul of integers below 2^53 is exact), the
     output on sampled rows, and a second call giving the same bits.  (Seed 31
     has an outlier weight S (q - Z) next to a tie of fp16, where a fused
     single-rounding conversion differs from the two roundings.)"""
-    log(f"[decomp] whole accumulator: M={M} N={N} K={K}")
+    log(f"[decomp] whole matrix: M={M} N={N} K={K}, tile {tile}")
+    assert q8.q8_gemm_tile("decomp", M, N, K) == tile
     wl = inputs.llm_int8_outliers(seed=seed, M=M, K=K, N=N, n_outlier_cols=5)
-    rows = sample_rows(M, 8, seed=seed, extra=(127, 128, 255, 256))
-    y = run_decomp_case(wl.x, wl.w, 6.0, rows=rows, what="whole")
+    y = run_decomp_case(wl.x, wl.w, 6.0, what="whole")
     wq, ws, wz = q8.q8_quantize_weight(g(wl.w), "int8_asym")
     y1, _, _, acc = q8.q8_linear_int8_decomp(g(wl.x), wq, ws, wz, threshold=6.0, return_outliers=True, acc_out=True)
     y2 = q8.q8_linear_int8_decomp(g(wl.x), wq, ws, wz, threshold=6.0)
@@ -432,6 +441,21 @@ def run_fp8_case(x, w, ub, rows=None, bias=None, what=""):
     y2 = q8.q8_gemm_fp8(xq, xs, wq, ws, bias=b)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"{what}: q8_gemm_fp8 differs"
     return y
+
+
+@pytest.mark.parametrize("tile,M,N,K", [((64, 64), 100, 500, 208),
+                                        ((64, 128), 500, 3000, 208),
+                                        ((128, 128), 1000, 3000, 208),
+                                        ((128, 128), 1024, 4096, 256),
+                                        ((256, 256), 2040, 6200, 336)])
+def test_fp8_gemm_tiles(tile, M, N, K):
+    """Every FP8 tile on the whole matrix, ragged M, N and K."""
+    log(f"[fp8] M={M} N={N} K={K}, tile {tile}")
+    assert q8.q8_gemm_tile("fp8", M, N, K) == tile
+    x = inputs.random_matrix(95 + M, (M, K), 1.0, torch.bfloat16)
+    w = inputs.random_matrix(96 + N, (N, K), 0.02, torch.float32)
+    bias = inputs.random_matrix(97, (N,), 0.1, torch.float32)
+    run_fp8_case(x, w, 1200.0, bias=bias, what="fp8 tile")
 
 
 @pytest.mark.parametrize("M,N,K", [(200, 300, 1040), (37, 1000, 128), (600, 2100, 256)])
@@ -537,8 +561,8 @@ def run_static_case(x, w, x_scale, rows=None, bias=None, clip_frac=0.2, what="")
     rq, rs, rz = oracle_weights(w)
     xr = x if rows is None else x[rows]
     _, inter = O.linear_static(xr, x_scale, rq, rs, rz, 1.0, bias=bias)
-    y_scale = float(np.float32(np.quantile(np.abs(inter["y"]), 1.0 - clip_frac) / 127.0))
-    yq_ref, _ = O.linear_static(xr, x_scale, rq, rs, rz, y_scale, bias=bias)
+    y_scale = float(np.float32(np.quantile(np.abs(inter["y"][::7]), 1.0 - clip_frac) / 127.0))
+    yq_ref = O.requantize_int8(inter["y"], y_scale)
     b = g(bias) if bias is not None else None
     yq = q8.q8_linear_static(g(x), x_scale, wq, ws, wz, y_scale, bias=b)
     got = host(yq) if rows is None else host(yq)[rows]
@@ -547,25 +571,25 @@ def run_static_case(x, w, x_scale, rows=None, bias=None, clip_frac=0.2, what="")
     log(f"  {what}: {yq_ref.size} int8 outputs bit-exact, {sat:.1%} saturated")
 
 
-@pytest.mark.parametrize("M,N,K,sx", [(1, 4096, 4096, 0.03),       # decode: streaming GEMV on codes
-                                      (16, 100, 4112, 0.02),       # decode, N tail, two K segments
-                                      (300, 520, 1040, 0.025),     # 64x64 tiles
-                                      (1000, 3000, 208, 0.03),     # 128x128 tiles
-                                      (2040, 6200, 336, 0.03)])    # 256x256 tiles, ragged M/N
-def test_linear_static_int8_output(M, N, K, sx):
-    log(f"[linear static] M={M} N={N} K={K} S_x={sx}")
+@pytest.mark.parametrize("tile,M,N,K,sx", [((0, 0), 1, 4096, 4096, 0.03),        # decode: streaming GEMV on codes
+                                           ((0, 0), 16, 100, 4112, 0.02),        # decode, N tail, two K segments
+                                           ((64, 64), 300, 520, 1040, 0.025),
+                                           ((64, 128), 500, 3000, 208, 0.03),
+                                           ((128, 128), 1000, 3000, 208, 0.03),
+                                           ((256, 256), 2040, 6200, 336, 0.03)])  # ragged M/N
+def test_linear_static_int8_output(tile, M, N, K, sx):
+    log(f"[linear static] M={M} N={N} K={K} S_x={sx}, tile {tile}")
+    assert q8.q8_gemm_tile("static", M, N, K) == tile
     x = inputs.random_matrix(150 + M, (M, K), 1.0, torch.bfloat16)
     w = inputs.random_matrix(160 + N, (N, K), 0.02, torch.float32)
-    rows = None if M * N * K <= 2e8 else sample_rows(M, 10, seed=M, extra=(255, 256))
-    run_static_case(x, w, sx, rows=rows, what=f"static {M}x{N}x{K}")
+    run_static_case(x, w, sx, what=f"static {M}x{N}x{K}")
 
 
 def test_linear_static_prefill_full_size_with_bias():
-    log("[linear static] prefill 2048x14336x4096 bf16 with bias, sampled rows")
+    log("[linear static] prefill 2048x14336x4096 bf16 with bias, whole matrix")
     wl = inputs.prefill_ffn_up()
     bias = inputs.random_matrix(170, (14336,), 0.5, torch.float32)
-    rows = sample_rows(2048, 4, seed=9, extra=(255, 256))
-    run_static_case(wl.x, wl.w, 0.03, rows=rows, bias=bias, what="static prefill")
+    run_static_case(wl.x, wl.w, 0.03, bias=bias, what="static prefill")
 
 
 # ---------------------------------------------------------------- FP8 experts on routed tokens
@@ -711,8 +735,7 @@ def test_linear_grouped_ragged(M, N, K, group, dt):
     log(f"[grouped] ragged M={M} N={N} K={K} group={group} {dt}")
     x = inputs.random_matrix(100 + M, (M, K), 1.0, dt)
     w = varied_groups(inputs.random_matrix(110 + N, (N, K), 0.02, torch.float32), group, N)
-    rows = None if M * N * K <= 2e8 else sample_rows(M, 10, seed=M, extra=(127, 128, 255, 256))
-    run_grouped_linear_case(x, w, group, torch.float32, rows=rows, what="ragged")
+    run_grouped_linear_case(x, w, group, torch.float32, what="ragged")
 
 
 def test_linear_grouped_prefill_full_size_sampled():

@@ -580,6 +580,20 @@ q8_status q8_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, 
   return launched(q8::launch_probe_fp8_mfma(a, b, c, d, count, st));
 }
 
+q8_status q8_gemm_tile(q8_op op, int64_t M, int64_t N, int64_t K, int32_t* bm, int32_t* bn) {
+  if (op != Q8_OP_LINEAR && op != Q8_OP_STATIC && op != Q8_OP_DECOMP && op != Q8_OP_FP8) return Q8_ERR_BAD_ARG;
+  Q8_TRY(check_mnk(M, N, K));
+  if (!bm || !bn) return Q8_ERR_NULL_PTR;
+  *bm = *bn = 0;
+  if (M == 0 || ((op == Q8_OP_LINEAR || op == Q8_OP_STATIC) && M <= q8::kGemvMaxM)) return Q8_OK;
+  const q8::GemmKind kind = op == Q8_OP_DECOMP ? q8::GEMM_INT8_DECOMP : op == Q8_OP_FP8 ? q8::GEMM_FP8 : q8::GEMM_INT8;
+  int tm = 0, tn = 0;
+  q8::gemm_tile(kind, M, N, &tm, &tn);
+  *bm = tm;
+  *bn = tn;
+  return Q8_OK;
+}
+
 q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_t K, const uint8_t* wq,
                       const float* w_scale, int64_t N, const float* bias, void* y, void* stream) {
   Q8_TRY(check_mnk(M, N, K));

@@ -657,22 +657,31 @@ hipError_t launch_tiles(const GemmArgs& g, int ydt, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Pick the largest tile that still gives most of the 256 CUs a workgroup.
 template <int KIND>
 hipError_t launch_kind(const GemmArgs& g, int ydt, hipStream_t st) {
-  auto tiles = [&](int bm, int bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
-  // the outlier flow needs the accumulators in VGPRs: no 256 x 256 tile there
+  int bm = 0, bn = 0;
+  gemm_tile((GemmKind)KIND, g.M, g.N, &bm, &bn);
   if constexpr (KIND != GEMM_INT8_DECOMP) {
-    if (tiles(256, 256) >= 192) return launch_tiles<256, 256, KIND>(g, ydt, st);
+    if (bm == 256) return launch_tiles<256, 256, KIND>(g, ydt, st);
   }
-  if (tiles(128, 128) >= 192) return launch_tiles<128, 128, KIND>(g, ydt, st);
-  // e.g. the LLM.int8 shape 512 x 4096: one round of 256 tiles, two
-  // independent accumulators per wave
-  if (tiles(64, 128) >= 192) return launch_tiles<64, 128, KIND>(g, ydt, st);
+  if (bm == 128) return launch_tiles<128, 128, KIND>(g, ydt, st);
+  if (bn == 128) return launch_tiles<64, 128, KIND>(g, ydt, st);
   return launch_tiles<64, 64, KIND>(g, ydt, st);
 }
 
 }  // namespace
+
+// Pick the largest tile that still gives most of the 256 CUs a workgroup.
+void gemm_tile(GemmKind kind, int64_t M, int64_t N, int* bm, int* bn) {
+  auto tiles = [&](int64_t tm, int64_t tn) { return ((M + tm - 1) / tm) * ((N + tn - 1) / tn); };
+  // the outlier flow needs the accumulators in VGPRs: no 256 x 256 tile there
+  if (kind != GEMM_INT8_DECOMP && tiles(256, 256) >= 192) { *bm = 256; *bn = 256; return; }
+  if (tiles(128, 128) >= 192) { *bm = 128; *bn = 128; return; }
+  // e.g. the LLM.int8 shape 512 x 4096: one round of 256 tiles, two
+  // independent accumulators per wave
+  if (tiles(64, 128) >= 192) { *bm = 64; *bn = 128; return; }
+  *bm = 64; *bn = 64;
+}
 
 hipError_t launch_gemm_fp8_grouped(const GemmArgs& g, hipStream_t st) {
   // tile size from the mean rows per group; the grid bounds the tile count:

@@ -54,6 +54,8 @@ constexpr int kOutInt8 = 3;
 enum GemmKind : int { GEMM_INT8 = 0, GEMM_INT8_DECOMP = 1, GEMM_FP8 = 2 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, int ydt, hipStream_t st);
+// The output tile (BM x BN) launch_gemm uses for an M x N problem of `kind`.
+void gemm_tile(GemmKind kind, int64_t M, int64_t N, int* bm, int* bn);
 // FP8 rowwise GEMM over groups of rows (bf16 out): g.M is the total row count,
 // g.b / g.b_scale hold groups consecutive [N, K] / [N] blocks.
 hipError_t launch_gemm_fp8_grouped(const GemmArgs& g, hipStream_t st);

@@ -5,6 +5,7 @@ current HIP stream, and turns a non-OK status into an exception.  All
 arithmetic happens in the HIP kernels."""
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional
 
@@ -386,3 +387,13 @@ def q8_probe_fp8_mfma(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor) -> torc
     st = _lib.lib().q8_probe_fp8_mfma(_ptr(a), _ptr(b), _ptr(c), _ptr(d), P, _stream(dev))
     _lib.check("q8_probe_fp8_mfma", st)
     return d
+
+
+def q8_gemm_tile(op: str, M: int, N: int, K: int) -> tuple:
+    """Introspection helper (include/q8_bench.h): the (rows, columns) output
+    tile of the MFMA GEMM that a call of op ("linear", "static", "decomp",
+    "fp8") runs at this shape; (0, 0) where none runs."""
+    bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = _lib.lib().q8_gemm_tile(_OP[op], M, N, K, ctypes.byref(bm), ctypes.byref(bn))
+    _lib.check("q8_gemm_tile", st)
+    return bm.value, bn.value
