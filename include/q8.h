@@ -13,7 +13,8 @@
  * --------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller.  The library
  *   never allocates, frees or keeps a pointer after a call returns.  Scratch
- *   space comes from a caller-provided workspace sized by q8_workspace_bytes.
+ *   space comes from a caller-provided workspace sized by q8_workspace_bytes
+ *   (q8_linear_noalloc: from a fixed device array of the library).
  * - Tensors are dense, row-major, 2-D.  X is [M, K] (tokens x input features),
  *   W is [N, K] (output features x input features, K contiguous), Y is [M, N].
  *   A caller with batch dimensions flattens them into M first ([FB] §5.2: the
@@ -22,7 +23,8 @@
  *   Calls only enqueue work on that stream and return; no call ever waits for
  *   the device, so results are valid once the stream has reached this point.
  *   The library keeps no state between calls apart from a per-device cache of
- *   the device check; calls on different streams may run concurrently.
+ *   the device check (and the scratch array of q8_linear_noalloc); calls on
+ *   different streams may run concurrently (q8_linear_noalloc excepted).
  * - Every argument is checked on the host BEFORE anything is enqueued.  On a
  *   non-Q8_OK status nothing has been written.  Q8_ERR_LAUNCH reports a
  *   failed kernel launch (hipGetLastError) after validation passed.
@@ -319,6 +321,28 @@ q8_status q8_linear_grouped(const void* x, q8_dtype x_dtype, int64_t M, int64_t 
                             int64_t group, int64_t N, const float* bias, void* y,
                             q8_dtype y_dtype, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * q8_linear_noalloc -- q8_linear with no workspace argument, for callers that
+ * cannot allocate device memory around a call (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * computation, kernels and results as q8_linear, bit for bit.  The scratch
+ * that q8_linear takes from the workspace (above 10 tokens: the activation
+ * codes, scales and code sums, q8_workspace_bytes(Q8_OP_LINEAR, M, N, K)
+ * bytes) comes from a library-owned 32 MiB device array per GPU, created with
+ * the library and kept until the process ends; nothing is allocated or freed
+ * by the call.  Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  The array keeps the last call's contents; nothing
+ * in it needs to start at zero.  The first call on a device looks up the
+ * array's address there (host side, once per device).
+ * Errors: as q8_linear, and Q8_ERR_WORKSPACE if the scratch the shape needs
+ * exceeds 32 MiB (M * K + 8 M plus alignment: e.g. M = 4096 at K = 8192).
+ */
+q8_status q8_linear_noalloc(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
+                            const int8_t* wq, const float* w_scale, const float* w_zp,
+                            int64_t N, const float* bias, void* y, q8_dtype y_dtype,
+                            int32_t* acc_out, void* stream);
 
 /* Bytes of workspace the call `op` needs at this shape (0 if none); returns 0
  * for invalid shapes as well, which the call itself then rejects. */

@@ -333,6 +333,28 @@ def test_gemm_tile_query():
     assert f(_lib.Q8_OP_LINEAR, 100, 100, 64, None, P2) == 1
 
 
+def test_linear_noalloc_validation():
+    """Argument errors and the scratch limit are reported before any HIP call
+    (host only)."""
+    f = _lib.lib().q8_linear_noalloc
+    E = _lib
+    ok = dict(x=P, xd=E.Q8_BF16, M=64, K=4096, wq=P, ws=P, wz=P, N=128, b=None, y=P2, yd=E.Q8_BF16, acc=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["x"], a["xd"], a["M"], a["K"], a["wq"], a["ws"], a["wz"], a["N"], a["b"], a["y"], a["yd"],
+                 a["acc"], None)
+    assert call(K=8) == 2
+    assert call(xd=9) == 3
+    assert call(wz=None) == 1
+    assert call(y=MIS) == 6
+    # scratch: M * K + 8 M + alignment must fit 32 MiB
+    assert call(M=4096, K=8192) == 7
+    assert call(M=8192, K=4096) == 7
+    assert _lib.lib().q8_workspace_bytes(E.Q8_OP_LINEAR, 4096, 128, 8192) > 32 << 20
+    assert _lib.lib().q8_workspace_bytes(E.Q8_OP_LINEAR, 4090, 128, 8192) <= 32 << 20
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """No fallback: without libq8.so every call raises (there is no CPU path)."""
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libq8.so"))

@@ -43,6 +43,7 @@ SIGNATURES = {
     "q8_linear_static": (_INT, [_P, _INT, _I64, _I64, _F, _P, _P, _P, _I64, _P, _F, _P, _P, _SZ, _P]),
     "q8_quantize_weight_grouped": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P]),
     "q8_linear_grouped": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _INT, _P, _SZ, _P]),
+    "q8_linear_noalloc": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _I64, _P, _P, _INT, _P, _P]),
     "q8_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     # include/q8_bench.h
     "q8_bench_mfma_loop": (_INT, [_INT, _I64, _I64, _P, _P]),

@@ -15,6 +15,7 @@
 #include "q8_bench_kernels.hpp"
 #include "q8_group.hpp"
 #include "q8_kernels.hpp"
+#include "q8_linear_impl.hpp"
 
 namespace {
 
@@ -211,6 +212,46 @@ q8_status launched(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_ERR_LAUNC
 
 }  // namespace
 
+namespace q8 {
+
+q8_status linear_check_args(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const int8_t* wq,
+                            const float* w_scale, const float* w_zp, int64_t N, const float* bias, const void* y,
+                            q8_dtype y_dtype, const int32_t* acc_out, size_t* workspace_needed) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
+  Q8_TRY(check_mnk(M, N, K));
+  if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (acc_out && !aligned16(acc_out)))
+    return Q8_ERR_ALIGN;
+  *workspace_needed = linear_ws(M, K).total;
+  return Q8_OK;
+}
+
+q8_status linear_run(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const int8_t* wq, const float* w_scale,
+                     const float* w_zp, int64_t N, const float* bias, void* y, q8_dtype y_dtype, void* workspace,
+                     int32_t* acc_out, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace, acc_out}));
+  if (M == 0) return Q8_OK;
+
+  if (M <= q8::kGemvFusedMaxM)
+    return launched(q8::launch_gemv_i8(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype,
+                                       acc_out, st));
+
+  const LinearWs ws = linear_ws(M, K);
+  char* base = static_cast<char*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
+  float* xs = reinterpret_cast<float*>(base + ws.xs);
+  int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
+  Q8_TRY(launched(q8::launch_quant_act_i8(x, x_dtype, M, K, xq, xs, rs, st)));
+  return launched(int8_on_codes(xq, xs, rs, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st));
+}
+
+q8_status stream_device(void* stream, int* dev) { return device_of(static_cast<hipStream_t>(stream), dev); }
+
+}  // namespace q8
+
 extern "C" {
 
 const char* q8_status_str(q8_status s) {
@@ -288,30 +329,11 @@ q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K, const
                     const float* w_scale, const float* w_zp, int64_t N, const float* bias, void* y,
                     q8_dtype y_dtype, void* workspace, size_t workspace_bytes, int32_t* acc_out,
                     void* stream) {
-  if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return Q8_ERR_BAD_DTYPE;
-  Q8_TRY(check_mnk(M, N, K));
-  if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
-  const LinearWs ws = linear_ws(M, K);
-  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
-  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
-      (bias && !aligned16(bias)) || (acc_out && !aligned16(acc_out)) ||
-      (ws.total > 0 && !aligned16(workspace)))
-    return Q8_ERR_ALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  Q8_TRY(check_device(st));
-  Q8_TRY(check_ptrs(st, {x, wq, w_scale, w_zp, bias, y, workspace, acc_out}));
-  if (M == 0) return Q8_OK;
-
-  if (M <= q8::kGemvFusedMaxM)
-    return launched(q8::launch_gemv_i8(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype,
-                                       acc_out, st));
-
-  char* base = static_cast<char*>(workspace);
-  int8_t* xq = reinterpret_cast<int8_t*>(base + ws.xq);
-  float* xs = reinterpret_cast<float*>(base + ws.xs);
-  int32_t* rs = reinterpret_cast<int32_t*>(base + ws.rs);
-  Q8_TRY(launched(q8::launch_quant_act_i8(x, x_dtype, M, K, xq, xs, rs, st)));
-  return launched(int8_on_codes(xq, xs, rs, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, st));
+  size_t need = 0;
+  Q8_TRY(q8::linear_check_args(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, acc_out, &need));
+  if (need > 0 && (!workspace || workspace_bytes < need)) return Q8_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return Q8_ERR_ALIGN;
+  return q8::linear_run(x, x_dtype, M, K, wq, w_scale, w_zp, N, bias, y, y_dtype, workspace, acc_out, stream);
 }
 
 q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_t* wq,

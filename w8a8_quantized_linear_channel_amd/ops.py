@@ -137,6 +137,31 @@ def q8_linear(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, w_zp: to
     return (y, acc) if acc_out else y
 
 
+def q8_linear_noalloc(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, w_zp: torch.Tensor,
+                      bias: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      acc_out: bool = False, out: Optional[torch.Tensor] = None):
+    """q8_linear without a workspace (the library's own scratch array); with
+    `out` (and acc_out False) the binding allocates nothing either.  Returns y
+    (and the INT32 accumulator if acc_out)."""
+    _need(x, "x")
+    dev = x.device
+    M, K = x.shape
+    N = wq.shape[0]
+    _need(wq, "wq", torch.int8, (N, K), dev)
+    _need(w_scale, "w_scale", torch.float32, (N,), dev)
+    _need(w_zp, "w_zp", torch.float32, (N,), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (N,), dev)
+    out_dtype = out_dtype or x.dtype
+    y = out if out is not None else torch.empty(M, N, dtype=out_dtype, device=dev)
+    _need(y, "y", out_dtype, (M, N), dev)
+    acc = torch.empty(M, N, dtype=torch.int32, device=dev) if acc_out else None
+    st = _lib.lib().q8_linear_noalloc(_ptr(x), _DT[x.dtype], M, K, _ptr(wq), _ptr(w_scale), _ptr(w_zp), N,
+                                      _ptr(bias), _ptr(y), _DT[out_dtype], _ptr(acc), _stream(dev))
+    _lib.check("q8_linear_noalloc", st)
+    return (y, acc) if acc_out else y
+
+
 def q8_linear_int8_decomp(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
                           w_zp: torch.Tensor, threshold: float = 6.0,
                           bias: Optional[torch.Tensor] = None, return_outliers: bool = False,
