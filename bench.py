@@ -54,9 +54,9 @@ METRIC = "q8_linear int8 TOPS (prefill) + GB/s (decode) and % of MI355X roofline
 # (x 2.0), WRITE_SIZE 262144 KiB (x 1.0).  Valid for the GEMM sources whose
 # hash is recorded here; after any change to them the figure is withheld.
 GEMM_TRAFFIC = {
-    "sources_sha256": "6bc7061fac34ea12a05d91278838864c39088f6a365b2f90ecde77a2ed8bb520",
-    "fetch_kib": 90484.91, "fetch_scale": 262144.0 / 131086.31,
-    "write_kib": 57345.75, "write_scale": 262144.0 / 262144.00,
+    "sources_sha256": "c5c3fbfe05428a954dd5db04f02125dc39a7edb572d237eef2a90c10fbd4bc95",
+    "fetch_kib": 90484.40, "fetch_scale": 262144.0 / 131085.38,
+    "write_kib": 57344.39, "write_scale": 262144.0 / 262144.00,
 }
 
 
@@ -195,7 +195,6 @@ def bench_prefill(dev, steps, warmup):
         "gemm_tops": ops / (gemm_ms * 1e-3) / 1e12,
         "shape": (M, N, K),
         "warm": warm,
-        "host_inputs": (wl.x, wl.w),
     }
     # act-quant kernel alone (HBM-bound): bytes = X bf16 in + codes out + 8 B/row.
     # Its launches are replayed from a HIP graph: launched one by one from
@@ -381,11 +380,44 @@ def bench_grouped(dev, steps, warmup, group=128):
 
 
 # ------------------------------------------------------------------ measured ceilings
+def stream_read_ceiling(dev, steps):
+    """HBM ceiling from the library's streaming-read kernel (include/q8_bench.h):
+    the best of a few launch widths, (a) at 16.8 MB per launch -- the decode
+    weight stream -- over 32 distinct buffers (537 MB, beyond the 256 MB
+    Infinity Cache) replayed from a HIP graph as the decode calls are, and
+    (b) one 512 MiB buffer per launch."""
+    res = {}
+    nb = 4096 * 4096 + 8 * 4096
+    bufs = [torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 255) for _ in range(32)]
+    best = None
+    for wgs in (512, 1024, 2048):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+        us = graph_us(lambda: [q8.q8_bench_stream_read(b, wgs, sink) for b in bufs], 1, max(4, steps // 4))
+        us /= len(bufs)
+        if best is None or us < best[0]:
+            best = (us, wgs)
+    res["16.8MB_rotating_32_buffers"] = {"GB/s": round(nb / (best[0] * 1e-6) / 1e9, 1), "us": round(best[0], 3),
+                                          "workgroups": best[1]}
+    del bufs
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
+    best = None
+    for wgs in (2048, 4096, 8192):
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+        _, ms, _ = timed_steps(lambda i, pair: (mark(pair, 0), q8.q8_bench_stream_read(src, wgs, sink), mark(pair, 1)),
+                               max(4, steps // 4), 2, [(ev(), ev()) for _ in range(max(4, steps // 4))])
+        if best is None or ms < best[0]:
+            best = (ms, wgs)
+    res["512MiB"] = {"GB/s": round(n / (best[0] * 1e-3) / 1e9, 1), "us": round(best[0] * 1e3, 2), "workgroups": best[1]}
+    del src
+    return res
+
+
 def bench_ceilings(dev, steps):
-    """What this machine reaches with plain device copies and with the vendor
-    GEMM library on the same shapes, beside the specification peaks: the copy
-    for the HBM-bound rows, hipBLASLt (torch._int_mm with INT32 output,
-    torch._scaled_mm rowwise) for the GEMMs.  A ceiling is the best of three
+    """What this machine reaches with a streaming read and with the vendor
+    GEMM library on the same shapes, beside the specification peaks: the
+    streaming read for the HBM-bound rows, hipBLASLt (torch._int_mm with INT32
+    output, torch._scaled_mm rowwise) for the GEMMs.  A ceiling is the best of three
     timed regions, each after the usual warm-up (the library's first region
     has been measured up to 20 % slower than its later ones)."""
     out = {}
@@ -398,12 +430,7 @@ def bench_ceilings(dev, steps):
             best = ms if best is None else min(best, ms)
         return best
 
-    n = 512 << 20
-    src = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
-    dst = torch.empty_like(src)
-    ms = t_ms(lambda: dst.copy_(src))
-    out["hbm_copy_GBs"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
-    del src, dst
+    out["hbm_stream_read"] = stream_read_ceiling(dev, steps)
     g = torch.Generator(device="cpu").manual_seed(5)
     try:
         M, N, K = 2048, 14336, 4096
@@ -436,24 +463,95 @@ def bench_ceilings(dev, steps):
 
 
 # ------------------------------------------------------------------ CPU oracle
-def cpu_baseline(x_host, w_host, target_s):
-    """The oracle (untuned numpy) on a bounded sample of the prefill step: the
-    first R token rows of X against the full weight matrix."""
+def _oracle_threads():
+    """Threads the oracle's numpy uses (its BLAS pool does the matrix
+    products; the rest of numpy is single-threaded)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:   # threadpoolctl is optional: fall back to the host's count
+        pass
+    return os.cpu_count() or 1
+
+
+def _time_rows(fn, rows_total, budget_s, min_rows=1):
+    """Run fn(rows) on a small sample, then grow the sample (at most to
+    rows_total) until a run takes at least half the budget; return (rows,
+    seconds) of the last run."""
+    rows = max(min_rows, min(rows_total, 8))
+    while True:
+        t = time.perf_counter()
+        fn(rows)
+        dt = time.perf_counter() - t
+        if rows >= rows_total or dt >= 0.5 * budget_s:
+            return rows, dt
+        rows = int(min(rows_total, max(2 * rows, rows * 0.8 * budget_s / max(dt, 1e-3))))
+
+
+def cpu_baselines(budget_s):
+    """The oracle (oracle/q8_oracle.py, untuned numpy; its integer and FP8
+    matrix products go to numpy's multi-threaded BLAS) on each workload's
+    forward step, host inputs, weights quantized beforehand (untimed).  Each
+    workload gets about budget_s seconds: the whole step if it fits, else the
+    first R token rows against all the weights, scaled to the step's unit."""
     from oracle import q8_oracle as O
-    wq, ws, wz = O.quantize_weight_int8_asym(w_host)        # offline, untimed
-    N, K = w_host.shape
-    rows = 4
-    t = time.perf_counter()
-    O.linear_int8(x_host[:rows], wq, ws, wz)
-    dt = time.perf_counter() - t
-    rows = int(max(4, min(x_host.shape[0], rows * target_s / max(dt, 1e-3))))
-    t = time.perf_counter()
-    O.linear_int8(x_host[:rows], wq, ws, wz)
-    dt = time.perf_counter() - t
-    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "seconds": dt,
-            "sample": f"first {rows} of 2048 token rows (activation quantization, exact int64 GEMM, "
-                      f"epilogue) against all {N}x{K} weights; numpy's integer matmul is single-threaded"}
+    cores = _oracle_threads()
+    out = {}
+    # prefill FFN-up (the headline workload)
+    wl = inputs.prefill_ffn_up()
+    wq, ws, wz = O.quantize_weight_int8_asym(wl.w)
+    N, K = wl.w.shape
+    rows, dt = _time_rows(lambda r: O.linear_int8(wl.x[:r], wq, ws, wz), wl.x.shape[0], budget_s)
+    out["prefill"] = {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+                      "seconds": dt, "sample": f"{rows} of {wl.x.shape[0]} token rows of the prefill FFN-up step "
+                                              f"(activation quantization, exact integer GEMM, epilogue) against "
+                                              f"all {N}x{K} weights"}
+    del wq, ws, wz, wl
+    # decode q_proj, M = 16: bytes as the GPU figure counts them
+    wl = inputs.decode_qproj(M=16)
+    wq, ws, wz = O.quantize_weight_int8_asym(wl.w)
+    N, K = wl.w.shape
+    reps, t = 0, time.perf_counter()
+    while time.perf_counter() - t < min(budget_s, 3.0) or reps == 0:
+        O.linear_int8(wl.x, wq, ws, wz)
+        reps += 1
+    dt = (time.perf_counter() - t) / reps
+    nbytes = N * K + 8 * N + 16 * K * 2 + 16 * N * 2
+    out["decode_M16"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                         "seconds": dt, "sample": f"the whole 16-token q_proj call, mean of {reps}"}
+    del wq, ws, wz, wl
+    # LLM.int8 decomposition
+    wl = inputs.llm_int8_outliers()
+    wq, ws, wz = O.quantize_weight_int8_asym(wl.w)
+    N, K = wl.w.shape
+    rows, dt = _time_rows(lambda r: O.linear_int8_decomp(wl.x[:r], wq, ws, wz, 6.0), wl.x.shape[0], budget_s, 64)
+    out["llm_int8"] = {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+                       "seconds": dt, "sample": f"{rows} of {wl.x.shape[0]} token rows (outlier columns found on "
+                                                f"those rows) against all {N}x{K} weights"}
+    del wq, ws, wz, wl
+    # FP8 rowwise
+    wl = inputs.fp8_rowwise()
+    wq, ws = O.quantize_fp8_rowwise(wl.w)
+    N, K = wl.w.shape
+    rows, dt = _time_rows(lambda r: O.linear_fp8(wl.x[:r], wq, ws, 1200.0), wl.x.shape[0], budget_s)
+    out["fp8"] = {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                  "seconds": dt, "sample": f"{rows} of {wl.x.shape[0]} token rows against all {N}x{K} weights"}
+    del wq, ws, wl
+    # tiny W8A8 linear
+    wl = inputs.tiny_linear()
+    wq, ws, wz = O.quantize_weight_int8_asym(wl.w)
+    reps, t = 0, time.perf_counter()
+    while time.perf_counter() - t < 0.5 or reps == 0:
+        O.linear_int8(wl.x, wq, ws, wz)
+        reps += 1
+    dt = (time.perf_counter() - t) / reps
+    M, K = wl.x.shape
+    N = wl.w.shape[0]
+    out["tiny"] = {"value": dt * 1e6, "unit": "us per call", "cores": cores, "kind": "oracle", "seconds": dt,
+                   "sample": f"the whole {M}x{N}x{K} call, mean of {reps}"}
+    return out
 
 
 def main():
@@ -462,7 +560,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=400,
                     help="minimum warm-up steps per leg (each leg also warms up for %g ms)" % WARM_MS)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+                    help="host seconds per workload for the oracle's cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "grouped", "copy"], default=None,
                     help="run one workload (for profiling); 'copy' runs a plain 256 MiB device copy, "
@@ -493,7 +592,7 @@ def main():
         M, N, K = pf["shape"]
         out.update({
             "value": round(pf["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-            "warmup": pf["warm"][0], "warmup_ms": round(pf["warm"][1], 1),
+            "warmup": args.warmup, "warmup_steps_run": pf["warm"][0], "warmup_ms": round(pf["warm"][1], 1),
             "ms_per_step": round(pf["ms_per_step"], 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
             "data": "synthetic: seeded numpy PCG64, X ~ N(0,1) in bf16, W ~ N(0,0.02) quantized once",
@@ -571,7 +670,9 @@ def main():
         out["grouped_decode"] = {"workload": "q8_linear_grouped decode q_proj, N = K = 4096, group 128, bf16, "
                                              "32 rotating weight sets", **gd}
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(*pf["host_inputs"], args.cpu_seconds)
+        cb = cpu_baselines(args.cpu_seconds)
+        out["cpu_baseline"] = cb.pop("prefill")
+        out["cpu_baseline_other_workloads"] = cb
     print(json.dumps(out), flush=True)
 
 

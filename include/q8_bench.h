@@ -3,6 +3,8 @@
  * - a register-only MFMA loop that gives the matrix-core rate the chip
  *   sustains with no memory traffic (the measured compute ceiling set beside
  *   the published peak when the GEMM kernels are timed);
+ * - a streaming read of a device buffer, the measured HBM ceiling set beside
+ *   the published bandwidth when the HBM-bound kernels are timed;
  * - a probe that runs the FP8 GEMM's matrix instruction once on given
  *   operands, so that the rounding of its internal sum can be measured
  *   against exact sums (the FP8 parity tolerance rests on it);
@@ -32,6 +34,19 @@ extern "C" {
  */
 q8_status q8_bench_mfma_loop(q8_format fmt, int64_t iters, int64_t workgroups, int32_t* sink,
                              void* stream);
+
+/*
+ * q8_bench_stream_read -- reads `bytes` of device memory at `src` once:
+ * `workgroups` x 256 threads, each reading 16-byte chunks at a grid stride
+ * with eight loads in flight and the non-temporal cache policy of the
+ * decode kernels' weight stream, xor-folding them into sink[t] (device int32
+ * [workgroups * 256], caller-owned).  Asynchronous on `stream`.
+ * Errors: Q8_ERR_BAD_ARG unless bytes is a positive multiple of 16 below
+ * 2^31 and 1 <= workgroups <= 65536; Q8_ERR_NULL_PTR, Q8_ERR_ALIGN (src and
+ * sink 16-byte aligned), Q8_ERR_DEVICE as for every call.
+ */
+q8_status q8_bench_stream_read(const void* src, int64_t bytes, int64_t workgroups, int32_t* sink,
+                               void* stream);
 
 /*
  * q8_probe_fp8_mfma -- for each of `count` independent problems p, one wave

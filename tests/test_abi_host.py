@@ -301,6 +301,17 @@ def test_bench_mfma_loop_validation():
     assert f(E.Q8_INT8_SYM, 10, 8, MIS, None) == 6
 
 
+def test_bench_stream_read_validation():
+    f = _lib.lib().q8_bench_stream_read
+    assert f(P, 0, 8, P2, None) == 5
+    assert f(P, 24, 8, P2, None) == 5
+    assert f(P, 1 << 31, 8, P2, None) == 5
+    assert f(P, 4096, 0, P2, None) == 5
+    assert f(P, 4096, 65537, P2, None) == 5
+    assert f(None, 4096, 8, P2, None) == 1
+    assert f(MIS, 4096, 8, P2, None) == 6
+
+
 def test_probe_fp8_mfma_validation():
     f = _lib.lib().q8_probe_fp8_mfma
     assert f(P, P, P, P2, 0, None) == 5

@@ -48,6 +48,7 @@ SIGNATURES = {
     # include/q8_bench.h
     "q8_bench_mfma_loop": (_INT, [_INT, _I64, _I64, _P, _P]),
     "q8_probe_fp8_mfma": (_INT, [_P, _P, _P, _P, _I64, _P]),
+    "q8_bench_stream_read": (_INT, [_P, _I64, _I64, _P, _P]),
     "q8_gemm_tile": (_INT, [_INT, _I64, _I64, _I64, _P, _P]),
     "q8_status_str": (ctypes.c_char_p, [_INT]),
 }

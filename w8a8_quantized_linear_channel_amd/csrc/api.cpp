@@ -591,6 +591,17 @@ q8_status q8_bench_mfma_loop(q8_format fmt, int64_t iters, int64_t workgroups, i
   return launched(q8::launch_mfma_loop(fmt == Q8_INT8_SYM ? 0 : 2, iters, workgroups, sink, st));
 }
 
+q8_status q8_bench_stream_read(const void* src, int64_t bytes, int64_t workgroups, int32_t* sink, void* stream) {
+  if (bytes < 16 || bytes % 16 != 0 || bytes >= (int64_t(1) << 31) || workgroups < 1 || workgroups > 65536)
+    return Q8_ERR_BAD_ARG;
+  if (!src || !sink) return Q8_ERR_NULL_PTR;
+  if (!aligned16(src) || !aligned16(sink)) return Q8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Q8_TRY(check_device(st));
+  Q8_TRY(check_ptrs(st, {src, sink}));
+  return launched(q8::launch_stream_read(src, bytes, workgroups, sink, st));
+}
+
 q8_status q8_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int64_t count,
                             void* stream) {
   if (count < 1 || count > 65536) return Q8_ERR_BAD_ARG;

@@ -71,7 +71,33 @@ __global__ __launch_bounds__(64) void k_probe_fp8(const uint8_t* __restrict__ a,
   }
 }
 
+// Streaming read: every thread reads 16-byte chunks of [src, src + bytes) at
+// a grid stride, eight loads in flight, with the non-temporal cache policy the
+// decode kernels use for their weights; the chunks are xor-folded into one
+// word per thread.
+__global__ __launch_bounds__(256) void k_stream_read(const uint8_t* __restrict__ src, uint32_t chunks,
+                                                     int* __restrict__ sink) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  const __amdgpu_buffer_rsrc_t r = byte_buffer(src, chunks * 16u);
+  v4i acc = {0, 0, 0, 0};
+  for (; i + 7 * stride < chunks; i += 8 * stride) {
+    v4i v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = load16_nt(r, (i + u * stride) * 16u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; i < chunks; i += stride) acc ^= load16_nt(r, i * 16u);
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, int64_t workgroups, int* sink, hipStream_t st) {
+  k_stream_read<<<(unsigned)workgroups, 256, 0, st>>>((const uint8_t*)src, (uint32_t)(bytes / 16), sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, float* d, int64_t count,
                                  hipStream_t st) {

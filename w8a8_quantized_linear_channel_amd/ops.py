@@ -422,3 +422,15 @@ def q8_gemm_tile(op: str, M: int, N: int, K: int) -> tuple:
     st = _lib.lib().q8_gemm_tile(_OP[op], M, N, K, ctypes.byref(bm), ctypes.byref(bn))
     _lib.check("q8_gemm_tile", st)
     return bm.value, bn.value
+
+
+def q8_bench_stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor) -> None:
+    """Measurement helper (include/q8_bench.h): one streaming read of the
+    device tensor src (its bytes, a multiple of 16); sink is a device int32
+    tensor of workgroups * 256 elements."""
+    dev = src.device
+    _need(src, "src", None, None, dev)
+    _need(sink, "sink", torch.int32, (workgroups * 256,), dev)
+    nbytes = src.numel() * src.element_size()
+    st = _lib.lib().q8_bench_stream_read(_ptr(src), nbytes, workgroups, _ptr(sink), _stream(dev))
+    _lib.check("q8_bench_stream_read", st)
