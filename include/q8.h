@@ -232,7 +232,7 @@ q8_status q8_gemm_fp8(const uint8_t* xq, const float* x_scale, int64_t M, int64_
  * arrays); wq: e4m3 [E, N, K] and w_scale: float [E, N] from
  * q8_quantize_weight(Q8_FP8_E4M3) on the [E*N, K] view; y: bf16 [T, N].
  * workspace: q8_workspace_bytes(Q8_OP_FP8, T, N, K).  Errors: Q8_ERR_BAD_SHAPE
- * unless 1 <= E <= 65536; Q8_ERR_BAD_ARG for a NaN or non-positive scale_ub.
+ * unless 1 <= E <= 1024; Q8_ERR_BAD_ARG for a NaN or non-positive scale_ub.
  */
 q8_status q8_linear_fp8_grouped(const void* x_bf16, int64_t T, int64_t K,
                                 const int32_t* expert_offsets, int64_t E,

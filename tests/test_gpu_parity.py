@@ -644,6 +644,38 @@ def test_fp8_grouped_ragged(counts, N, K):
     run_grouped_case(x[:int(offsets[-1])], w, offsets, what="moe ragged")
 
 
+def test_fp8_grouped_many_experts_and_malformed_offsets():
+    """300 experts, most of them holding a few tokens or none; then offsets
+    that decrease, go below 0 and past T.  The kernel reads them as the
+    running maximum of max(offsets, 0) capped at T (group e spans c[e] ..
+    c[e+1]); rows inside those spans are compared with the oracle for their
+    expert, rows outside every span are left alone."""
+    log("[fp8 experts] 300 experts; malformed offsets")
+    rng = np.random.default_rng(210)
+    counts = rng.integers(0, 8, 300)
+    counts[rng.random(300) < 0.4] = 0
+    run_grouped_case(inputs.random_matrix(211, (int(counts.sum()), 128), 1.0, torch.bfloat16),
+                     inputs.random_matrix(212, (300, 96, 128), 0.02, torch.float32),
+                     np.concatenate([[0], np.cumsum(counts)]), what="300 experts")
+    T, N, K = 800, 160, 192
+    raw = np.array([5, -3, 400, 200, 900, 1200, 700])
+    E = raw.size - 1
+    c = np.minimum(np.maximum.accumulate(np.maximum(raw, 0)), T)
+    assert c.tolist() == [5, 5, 400, 400, 800, 800, 800]
+    x = inputs.random_matrix(213, (T, K), 1.0, torch.bfloat16)
+    w = inputs.random_matrix(214, (E, N, K), 0.02, torch.float32)
+    wq, ws, _ = q8.q8_quantize_weight(g(w.reshape(E * N, K)), "fp8_e4m3")
+    y = q8.q8_linear_fp8_grouped(g(x), g(torch.tensor(raw, dtype=torch.int32)), wq.view(E, N, K), ws.view(E, N),
+                                 scale_ub=1200.0)
+    rq, rs = O.quantize_fp8_rowwise(w.reshape(E * N, K))
+    rq, rs = rq.reshape(E, N, K), rs.reshape(E, N)
+    for e in range(E):
+        lo, hi = int(c[e]), int(c[e + 1])
+        if hi > lo:
+            yr, _ = O.linear_fp8(x[lo:hi], rq[e], rs[e], 1200.0)
+            check_close_fp8(out_f64(y[lo:hi]), yr, x[lo:hi], w[e], 1200.0, f"malformed offsets, expert {e} rows {lo}..{hi - 1}")
+
+
 # ---------------------------------------------------------------- per-group weights (q8_linear_grouped)
 def varied_groups(w, group, seed):
     """The same weights with every group scaled by 10^u (u in -1..1) and the

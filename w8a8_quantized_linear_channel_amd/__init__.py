@@ -11,8 +11,15 @@ from .ops import (  # noqa: F401
     q8_gemm_int8,
     q8_linear,
     q8_linear_fp8,
+    q8_linear_fp8_grouped,
+    q8_linear_grouped,
     q8_linear_int8_decomp,
+    q8_linear_noalloc,
+    q8_linear_static,
+    q8_linear_w8a16,
     q8_quantize_act,
+    q8_quantize_act_static,
     q8_quantize_weight,
+    q8_quantize_weight_grouped,
     q8_workspace_bytes,
 )

@@ -22,7 +22,7 @@ namespace {
 constexpr int64_t kMaxK = 65536;          // keeps acc - Z*rowsum inside int32 (|.| <= 32512 K)
 constexpr int64_t kMaxRows = (1LL << 31) - 1;
 constexpr size_t kAlign = 256;
-constexpr int64_t kMaxGroups = 1 << 16;         // experts of one grouped call
+constexpr int64_t kMaxGroups = 1024;            // experts of one grouped call (the kernels' bound)
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -38,6 +38,8 @@
 // XCD, 4 tile-rows share each weight tile in L2.
 //
 // Indices are 32-bit: the host guarantees M*K, N*K and M*N are below 2^31.
+#include <climits>
+
 #include "q8_device.hpp"
 #include "q8_kernels.hpp"
 
@@ -50,6 +52,7 @@ constexpr int kBK = 64;             // bytes of K per stage
 constexpr int kStages = 4;          // LDS buffers (prefetch distance kStages - 1)
 constexpr int kGroupM = 4;          // tile-rows per L2 group
 constexpr int kXcds = 8;
+constexpr int kMaxGroupsDev = 1024;   // groups (experts) of one grouped call
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
@@ -144,33 +147,88 @@ __device__ __forceinline__ void tile_coords(int ntm, int ntn, int& tm, int& tn) 
 // counted over the groups' tile-rows in order; the offsets are clamped to
 // [0, M] and made non-decreasing, so no group reaches outside the arrays.
 // Returns false for the tiles past the last group (the grid is an upper bound).
-template <int BM, int BN, int ES>
-__device__ __forceinline__ bool group_tile(GemmArgs& g, int& tm, int& tn) {
-  const int T = (int)g.M, N = (int)g.N, K = (int)g.K;
-  const int ntn = (N + BN - 1) / BN;
-  const int t = blockIdx.x;
-  tn = t % ntn;
-  int r = t / ntn;
-  int lo = 0;
-  for (int e = 0; e < g.groups; ++e) {
-    int a = g.group_offsets[e], b = g.group_offsets[e + 1];
-    a = a < lo ? lo : (a > T ? T : a);
-    b = b < a ? a : (b > T ? T : b);
-    lo = b;
-    const int tr = (b - a + BM - 1) / BM;
-    if (r < tr) {
-      tm = r;
-      g.M = b - a;
-      g.a += (size_t)a * K;
-      g.a_scale += a;
-      g.y = (uint8_t*)g.y + (size_t)a * N * ES;
-      g.b += (size_t)e * N * K;
-      g.b_scale += (size_t)e * N;
-      return true;
-    }
-    r -= tr;
+//
+// The workgroup resolves its tile in parallel: the clamped offsets are the
+// running maximum of max(offsets[e], 0) capped at M (group e spans c[e] ..
+// c[e+1]), and the groups' tile-row counts are summed by a block scan, so a
+// workgroup reads the E + 1 offsets once, split over its threads, and finds
+// its group by binary search: O(E / threads + log E) per workgroup.
+template <int NT>
+__device__ __forceinline__ int block_scan_incl(int v, int* red, bool max_op) {
+  const int t = threadIdx.x;
+  red[t] = v;
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < NT; d <<= 1) {
+    const int o = t >= d ? red[t - d] : (max_op ? INT_MIN : 0);
+    __syncthreads();
+    v = max_op ? (v > o ? v : o) : v + o;
+    red[t] = v;
+    __syncthreads();
   }
-  return false;
+  return v;
+}
+
+template <int BM, int BN, int ES, int NT>
+__device__ __forceinline__ bool group_tile(GemmArgs& g, int& tm, int& tn, int* lds) {
+  const int T = (int)g.M, N = (int)g.N, K = (int)g.K, E = g.groups;
+  const int ntn = (N + BN - 1) / BN;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  tn = t % ntn;
+  const int r = t / ntn;
+  int* const c = lds;                 // [E + 1] clamped offsets
+  int* const R = lds + (E + 1);       // [E + 1] first tile-row of each group
+  int* const red = R + (E + 1);       // [NT] scan scratch
+  const int per = (E + 1 + NT - 1) / NT, lo = tid * per;
+  const int hi = lo + per < E + 1 ? lo + per : E + 1;
+  // running maximum of max(offsets, 0) over this thread's slice, then across threads
+  int m = 0;
+  for (int e = lo; e < hi; ++e) m = g.group_offsets[e] > m ? g.group_offsets[e] : m;
+  const int incl = block_scan_incl<NT>(m, red, true);
+  int run = tid > 0 ? red[tid - 1] : 0;       // exclusive: the maximum before this slice
+  run = run > 0 ? run : 0;
+  for (int e = lo; e < hi; ++e) {
+    run = g.group_offsets[e] > run ? g.group_offsets[e] : run;
+    c[e] = run < T ? run : T;
+  }
+  (void)incl;
+  __syncthreads();
+  // tile-rows of the groups in this slice, then their running sum
+  int cnt = 0;
+  for (int e = lo; e < hi && e < E; ++e) cnt += (c[e + 1] - c[e] + BM - 1) / BM;
+  block_scan_incl<NT>(cnt, red, false);
+  int acc = tid > 0 ? red[tid - 1] : 0;
+  for (int e = lo; e < hi; ++e) {
+    R[e] = acc;
+    if (e < E) acc += (c[e + 1] - c[e] + BM - 1) / BM;
+  }
+  __syncthreads();
+  const bool inside = r < R[E];
+  int e = 0;
+  if (inside) {                       // the last group whose first tile-row is <= r
+    int lo2 = 0, hi2 = E - 1;
+    while (lo2 < hi2) {
+      const int mid = (lo2 + hi2 + 1) >> 1;
+      if (R[mid] <= r) lo2 = mid;
+      else hi2 = mid - 1;
+    }
+    e = lo2;
+  }
+  // every lane holds the same values: make them scalar for the DMA bases
+  const int a = __builtin_amdgcn_readfirstlane(c[e]), b = __builtin_amdgcn_readfirstlane(c[e + 1]);
+  const int trow = __builtin_amdgcn_readfirstlane(r - R[e]);
+  e = __builtin_amdgcn_readfirstlane(e);
+  const bool in = __builtin_amdgcn_readfirstlane(inside ? 1 : 0) != 0;
+  __syncthreads();                    // the LDS is the main loop's next
+  if (!in) return false;
+  tm = trow;
+  g.M = b - a;
+  g.a += (size_t)a * K;
+  g.a_scale += a;
+  g.y = (uint8_t*)g.y + (size_t)a * N * ES;
+  g.b += (size_t)e * N * K;
+  g.b_scale += (size_t)e * N;
+  return true;
 }
 
 template <int BM, int BN, int KIND, int YDT, int NW, bool GROUPED = false>
@@ -198,7 +256,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   GemmArgs g = g0;
   int tm, tn;
   if constexpr (GROUPED) {
-    if (!group_tile<BM, BN, YDT == DT_F32 ? 4 : 2>(g, tm, tn)) return;   // whole workgroup: no barrier yet
+    static_assert(2 * (kMaxGroupsDev + 1) * 4 + kThreads * 4 <= kStages * kStageBytes, "group scan does not fit");
+    if (!group_tile<BM, BN, YDT == DT_F32 ? 4 : 2, kThreads>(g, tm, tn, (int*)smem)) return;   // uniform
   } else {
     tile_coords((int)((g.M + BM - 1) / BM), (int)((g.N + BN - 1) / BN), tm, tn);
   }
@@ -518,7 +577,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   constexpr int kPitch = TL::TN * 4 + 16;
   constexpr int LPR = TL::TN / 8;                       // readback lanes per row
   constexpr int RPI = 64 / LPR;                         // rows per readback instruction
-  static_assert(kFacBytes + 4 * 32 * kPitch <= kStages * kStageBytes, "epilogue staging does not fit");
+  static_assert(kFacBytes + NW * 32 * kPitch <= kStages * kStageBytes, "epilogue staging does not fit");
   uint8_t* const stg = smem + kFacBytes + wave * 32 * kPitch;
   const int rc = lane % LPR, rr = lane / LPR;
   const int ncl = nw + 8 * rc;                          // first of the lane's 8 columns in the tile
