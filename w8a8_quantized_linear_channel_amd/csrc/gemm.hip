@@ -595,6 +595,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   auto zcorr = [](int acc, int z, int rs) { return acc + __mul24(-z, rs); };
   constexpr int ES = YDT == DT_F32 ? 4 : 2;
   const bool vec = (N & 7) == 0;                        // 8-column groups start 16-byte aligned
+  const bool full = vec && m0 + BM <= M && n0 + BN <= N; // an interior tile: no row or column past Y
 #pragma unroll
   for (int i = 0; i < TL::FM; ++i) {
 #pragma unroll
@@ -620,15 +621,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
       rsx[t] = f_sx[mw + i * 32 + row];
       rrs[t] = KIND == GEMM_INT8 ? f_rs[mw + i * 32 + row] : 0;
     }
-#pragma unroll
-    for (int t = 0; t < TI; ++t) {
+    // one output row of the slab.  CHK: bounds and 16-byte alignment are
+    // checked per row (a tile at the edge of Y); ACC: the INT32 accumulator
+    // may be stored too.  An interior tile without the accumulator output
+    // runs without per-row tests.
+    auto row = [&](int t, auto CHK, auto ACC) __attribute__((always_inline)) {
+      constexpr bool chk = decltype(CHK)::value;
       const int m = m0 + mw + i * 32 + t * RPI + rr;
-      const bool ok = m < M && n < N;
+      const bool ok = !chk || (m < M && n < N);
       const int a[8] = {ra[t][0], ra[t][1], ra[t][2], ra[t][3], rb[t][0], rb[t][1], rb[t][2], rb[t][3]};
       const size_t o = (size_t)(uint32_t)(m * N + n);
-      if constexpr (KIND == GEMM_INT8) {
+      if constexpr (KIND == GEMM_INT8 && decltype(ACC)::value) {
         if (g.acc_out && ok) {
-          if (vec) {
+          if (!chk || vec) {
             *(v4i*)(g.acc_out + o) = ra[t];
             *(v4i*)(g.acc_out + o + 4) = rb[t];
           } else {
@@ -640,50 +645,56 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
       if constexpr (YDT == DT_I8) {
         // requantized INT8 output (int8 GEMM only): the codes are decided in
         // float64 exactly as the definition states
-        if (!ok) continue;
+        if (!ok) return;
         int qv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = requant_i8(sx, csb[e], zcorr(a[e], czi[e], rrs[t]), cbb[e], g.y_inv);
         int8_t* yq = (int8_t*)g.y + o;
-        if (vec) {
+        if (!chk || vec) {
           *(v2i*)yq = v2i{(int)pack_lo_bytes(qv[0], qv[1], qv[2], qv[3]), (int)pack_lo_bytes(qv[4], qv[5], qv[6], qv[7])};
         } else {
           for (int e = 0; e < 8 && n + e < N; ++e) yq[e] = (int8_t)qv[e];
         }
-        continue;
-      }
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (KIND == GEMM_INT8) {
-          v[e] = (sx * csb[e]) * (float)zcorr(a[e], czi[e], rrs[t]) + cbb[e];
-        } else if constexpr (KIND == GEMM_FP8) {
-          v[e] = __int_as_float(a[e]) * (sx * csb[e]) + cbb[e];
-        } else {
-          v[e] = __int_as_float(a[e]) + cbb[e];
-        }
-      }
-      if (!ok) continue;
-      if (vec) {
-        // the output is written once and not read back here: non-temporal stores
-        if constexpr (YDT == DT_F32) {
-          v4i* yp = (v4i*)((float*)g.y + o);
-          __builtin_nontemporal_store(v4i{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
-                                          __float_as_int(v[3])}, yp);
-          __builtin_nontemporal_store(v4i{__float_as_int(v[4]), __float_as_int(v[5]), __float_as_int(v[6]),
-                                          __float_as_int(v[7])}, yp + 1);
-        } else {
-          uint32_t h[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = YDT == DT_F16 ? f32_to_f16(v[e]) : f32_to_bf16(v[e]);
-          __builtin_nontemporal_store(v4i{(int)(h[0] | (h[1] << 16)), (int)(h[2] | (h[3] << 16)),
-                                          (int)(h[4] | (h[5] << 16)), (int)(h[6] | (h[7] << 16))},
-                                      (v4i*)((uint16_t*)g.y + o));
-        }
       } else {
-        if constexpr (YDT != DT_I8)   // (the INT8 output left above)
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (KIND == GEMM_INT8) {
+            v[e] = (sx * csb[e]) * (float)zcorr(a[e], czi[e], rrs[t]) + cbb[e];
+          } else if constexpr (KIND == GEMM_FP8) {
+            v[e] = __int_as_float(a[e]) * (sx * csb[e]) + cbb[e];
+          } else {
+            v[e] = __int_as_float(a[e]) + cbb[e];
+          }
+        }
+        if (!ok) return;
+        if (!chk || vec) {
+          // the output is written once and not read back here: non-temporal stores
+          if constexpr (YDT == DT_F32) {
+            v4i* yp = (v4i*)((float*)g.y + o);
+            __builtin_nontemporal_store(v4i{__float_as_int(v[0]), __float_as_int(v[1]), __float_as_int(v[2]),
+                                            __float_as_int(v[3])}, yp);
+            __builtin_nontemporal_store(v4i{__float_as_int(v[4]), __float_as_int(v[5]), __float_as_int(v[6]),
+                                            __float_as_int(v[7])}, yp + 1);
+          } else {
+            v4i pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pk[e] = (int)pack2_out<YDT>(v[2 * e], v[2 * e + 1]);
+            __builtin_nontemporal_store(pk, (v4i*)((uint16_t*)g.y + o));
+          }
+        } else {
           for (int e = 0; e < 8 && n + e < N; ++e) store_out<YDT>(g.y, o + e, v[e]);
+        }
       }
+    };
+    using Tt = std::true_type;
+    using Ft = std::false_type;
+    if (full && !g.acc_out) {
+#pragma unroll
+      for (int t = 0; t < TI; ++t) row(t, Ft{}, Ft{});
+    } else {
+#pragma unroll
+      for (int t = 0; t < TI; ++t) row(t, Tt{}, Tt{});
     }
   }
   (void)ES;

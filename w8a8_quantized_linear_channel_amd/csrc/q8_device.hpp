@@ -64,6 +64,19 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// Two outputs packed into one word, round-to-nearest-even: one
+// v_cvt_pk_bf16_f32 for bf16.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <int DT> __device__ __forceinline__ uint32_t pack2_out(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2_out<DT_BF16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+template <> __device__ __forceinline__ uint32_t pack2_out<DT_F16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
+}
+
 template <int DT> __device__ __forceinline__ void store_out(void* y, int64_t i, float v);
 template <> __device__ __forceinline__ void store_out<DT_F32>(void* y, int64_t i, float v) {
   ((float*)y)[i] = v;
