@@ -397,12 +397,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
 // workgroup costs more vector work than the weight stream takes to arrive, so
 // the rows are quantized once and this kernel only streams.  A workgroup owns
 // 16 weight rows and its 4 waves split K; each wave copies its 1 KB share of
-// the 16 weight rows and of the M code rows into its own LDS region, one
-// contiguous 1 KB DMA per row, and runs v_mfma_i32_16x16x64_i8 on them
-// (weights as A, codes as B).  Only the wave itself reads its region, so a
-// wait on its own DMA replaces a barrier.  Rows past N (or M) repeat the last
-// row and only feed outputs that are not stored; columns past K repeat the
-// segment's last 16 bytes and their codes are masked to zero.
+// the M code rows into its own LDS region (one contiguous 1 KB DMA per row),
+// loads its share of the 16 weight rows straight into registers as the fused
+// kernel does, and runs v_mfma_i32_16x16x64_i8 (weights as A, codes as B).
+// (Staging the weights through LDS as well, one 1 KB DMA per row, took 7.4
+// against ~5 us: the MFMAs then wait for both streams.)  Only the wave itself
+// reads its region, so a wait on its own DMA replaces a barrier.  Rows past N
+// (or M) repeat the last row and only feed outputs that are not stored;
+// columns past K read past the row and their codes are masked to zero.
 constexpr int kWPitch = kKW + 16;   // LDS bytes per row of a wave's K share (16-byte pad)
 
 template <int YDT>
@@ -414,7 +416,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_q8(const int8_t* __restric
                                                          const float* __restrict__ w_zp, int N,
                                                          const float* __restrict__ bias, void* __restrict__ y,
                                                          int32_t* __restrict__ acc_out, double y_inv) {
-  __shared__ __attribute__((aligned(16))) uint8_t wsm[kWaves][kRows * kWPitch];
   __shared__ __attribute__((aligned(16))) uint8_t csm[kWaves][kRows * kWPitch];
   __shared__ v4i part[kWaves][64];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -440,32 +441,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_q8(const int8_t* __restric
     s_m = x_scale[mc];
     r_m = x_rowsum[mc];
   }
-  uint8_t* const wl = wsm[wave];
   uint8_t* const cl = csm[wave];
   const int xr = lr < M ? lr : M - 1;     // code rows past M repeat the last: they feed unstored columns
+  // weights straight into registers, as in the fused kernel: 16 loads of 16
+  // bytes per lane (row n0 + lr, k-step s at s * 64 + 16 lg of the wave's
+  // quarter), non-temporal, one offset per lane through a buffer resource;
+  // past the segment they read the next row's bytes or the range check's
+  // zeros, against zero codes
+  const int wrow = (n0 + lr < N ? n0 + lr : N - 1);
+  const __amdgpu_buffer_rsrc_t wres = byte_buffer(wq, (uint32_t)N * (uint32_t)K);
+  v4i wv[kSteps];
   v4i acc = {0, 0, 0, 0};
   for (int k0 = 0; k0 < K; k0 += kSeg) {
     const int seg = (K - k0) < kSeg ? (K - k0) : kSeg;
     int c = wave * kKW + 16 * lane;
     c = c < seg ? c : seg - 16;                       // clamped; its codes are masked below
     if (k0 > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // this wave's reads of the last segment are done
-    // the wave's 1 KB share of each of the 16 weight rows, then of the 16 code
-    // rows: contiguous 1 KB per instruction (rows past N or M repeat the last)
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      const int n = n0 + i < N ? n0 + i : N - 1;
-      dma16((const uint8_t*)wq, (uint32_t)(n * K + k0 + c), wl + i * kWPitch);
-    }
+    // the wave's 1 KB share of each of the M code rows first (contiguous 1 KB
+    // per instruction), then the weights: the codes' wait leaves the weight
+    // loads in flight
     const int mr = M < kRows ? M : kRows;
     for (int i = 0; i < mr; ++i) dma16((const uint8_t*)xq, (uint32_t)(i * K + k0 + c), cl + i * kWPitch);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint32_t wbase = (uint32_t)(wrow * K + k0 + wave * kKW + lg * 16);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int o = s * 64 + lg * 16;
-      const v4i a = *(const v4i*)(wl + lr * kWPitch + o);
+    for (int st = 0; st < kSteps; ++st) wv[st] = load16_nt(wres, wbase + st * 64);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int o = st * 64 + lg * 16;
       v4i b = *(const v4i*)(cl + xr * kWPitch + o);
-      if (seg != kSeg && wave * kKW + s * 64 + lg * 16 >= seg) b = v4i{0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+      if (seg != kSeg && wave * kKW + st * 64 + lg * 16 >= seg) b = v4i{0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[st], b, acc, 0, 0, 0);
     }
   }
   part[wave][lane] = acc;
