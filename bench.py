@@ -54,9 +54,9 @@ METRIC = "q8_linear int8 TOPS (prefill) + GB/s (decode) and % of MI355X roofline
 # (x 2.0), WRITE_SIZE 262144 KiB (x 1.0).  Valid for the GEMM sources whose
 # hash is recorded here; after any change to them the figure is withheld.
 GEMM_TRAFFIC = {
-    "sources_sha256": "c5c3fbfe05428a954dd5db04f02125dc39a7edb572d237eef2a90c10fbd4bc95",
-    "fetch_kib": 90484.40, "fetch_scale": 262144.0 / 131085.38,
-    "write_kib": 57344.39, "write_scale": 262144.0 / 262144.00,
+    "sources_sha256": "c2b0db0a0c5e95cfbdd4bb769db1854c5d0c938ae512d706ab78791b73838857",
+    "fetch_kib": 90436.42, "fetch_scale": 262144.0 / 131085.62,
+    "write_kib": 57373.93, "write_scale": 262144.0 / 262144.00,
 }
 
 
@@ -554,6 +554,14 @@ def cpu_baselines(budget_s):
     return out
 
 
+_T0 = time.time()
+
+
+def progress(leg):
+    """One line on stderr as each leg finishes; stdout keeps the single JSON line."""
+    print(f"bench: {leg} done at {time.time() - _T0:.1f} s", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -589,6 +597,7 @@ def main():
         return
     if args.only in (None, "prefill"):
         pf = bench_prefill(dev, args.steps, args.warmup)
+        progress("prefill")
         M, N, K = pf["shape"]
         out.update({
             "value": round(pf["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
@@ -619,6 +628,7 @@ def main():
                                          "bytes_per_call": d["bytes_per_call"]}}
         out["decode"] = {"workload": "decode q_proj q8_linear, N = K = 4096, bf16, 32 rotating weight sets",
                          **dec}
+        progress("decode")
         wo = {}
         for M in (16, 1):
             d = bench_decode(dev, M, replays=max(4, args.steps // 4), mode="w8a16")
@@ -628,14 +638,17 @@ def main():
                                         "bytes_per_call": d["bytes_per_call"]}}
         out["decode_w8a16"] = {"workload": "weight-only q8_linear_w8a16 decode q_proj, N = K = 4096, bf16 x, "
                                            "32 rotating weight sets", **wo}
+        progress("decode_w8a16")
     if args.only in (None, "decomp"):
         d = bench_decomp(dev, args.steps, args.warmup)
+        progress("llm_int8")
         out["llm_int8"] = {"workload": "LLM.int8 decomposition 512x4096x4096 fp16, 6 outlier columns",
                            "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
                            "roofline": {k: round(v, 4) if isinstance(v, float) else v
                                         for k, v in d["roofline"].items()}}
     if args.only in (None, "fp8"):
         d = bench_fp8(dev, args.steps, args.warmup)
+        progress("fp8")
         out["fp8"] = {"workload": "FP8 e4m3 rowwise 4096x4096x14336 bf16, scale_ub 1200",
                       "ms_per_step": round(d["ms_per_step"], 5), "TFLOPS": round(d["tflops"], 1),
                       "gemm_us": round(d["gemm_us"], 2),
@@ -643,19 +656,23 @@ def main():
                                    for k, v in d["roofline"].items()}}
     if args.only is None:
         d = bench_moe_fp8(dev, args.steps, args.warmup)
+        progress("moe_fp8")
         T, N, K, E = d["shape"]
         out["moe_fp8"] = {"workload": f"FP8 expert projection, {T} routed tokens over {E} experts "
                                       f"{d['tokens_per_expert']}, N = K = {N}, bf16 out, ub 1200",
                           "ms_per_step": round(d["ms_per_step"], 5), "TFLOPS": round(d["tflops"], 1),
                           "frac_of_fp8_peak": round(d["tflops"] / PEAK_FP8_TFLOPS, 4)}
         d = bench_static(dev, args.steps, args.warmup)
+        progress("static_int8_out")
         out["static_int8_out"] = {"workload": "prefill FFN-up 2048x14336x4096, static activation scale, INT8 output "
                                               "(q8_linear_static: static quantization + int8 GEMM, float64 requantize)",
                                   "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
                                   "frac_of_int8_peak": round(d["tops"] / PEAK_INT8_TOPS, 4)}
         out["ceilings"] = bench_ceilings(dev, args.steps)
+        progress("ceilings")
     if args.only in (None, "grouped"):
         d = bench_grouped(dev, args.steps, args.warmup)
+        progress("grouped_prefill")
         out["grouped_prefill"] = {"workload": "prefill FFN-up 2048x14336x4096, per-group weights (group 128), "
                                               "q8_linear_grouped: row quantizer with group code sums + grouped GEMM",
                                   "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
@@ -669,8 +686,10 @@ def main():
                                         "bytes_per_call": d["bytes_per_call"]}}
         out["grouped_decode"] = {"workload": "q8_linear_grouped decode q_proj, N = K = 4096, group 128, bf16, "
                                              "32 rotating weight sets", **gd}
+        progress("grouped_decode")
     if args.only in (None, "prefill") and not args.no_cpu_baseline:
         cb = cpu_baselines(args.cpu_seconds)
+        progress("cpu_baseline")
         out["cpu_baseline"] = cb.pop("prefill")
         out["cpu_baseline_other_workloads"] = cb
     print(json.dumps(out), flush=True)
