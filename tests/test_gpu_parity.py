@@ -2,8 +2,11 @@
 inputs.  Integer results (codes, scale bit patterns, zero-points, row sums,
 INT32 accumulators, outlier sets) must match bit for bit; floating outputs
 within max relative error 1e-2 (floored at 0.1% of the largest output).
-Large workloads run at full size on the GPU and are compared on sampled rows
-the oracle computes one by one (every kernel here is row-independent in X)."""
+Large workloads run at full size on the GPU and are compared on every output,
+except two that are compared on sampled rows the oracle computes one by one
+(every kernel here is row-independent in X): the full-size FP8 GEMM, whose
+per-output error bound is built from all K products of each output, and the
+largest weight matrix (2^31 - 2^16 elements)."""
 import numpy as np
 import pytest
 import torch
@@ -204,18 +207,17 @@ def test_quantize_act_fp8_scale_ub(ub):
     assert_equal(f32_bits(host(xs)), f32_bits(rs), "scale bits")
 
 
-def test_quantize_fp8_full_size_sampled_rows():
-    log("[fp8 quant] 4096x14336 activations and weights, sampled rows")
+def test_quantize_fp8_full_size():
+    log("[fp8 quant] 4096x14336 activations and weights, every row")
     wl = inputs.fp8_rowwise()
     xq, xs, _ = q8.q8_quantize_act(g(wl.x), "fp8_e4m3", scale_ub=1200.0)
     wq, ws, _ = q8.q8_quantize_weight(g(wl.w), "fp8_e4m3")
-    rows = sample_rows(4096, 24, seed=1)
-    rq, rs = O.quantize_fp8_rowwise(wl.x[rows], 1200.0)
-    assert_equal(host(xq)[rows], rq, "activation codes")
-    assert_equal(f32_bits(host(xs)[rows]), f32_bits(rs), "activation scale bits")
-    rq, rs = O.quantize_fp8_rowwise(wl.w[rows])
-    assert_equal(host(wq)[rows], rq, "weight codes")
-    assert_equal(f32_bits(host(ws)[rows]), f32_bits(rs), "weight scale bits")
+    rq, rs = O.quantize_fp8_rowwise(wl.x, 1200.0)
+    assert_equal(host(xq), rq, "activation codes")
+    assert_equal(f32_bits(host(xs)), f32_bits(rs), "activation scale bits")
+    rq, rs = O.quantize_fp8_rowwise(wl.w)
+    assert_equal(host(wq), rq, "weight codes")
+    assert_equal(f32_bits(host(ws)), f32_bits(rs), "weight scale bits")
 
 
 # ---------------------------------------------------------------- q8_linear
@@ -272,11 +274,10 @@ def test_linear_decode_qproj_full_size(M):
     wq, ws, wz = q8.q8_quantize_weight(g(wl.w), "int8_asym")
     y, acc = q8.q8_linear(g(wl.x), wq, ws, wz, out_dtype=torch.bfloat16, acc_out=True)
     rq, rs, rz = oracle_weights(wl.w)
-    cols = np.sort(np.random.default_rng(M).choice(4096, 384, replace=False))
-    cols = np.unique(np.r_[cols, [0, 15, 16, 4095]])
-    y_ref, inter = O.linear_int8(wl.x, rq[cols], rs[cols], rz[cols])
-    assert_equal(host(acc)[:, cols], inter["acc"].astype(np.int32), "INT32 accumulator")
-    check_close(out_f64(y)[:, cols], y_ref, "output")
+    # every output: the oracle's integer product is one float64 BLAS call
+    y_ref, inter = O.linear_int8(wl.x, rq, rs, rz)
+    assert_equal(host(acc), inter["acc"].astype(np.int32), "INT32 accumulator")
+    check_close(out_f64(y), y_ref, "output")
 
 
 @pytest.mark.parametrize("M,N,K,dt", [(3, 100, 4112, torch.bfloat16),      # fused: two K segments, N tail
@@ -507,9 +508,7 @@ def run_w8a16_case(x, w, out_dtype, cols=None, bias=None, what=""):
 def test_w8a16_decode_qproj_full_size(M, dt):
     log(f"[w8a16] decode q_proj M={M} N=K=4096 {dt}")
     wl = inputs.decode_qproj(M=M)
-    cols = np.sort(np.random.default_rng(100 + M).choice(4096, 384, replace=False))
-    cols = np.unique(np.r_[cols, [0, 15, 16, 4095]])
-    run_w8a16_case(wl.x.to(dt), wl.w, torch.bfloat16, cols=cols, what=f"w8a16 M={M}")
+    run_w8a16_case(wl.x.to(dt), wl.w, torch.bfloat16, what=f"w8a16 M={M}")
 
 
 @pytest.mark.parametrize("M,N,K,dt", [(3, 100, 4112, torch.bfloat16),     # two K segments, N tail
@@ -546,11 +545,9 @@ def test_quantize_act_static_codes(name, M, K, dt, scale):
     log(f"[act static] {name} S={scale}")
     x = inputs.random_matrix(140 + M, (M, K), 1.0, dt)
     xq, rs = q8.q8_quantize_act_static(g(x), scale)
-    rows = None if M * K <= 1e6 else sample_rows(M, 24, seed=3)
-    xr = x if rows is None else x[rows]
-    rq, rr = O.quantize_act_int8_static(xr, scale)
-    assert_equal(host(xq) if rows is None else host(xq)[rows], rq, "static codes")
-    assert_equal(host(rs) if rows is None else host(rs)[rows], rr, "static row sums")
+    rq, rr = O.quantize_act_int8_static(x, scale)
+    assert_equal(host(xq), rq, "static codes")
+    assert_equal(host(rs), rr, "static row sums")
 
 
 def run_static_case(x, w, x_scale, rows=None, bias=None, clip_frac=0.2, what=""):
@@ -747,9 +744,7 @@ def test_quantize_weight_grouped_edge_groups():
 def test_linear_grouped_decode_qproj_full_size(M, group):
     log(f"[grouped] decode q_proj M={M} N=K=4096 group={group} bf16")
     wl = inputs.decode_qproj(M=M)
-    cols = np.sort(np.random.default_rng(M + group).choice(4096, 384, replace=False))
-    cols = np.unique(np.r_[cols, [0, 15, 16, 4095]])
-    run_grouped_linear_case(wl.x, wl.w, group, torch.bfloat16, cols=cols, what="decode")
+    run_grouped_linear_case(wl.x, wl.w, group, torch.bfloat16, what="decode")
 
 
 @pytest.mark.parametrize("M,N,K,group,dt", [(3, 100, 4224, 128, torch.bfloat16),   # decode: partial 2nd segment, N tail
@@ -770,11 +765,10 @@ def test_linear_grouped_ragged(M, N, K, group, dt):
     run_grouped_linear_case(x, w, group, torch.float32, what="ragged")
 
 
-def test_linear_grouped_prefill_full_size_sampled():
-    log("[grouped] prefill FFN-up 2048x14336x4096 group=128 bf16, sampled rows")
+def test_linear_grouped_prefill_full_size():
+    log("[grouped] prefill FFN-up 2048x14336x4096 group=128 bf16, whole matrix")
     wl = inputs.prefill_ffn_up()
-    rows = sample_rows(2048, 6, seed=8, extra=(127, 128, 1024))
-    y = run_grouped_linear_case(wl.x, wl.w, 128, torch.bfloat16, rows=rows, what="prefill")
+    y = run_grouped_linear_case(wl.x, wl.w, 128, torch.bfloat16, what="prefill")
     wq, ws, wz = q8.q8_quantize_weight_grouped(g(wl.w), 128)
     y2 = q8.q8_linear_grouped(g(wl.x), wq, ws, wz, 128, out_dtype=torch.bfloat16)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "second call differs"
