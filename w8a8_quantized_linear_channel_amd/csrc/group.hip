@@ -109,7 +109,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
                                                             const float* __restrict__ bias, void* __restrict__ y) {
   constexpr int SPG = GS / 64;         // k-steps per group
   constexpr int NG = kKW / GS;         // groups in a wave's share of a segment
-  __shared__ __attribute__((aligned(16))) uint8_t wsm[kWaves][kRows * kWPitch];
   __shared__ __attribute__((aligned(16))) uint8_t csm[kWaves][kRows * kWPitch];
   __shared__ v4f part[kWaves][64];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -127,55 +126,68 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
   // quad (clamped to the last quad past N; those outputs are not stored)
   const bool quad = (N & 3) == 0;
   const int q0 = n0 + 4 * lg < N ? n0 + 4 * lg : N - 4;
-  uint8_t* const wl = wsm[wave];
   uint8_t* const cl = csm[wave];
   const int xr = lr < M ? lr : M - 1;    // code rows past M repeat the last: they feed unstored columns
+  const int wrow = (n0 + lr < N ? n0 + lr : N - 1);
+  const __amdgpu_buffer_rsrc_t wres = byte_buffer(wq, (uint32_t)N * (uint32_t)K);
+  v4i wv[kSteps];
   v4f f = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int k0 = 0; k0 < K; k0 += kSeg) {
     const int seg = (K - k0) < kSeg ? (K - k0) : kSeg;
     int c = wave * kKW + 16 * lane;
     c = c < seg ? c : seg - 16;                          // clamped; its codes are masked below
     if (k0 > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // this wave's reads of the last segment are done
-#pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-      const int n = n0 + i < N ? n0 + i : N - 1;
-      dma16((const uint8_t*)wq, (uint32_t)(n * K + k0 + c), wl + i * kWPitch);
-    }
-    const int mr = M < kRows ? M : kRows;
-    for (int i = 0; i < mr; ++i) dma16((const uint8_t*)xq, (uint32_t)(i * K + k0 + c), cl + i * kWPitch);
-    // the parameters of the share's groups, issued before the wait below so
-    // they arrive with the DMA (groups past K are clamped and not used)
+    // the parameters of the share's groups first (groups past K are clamped
+    // and not used), then the wave's 1 KB share of each code row, then the
+    // weights straight into registers: the wait below leaves the weight
+    // loads in flight
+    // One branch around all the groups' loads, not one per group: a
+    // branch per group lets the compiler's wait insertion hold each group's
+    // loads until the previous group's have returned.
     float ps[NG][4], pz[NG][4];
     int pg[NG];
     const int g0 = (k0 + wave * kKW) / GS;
+    if (quad) {   // the lane's four columns are one aligned 16-byte quad
 #pragma unroll
-    for (int t = 0; t < NG; ++t) {
-      const int gi = g0 + t < G ? g0 + t : G - 1;
-      if (quad) {   // the lane's four columns are one aligned 16-byte quad
+      for (int t = 0; t < NG; ++t) {
+        const int gi = g0 + t < G ? g0 + t : G - 1;
         const v4f sv = *(const v4f*)(w_scale + gi * N + q0), zv = *(const v4f*)(w_zp + gi * N + q0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           ps[t][r] = sv[r];
           pz[t][r] = zv[r];
         }
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NG; ++t) {
+        const int gi = g0 + t < G ? g0 + t : G - 1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           ps[t][r] = w_scale[gi * N + nc[r]];
           pz[t][r] = w_zp[gi * N + nc[r]];
         }
       }
-      pg[t] = gsum[gi * M + mc];
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < NG; ++t) pg[t] = gsum[(g0 + t < G ? g0 + t : G - 1) * M + mc];
+    const int mr = M < kRows ? M : kRows;
+    for (int i = 0; i < mr; ++i) dma16((const uint8_t*)xq, (uint32_t)(i * K + k0 + c), cl + i * kWPitch);
+    // 16 loads of 16 bytes per lane (row n0 + lr, k-step s at s * 64 + 16 lg
+    // of the wave's quarter), non-temporal, through a buffer resource; past
+    // the segment they read the next row's bytes or the range check's zeros,
+    // against zero codes
+    const uint32_t wbase = (uint32_t)(wrow * K + k0 + wave * kKW + lg * 16);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) wv[st] = load16_nt(wres, wbase + st * 64);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
     v4i acc = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int o = s * 64 + lg * 16;
-      const v4i a = *(const v4i*)(wl + lr * kWPitch + o);
       v4i b = *(const v4i*)(cl + xr * kWPitch + o);
       if (seg != kSeg && wave * kKW + s * 64 + lg * 16 >= seg) b = v4i{0, 0, 0, 0};
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[s], b, acc, 0, 0, 0);
       if ((s + 1) % SPG == 0) {
         const int t = s / SPG;
         if (wave * kKW + t * GS < seg) {
