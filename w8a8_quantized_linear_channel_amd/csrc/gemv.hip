@@ -173,28 +173,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   auto load_groups = [&](int k0) __attribute__((always_inline)) {
     if constexpr (GS > 0) {
       const int G = K / GS, g0 = (k0 + wave * kKW) / GS;
-      // N a multiple of 4: the lane's columns are one aligned 16-byte quad
-      // (clamped to the last quad past N; those outputs are not stored)
-      const bool quad = (N & 3) == 0;
-      const int q0 = n0 + 4 * lg < N ? n0 + 4 * lg : N - 4;
+      // The lane's four columns, clamped to the last one past N (those
+      // outputs are not stored), one 4-byte load each: no branch between the
+      // weight loads issued before and these, since the compiler's wait
+      // insertion holds loads under a branch until earlier ones (here the
+      // weights) have returned.
+      int nc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nc[r] = n0 + 4 * lg + r < N ? n0 + 4 * lg + r : N - 1;
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
         const int gi = g0 + t < G ? g0 + t : G - 1;
-        if (quad) {
-          const v4f sv = *(const v4f*)(w_scale + gi * N + q0), zv = *(const v4f*)(w_zp + gi * N + q0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            gsc[t][r] = sv[r];
-            gzp[t][r] = zv[r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int n = n0 + 4 * lg + r;
-            const int nc = n < N ? n : N - 1;
-            gsc[t][r] = w_scale[gi * N + nc];
-            gzp[t][r] = w_zp[gi * N + nc];
-          }
+        for (int r = 0; r < 4; ++r) {
+          gsc[t][r] = w_scale[gi * N + nc[r]];
+          gzp[t][r] = w_zp[gi * N + nc[r]];
         }
       }
     }
