@@ -104,7 +104,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_w8a16(const uint16_t* __re
   const int xr = lr < M ? lr : M - 1;
   const v4i ones = DT == DT_BF16 ? v4i{0x3f803f80, 0x3f803f80, 0x3f803f80, 0x3f803f80} : v4i{0, 0, 0, 0};
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f}, accs = {0.0f, 0.0f, 0.0f, 0.0f};
+  // Epilogue factors (wave 0), requested before the activations and the
+  // weights.  Requested after the weights, by wave 0 only, they made the
+  // compiler's merged wait count hold wave 0's first MFMA until nearly all
+  // its weights had arrived, and wave 0 finished last.
   float fsc[4] = {0, 0, 0, 0}, fzp[4] = {0, 0, 0, 0}, fbi[4] = {0, 0, 0, 0};
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + 4 * lg + r;
+      const int nc = n < N ? n : N - 1;
+      fsc[r] = w_scale[nc];
+      fzp[r] = w_zp[nc];
+      fbi[r] = bias ? bias[nc] : 0.0f;
+    }
+  }
 
   for (int k0 = 0; k0 < K; k0 += kSeg) {
     const int seg = (K - k0) < kSeg ? (K - k0) : kSeg;
@@ -133,16 +147,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_w8a16(const uint16_t* __re
         zfix = hb | (hb << 16);
       }
     }
-    if (k0 == 0 && wave == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n0 + 4 * lg + r;
-        const int nc = n < N ? n : N - 1;
-        fsc[r] = w_scale[nc];
-        fzp[r] = w_zp[nc];
-        fbi[r] = bias ? bias[nc] : 0.0f;
-      }
-    }
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       v4i a0, a1;
@@ -155,6 +159,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_w8a16(const uint16_t* __re
         acc = mma16<DT>(j == 0 ? a0 : a1, b, acc);
         if constexpr (DT == DT_BF16) accs = mma16<DT>(ones, b, accs);
       }
+      // one k-step at a time, in order: left free, the scheduler hoists the
+      // widening of many k-steps above the first MFMAs, and with it the
+      // waits for their weights
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
