@@ -68,6 +68,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   __shared__ float rscale[kRows];
   __shared__ int rsum[kRows];
   __shared__ v4i part[kWaves][64];
+  // per-channel factors of the 16 columns, one 1 KB DMA by wave 0: scales at
+  // [0, 16), zero points at [16, 32), biases at [32, 48); the rest unused
+  __shared__ __attribute__((aligned(16))) float fac[256];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -130,6 +133,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     const uint32_t base = (uint32_t)(wrow * K + k0 + wave * kKW + lg * 16);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) wv[s] = load16_nt(wres, base + s * 64);
+  };
+  // Per channel, with all 16 columns present, wave 0 requests the epilogue
+  // factors by one DMA between the first and second half of its weights:
+  // requested with X they delay X, and requested after the weights (as
+  // vector loads, below) they arrive after the last weight and hold up the
+  // epilogue.  Lane l fetches 16 bytes: chunk l % 4 of the scales (l < 4 or
+  // l >= 12), zero points (4 <= l < 8) or biases (8 <= l < 12).
+  const bool fac_dma = GS == 0 && n0 + kRows <= N;
+  auto load_w_first = [&]() __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(wrow * K + wave * kKW + lg * 16);
+#pragma unroll
+    for (int s = 0; s < kSteps / 2; ++s) wv[s] = load16_nt(wres, base + s * 64);
+    if (fac_dma && wave == 0) {
+      const int arr = lane >> 2;
+      const float* src = arr == 1 ? w_zp : (arr == 2 && bias ? bias : w_scale);
+      dma16_ptr(src + n0 + 4 * (lane & 3), (uint8_t*)fac);
+    }
+#pragma unroll
+    for (int s = kSteps / 2; s < kSteps; ++s) wv[s] = load16_nt(wres, base + s * 64);
   };
   // epilogue factors (wave 0): acc register r of lane (lr, lg) is
   // D[n = 4 lg + r][m = lr].
@@ -199,10 +221,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
       if (sg > 0) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);   // reads of the last segment are done
       dma_x(k0, seg);
     }
-    if (sg == 0) load_w(0);
+    if (sg == 0) load_w_first();
     if constexpr (DT != DT_F32) {
       // this segment's X: everything but the 16 weight loads issued last
+      // (and wave 0's factor DMA among them)
       if (sg > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if (fac_dma && wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps + 1) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
     }
     // issued after the wait, so X does not wait for them; they have the
@@ -217,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
       }
       if (sg == 0) load_groups(k0);
     } else {
-      if (sg == 0 && wave == 0) load_factors();
+      if (sg == 0 && wave == 0 && !fac_dma) load_factors();
     }
 #pragma unroll 4
     for (int m = 0; m < M; ++m) {
@@ -357,6 +381,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   }
   __syncthreads();
   if (wave == 0) {
+    if (fac_dma) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the factor DMA (this wave's)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        fsc[r] = fac[4 * lg + r];
+        fzp[r] = fac[16 + 4 * lg + r];
+        fbi[r] = fac[32 + 4 * lg + r];
+      }
+    }
     v4i t = part[0][lane];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) t += part[w][lane];

@@ -264,6 +264,14 @@ __device__ __forceinline__ void dma16(const uint8_t* gbase, uint32_t voff, uint8
                : "s"(m0), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+// As dma16, from a per-lane 64-bit address.
+__device__ __forceinline__ void dma16_ptr(const void* gp, uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gp)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 }  // namespace q8
