@@ -90,6 +90,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_w8a16(const uint16_t* __re
   __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves][kRows * kXPitch];
   __shared__ v4f part[kWaves][64];
   __shared__ v4f psum[kWaves][64];
+  // per-channel factors of the 16 columns, one 1 KB DMA by wave 0: scales at
+  // [0, 16), zero points at [16, 32), biases at [32, 48)
+  __shared__ __attribute__((aligned(16))) float fac[256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -104,12 +107,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_w8a16(const uint16_t* __re
   const int xr = lr < M ? lr : M - 1;
   const v4i ones = DT == DT_BF16 ? v4i{0x3f803f80, 0x3f803f80, 0x3f803f80, 0x3f803f80} : v4i{0, 0, 0, 0};
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f}, accs = {0.0f, 0.0f, 0.0f, 0.0f};
-  // Epilogue factors (wave 0), requested before the activations and the
-  // weights.  Requested after the weights, by wave 0 only, they made the
-  // compiler's merged wait count hold wave 0's first MFMA until nearly all
-  // its weights had arrived, and wave 0 finished last.
+  // Epilogue factors (wave 0).  With all 16 columns present they come by one
+  // DMA between the two halves of the first segment's weight loads: they
+  // neither delay the activations nor arrive after the last weight.
+  // Otherwise (the last workgroup of a ragged N) by vector loads here, ahead
+  // of the activations.  (Vector loads after the weights, by wave 0 only,
+  // made the compiler's merged wait count hold wave 0's first MFMA until
+  // nearly all its weights had arrived.)
+  const bool fac_dma = n0 + kRows <= N;
   float fsc[4] = {0, 0, 0, 0}, fzp[4] = {0, 0, 0, 0}, fbi[4] = {0, 0, 0, 0};
-  if (wave == 0) {
+  if (wave == 0 && !fac_dma) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = n0 + 4 * lg + r;
@@ -135,10 +142,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_w8a16(const uint16_t* __re
     }
     v4i wv[kSteps];
     const uint32_t wbase = (uint32_t)(wrow * K + k0 + wave * kKW + lg * 16);
+    const bool fdma = k0 == 0 && fac_dma && wave == 0;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) wv[s] = load16_nt(wres, wbase + s * 64);
+    for (int s = 0; s < kSteps / 2; ++s) wv[s] = load16_nt(wres, wbase + s * 64);
+    if (fdma) {
+      // lane l: chunk l % 4 of the scales (l < 4 or l >= 12), zero points
+      // (4 <= l < 8) or biases (8 <= l < 12)
+      const int arr = lane >> 2;
+      const float* src = arr == 1 ? w_zp : (arr == 2 && bias ? bias : w_scale);
+      dma16_ptr(src + n0 + 4 * (lane & 3), (uint8_t*)fac);
+    }
+#pragma unroll
+    for (int s = kSteps / 2; s < kSteps; ++s) wv[s] = load16_nt(wres, wbase + s * 64);
     // the activations are in: everything but the 16 weight loads issued last
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
+    // (and the factor DMA among them)
+    if (fdma) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps + 1) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
     if constexpr (DT == DT_F16) {
       if (k0 == 0) {
         asm volatile("" : "+v"(zraw));
@@ -169,6 +188,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_w8a16(const uint16_t* __re
   part[wave][lane] = acc;
   psum[wave][lane] = accs;
   __syncthreads();
+  if (wave == 0 && fac_dma) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the factor DMA (this wave's)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      fsc[r] = fac[4 * lg + r];
+      fzp[r] = fac[16 + 4 * lg + r];
+      fbi[r] = bias ? fac[32 + 4 * lg + r] : 0.0f;
+    }
+  }
   if (wave == 0 && lr < M) {
     v4f t = part[0][lane], ts = psum[0][lane];
 #pragma unroll
