@@ -71,6 +71,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   // per-channel factors of the 16 columns, one 1 KB DMA by wave 0: scales at
   // [0, 16), zero points at [16, 32), biases at [32, 48); the rest unused
   __shared__ __attribute__((aligned(16))) float fac[256];
+  // per-group weights of 128: each wave's 8 groups' scales and zero points
+  // for the 16 columns, one 1 KB DMA per wave (group t's scales at
+  // [32 t, 32 t + 16), its zero points at [32 t + 16, 32 t + 32))
+  __shared__ __attribute__((aligned(16))) float gpar[GS == 128 ? kWaves : 1][256];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,11 +144,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   // vector loads, below) they arrive after the last weight and hold up the
   // epilogue.  Lane l fetches 16 bytes: chunk l % 4 of the scales (l < 4 or
   // l >= 12), zero points (4 <= l < 8) or biases (8 <= l < 12).
-  const bool fac_dma = GS == 0 && n0 + kRows <= N;
+  // (Per group, only the biases of that DMA are used.)  With groups of 128
+  // and N a multiple of 4, every wave fetches its groups' parameters the
+  // same way, by one DMA after its first four weight loads: loaded after X,
+  // they held the folds, and with them the MFMAs past the first group, until
+  // after the last weight.  Lane l fetches 16 bytes: chunk l % 4 of the
+  // scales (bit 2 of l clear) or zero points (set) of group l / 8.
+  const bool fac_dma = n0 + kRows <= N;
+  const bool gp_dma = GS == 128 && n0 + kRows <= N && (N & 3) == 0;
   auto load_w_first = [&]() __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)(wrow * K + wave * kKW + lg * 16);
 #pragma unroll
-    for (int s = 0; s < kSteps / 2; ++s) wv[s] = load16_nt(wres, base + s * 64);
+    for (int s = 0; s < kSteps / 4; ++s) wv[s] = load16_nt(wres, base + s * 64);
+    if constexpr (GS == 128) {
+      if (gp_dma) {
+        const int G = K / GS;
+        const int t = lane >> 3, g = wave * (kKW / GS) + t < G ? wave * (kKW / GS) + t : G - 1;
+        const float* src = ((lane >> 2) & 1) ? w_zp : w_scale;
+        dma16_ptr(src + (size_t)g * N + n0 + 4 * (lane & 3), (uint8_t*)gpar[wave]);
+      }
+    }
+#pragma unroll
+    for (int s = kSteps / 4; s < kSteps / 2; ++s) wv[s] = load16_nt(wres, base + s * 64);
     if (fac_dma && wave == 0) {
       const int arr = lane >> 2;
       const float* src = arr == 1 ? w_zp : (arr == 2 && bias ? bias : w_scale);
@@ -226,20 +247,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
       // this segment's X: everything but the 16 weight loads issued last
       // (and wave 0's factor DMA among them)
       if (sg > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else if (fac_dma && wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps + 1) : "memory");
+      else if (gp_dma && fac_dma && wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps + 2) : "memory");
+      else if (gp_dma || (fac_dma && wave == 0)) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps + 1) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
     }
     // issued after the wait, so X does not wait for them; they have the
     // whole coding and MFMA phase to arrive
     if constexpr (GS > 0) {
-      if (sg == 0 && wave == 0) {
+      if (sg == 0 && wave == 0 && !fac_dma) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int n = n0 + 4 * lg + r;
           fbi[r] = bias ? bias[n < N ? n : N - 1] : 0.0f;
         }
       }
-      if (sg == 0) load_groups(k0);
+      if (sg == 0 && !gp_dma) load_groups(k0);
     } else {
       if (sg == 0 && wave == 0 && !fac_dma) load_factors();
     }
@@ -315,6 +337,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
       }
     } else {
       if (sg > 0) load_groups(k0);   // pass 1 loaded segment 0's groups
+      if constexpr (GS == 128) {
+        if (sg == 0 && gp_dma) {
+          // this wave's parameter DMA: issued after its first 4 weight loads,
+          // followed by 12 more (and wave 0's factor DMA)
+          if (fac_dma && wave == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps - kSteps / 4 + 1) : "memory");
+          else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps - kSteps / 4) : "memory");
+#pragma unroll
+          for (int t = 0; t < NG; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              gsc[t][r] = gpar[wave][32 * t + 4 * lg + r];
+              gzp[t][r] = gpar[wave][32 * t + 16 + 4 * lg + r];
+            }
+        }
+      }
       const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
@@ -352,6 +389,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     // the four fp32 partial tiles meet in LDS; wave 0 scales by S_x
     part[wave][lane] = __builtin_bit_cast(v4i, fsum);
     __syncthreads();
+    if (wave == 0 && fac_dma) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the factor DMA (this wave's)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fbi[r] = fac[32 + 4 * lg + r];
+    }
     if (wave == 0) {
       v4f t = __builtin_bit_cast(v4f, part[0][lane]);
 #pragma unroll
