@@ -111,6 +111,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
   constexpr int NG = kKW / GS;         // groups in a wave's share of a segment
   __shared__ __attribute__((aligned(16))) uint8_t csm[kWaves][kRows * kWPitch];
   __shared__ v4f part[kWaves][64];
+  // groups of 128: each wave's 8 groups' scales and zero points for the 16
+  // columns, one 1 KB DMA per wave and segment (group t's scales at
+  // [32 t, 32 t + 16), its zero points at [32 t + 16, 32 t + 32))
+  __shared__ __attribute__((aligned(16))) float gpar[GS == 128 ? kWaves : 1][256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -141,31 +145,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
     // and not used), then the wave's 1 KB share of each code row, then the
     // weights straight into registers: the wait below leaves the weight
     // loads in flight
-    // One branch around all the groups' loads, not one per group: a
-    // branch per group lets the compiler's wait insertion hold each group's
-    // loads until the previous group's have returned.
+    // The parameters of the share's groups (groups past K are clamped and
+    // not used).  With groups of 128, N a multiple of 4 and all 16 columns
+    // present, by one DMA after the first four weight loads (gp); else by
+    // vector loads here, ahead of the codes, under one branch around all the
+    // groups' loads (a branch per group let the compiler's wait insertion
+    // hold each group's loads until the previous group's had returned).
+    const bool gp = GS == 128 && quad && n0 + kRows <= N;
     float ps[NG][4], pz[NG][4];
     int pg[NG];
     const int g0 = (k0 + wave * kKW) / GS;
-    if (quad) {   // the lane's four columns are one aligned 16-byte quad
+    if (!gp) {
+      if (quad) {   // the lane's four columns are one aligned 16-byte quad
 #pragma unroll
-      for (int t = 0; t < NG; ++t) {
-        const int gi = g0 + t < G ? g0 + t : G - 1;
-        const v4f sv = *(const v4f*)(w_scale + gi * N + q0), zv = *(const v4f*)(w_zp + gi * N + q0);
+        for (int t = 0; t < NG; ++t) {
+          const int gi = g0 + t < G ? g0 + t : G - 1;
+          const v4f sv = *(const v4f*)(w_scale + gi * N + q0), zv = *(const v4f*)(w_zp + gi * N + q0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ps[t][r] = sv[r];
-          pz[t][r] = zv[r];
+          for (int r = 0; r < 4; ++r) {
+            ps[t][r] = sv[r];
+            pz[t][r] = zv[r];
+          }
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int t = 0; t < NG; ++t) {
-        const int gi = g0 + t < G ? g0 + t : G - 1;
+        for (int t = 0; t < NG; ++t) {
+          const int gi = g0 + t < G ? g0 + t : G - 1;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ps[t][r] = w_scale[gi * N + nc[r]];
-          pz[t][r] = w_zp[gi * N + nc[r]];
+          for (int r = 0; r < 4; ++r) {
+            ps[t][r] = w_scale[gi * N + nc[r]];
+            pz[t][r] = w_zp[gi * N + nc[r]];
+          }
         }
       }
     }
@@ -179,8 +189,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(const int8_t* __rest
     // against zero codes
     const uint32_t wbase = (uint32_t)(wrow * K + k0 + wave * kKW + lg * 16);
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) wv[st] = load16_nt(wres, wbase + st * 64);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
+    for (int st = 0; st < kSteps / 4; ++st) wv[st] = load16_nt(wres, wbase + st * 64);
+    if constexpr (GS == 128) {
+      if (gp) {
+        // lane l: chunk l % 4 of the scales (bit 2 of l clear) or zero
+        // points (set) of group g0 + l / 8
+        const int t = lane >> 3, gi = g0 + t < G ? g0 + t : G - 1;
+        const float* src = ((lane >> 2) & 1) ? w_zp : w_scale;
+        dma16_ptr(src + (size_t)gi * N + n0 + 4 * (lane & 3), (uint8_t*)gpar[wave]);
+      }
+    }
+#pragma unroll
+    for (int st = kSteps / 4; st < kSteps; ++st) wv[st] = load16_nt(wres, wbase + st * 64);
+    // the codes are in: everything but the weight loads (and the parameter
+    // DMA among them)
+    if (gp) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps + 1) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps) : "memory");
+    if constexpr (GS == 128) {
+      if (gp) {
+        // the parameter DMA, followed by 12 weight loads
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSteps - kSteps / 4) : "memory");
+#pragma unroll
+        for (int t = 0; t < NG; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            ps[t][r] = gpar[wave][32 * t + 4 * lg + r];
+            pz[t][r] = gpar[wave][32 * t + 16 + 4 * lg + r];
+          }
+      }
+    }
     v4i acc = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
