@@ -284,6 +284,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
     if constexpr (KIND != GEMM_FP8) pf_zi = (int)g.b_zp[n];
     pf_bb = g.bias ? g.bias[n] : 0.0f;
   }
+  // LLM.int8: the outlier count and the first 16 outlier columns, requested
+  // now (the list holds K entries, K >= 16), so that the epilogue's outlier
+  // flow does not begin with two dependent round trips (count, then list)
+  int pf_cnt = 0, pf_col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (KIND == GEMM_INT8_DECOMP) {
+    pf_cnt = *g.out_cnt;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf_col[e] = g.out_idx[(lane >> 5) * 8 + e];
+  }
 
   // ---- DMA loader.  One wave instruction fills 1 KB = 16 LDS rows; lane l
   // lands at row l/4, physical chunk l%4, which holds logical chunk
@@ -533,23 +542,56 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
           acc[i][j][r] = __float_as_int((sx * f_sb[nl]) * (float)(a - f_zi[nl] * rs));
         }
     }
-    const int cnt = *g.out_cnt;
+    // the prefetched count and columns are first used here (the empty asm
+    // keeps their uses from being hoisted next to their loads)
+    asm volatile("" : "+v"(pf_cnt));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(pf_col[e]));
+    const int cnt = pf_cnt;
     const int kg = lane >> 5;                          // 8-column group of the 16-column step
     for (int kc = 0; kc < cnt; kc += 16) {
       int col[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int jj = kc + kg * 8 + e;
-        col[e] = jj < cnt ? g.out_idx[jj] : -1;
+        col[e] = jj < cnt ? (kc == 0 ? pf_col[e] : g.out_idx[jj]) : -1;
       }
+      // Every load is issued unconditionally, at a clamped address, and all
+      // of them before any is used; each value is zeroed afterwards where its
+      // column or row does not exist.  (Written as `cond ? load : 0`, the
+      // compiler moved each load under a branch and waited for it before
+      // issuing the next: 8 + 8 round trips in a row.)  The empty asm
+      // statements take every loaded value after the last load is issued.
+      uint32_t xr[TL::FM][8], wr[TL::FN][8];
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i) {
+        const int m = m0 + mw + i * 32 + lm;
+        const int mc = m < M ? m : M - 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xr[i][e] = g.x_f16[mc * K + (col[e] >= 0 ? col[e] : 0)];
+      }
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) {
+        const int n = n0 + nw + j * 32 + lm;
+        const int ncl = n < N ? n : N - 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wr[j][e] = (uint32_t)(uint8_t)g.b[ncl * K + (col[e] >= 0 ? col[e] : 0)];
+      }
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(xr[i][e]));
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(wr[j][e]));
       v8h xo[TL::FM], wo[TL::FN];
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i) {
         const int m = m0 + mw + i * 32 + lm;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          xo[i][e] = (col[e] >= 0 && m < M) ? __builtin_bit_cast(_Float16, g.x_f16[m * K + col[e]])
-                                            : (_Float16)0.0f;
+          xo[i][e] = (col[e] >= 0 && m < M) ? __builtin_bit_cast(_Float16, (uint16_t)xr[i][e]) : (_Float16)0.0f;
       }
 #pragma unroll
       for (int j = 0; j < TL::FN; ++j) {
@@ -557,8 +599,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
         const bool nok = n < N;
         const float sb = f_sb[nl], zb = (float)f_zi[nl];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          wo[j][e] = (col[e] >= 0 && nok) ? outlier_weight_f16(sb, (int8_t)g.b[n * K + col[e]], zb) : (_Float16)0.0f;
+        for (int e = 0; e < 8; ++e) {
+          const _Float16 w = outlier_weight_f16(sb, (int8_t)(uint8_t)wr[j][e], zb);
+          wo[j][e] = (col[e] >= 0 && nok) ? w : (_Float16)0.0f;
+        }
       }
 #pragma unroll
       for (int i = 0; i < TL::FM; ++i)
