@@ -162,7 +162,10 @@ q8_status q8_linear(const void* x, q8_dtype x_dtype, int64_t M, int64_t K,
  * NULL.  Both stay on the device: the call never synchronizes.
  * acc_out: int32 [M, N] debug copy of the int8-path accumulator, or NULL.
  * threshold NaN is Q8_ERR_BAD_ARG.
- * workspace: q8_workspace_bytes(Q8_OP_DECOMP, M, N, K) bytes.
+ * workspace: q8_workspace_bytes(Q8_OP_DECOMP, M, N, K) bytes: the activation
+ * codes, scales and row sums, the column flags, the outlier list and count,
+ * and the first 16 outlier columns of X and of W_O in compact fp16 form
+ * ((M + N) x 32 bytes), which the product reads instead of gathering them.
  */
 q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K,
                                 const int8_t* wq, const float* w_scale,

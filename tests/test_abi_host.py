@@ -63,9 +63,10 @@ def test_workspace_sizes():
     # GEMM path: codes + scale + row sum, each 256-byte aligned
     assert ws(_lib.Q8_OP_LINEAR, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192
     assert ws(_lib.Q8_OP_FP8, 4096, 4096, 14336) == 4096 * 14336 + 16384
-    # decomposition: codes, scale, row sum, column flags, outlier list, count
+    # decomposition: codes, scale, row sum, column flags, outlier list, count,
+    # and the fp16 panels of the first 16 outlier columns of X and W
     d = ws(_lib.Q8_OP_DECOMP, 512, 4096, 4096)
-    assert d == 512 * 4096 + 2048 + 2048 + 4096 + 4096 * 4 + 256
+    assert d == 512 * 4096 + 2048 + 2048 + 4096 + 4096 * 4 + 256 + 512 * 32 + 4096 * 32
     # static path: codes, per-row scale copy and code sums at every M
     assert ws(_lib.Q8_OP_STATIC, 1, 4096, 4096) == 4096 + 2 * 256
     assert ws(_lib.Q8_OP_STATIC, 2048, 14336, 4096) == 2048 * 4096 + 2 * 8192

@@ -412,6 +412,19 @@ def test_decomp_thresholds(tau):
     run_decomp_case(wl.x, wl.w, tau, what=f"tau={tau}")
 
 
+@pytest.mark.parametrize("n_cols,M,N,K", [(16, 200, 520, 1024), (17, 200, 520, 1024), (21, 333, 700, 2048),
+                                          (40, 64, 4096, 4096)])
+def test_decomp_more_outliers_than_the_panels(n_cols, M, N, K):
+    """The first 16 outlier columns reach the GEMM through the quantizer's
+    compact fp16 panels and any further ones through its gather path: exactly
+    16, one more, and several chunks past the panels, on ragged and tile-
+    aligned shapes, with the whole INT32 accumulator and every output."""
+    log(f"[decomp] {n_cols} outlier columns: M={M} N={N} K={K}")
+    wl = inputs.llm_int8_outliers(seed=40 + n_cols, M=M, K=K, N=N, n_outlier_cols=n_cols)
+    run_decomp_case(wl.x, wl.w, 6.0, what=f"{n_cols} outliers")
+    assert len(O.outlier_columns(wl.x, 6.0)) == n_cols
+
+
 def test_decomp_exact_threshold_and_bias():
     log("[decomp] entries exactly at 6.0, bias, ragged shapes")
     x = inputs.random_matrix(80, (45, 2064), 1.0, torch.float32).numpy().clip(-3.5, 3.5)

@@ -118,8 +118,10 @@ GroupedWs grouped_ws(int64_t M, int64_t K) {
 }
 bool valid_group(int64_t group, int64_t K) { return (group == 64 || group == 128) && K % group == 0; }
 
-struct DecompWs { size_t xq, xs, rs, flags, idx, cnt, total; };
-DecompWs decomp_ws(int64_t M, int64_t K) {
+// LLM.int8: codes, scales, row sums, column flags, outlier list and count,
+// and the fp16 panels of the first kPanelCols outlier columns of X and W.
+struct DecompWs { size_t xq, xs, rs, flags, idx, cnt, xp, wp, total; };
+DecompWs decomp_ws(int64_t M, int64_t N, int64_t K) {
   if (M == 0) return DecompWs{};   // an empty batch needs no scratch
   Carve c;
   DecompWs w;
@@ -129,6 +131,8 @@ DecompWs decomp_ws(int64_t M, int64_t K) {
   w.flags = c.take((size_t)K);
   w.idx = c.take((size_t)K * 4);
   w.cnt = c.take(4);
+  w.xp = c.take((size_t)M * q8::kPanelCols * 2);
+  w.wp = c.take((size_t)N * q8::kPanelCols * 2);
   w.total = c.off;
   return w;
 }
@@ -274,7 +278,7 @@ size_t q8_workspace_bytes(q8_op op, int64_t M, int64_t N, int64_t K) {
   if (check_mnk(M, N, K) != Q8_OK) return 0;
   switch (op) {
     case Q8_OP_LINEAR: return linear_ws(M, K).total;
-    case Q8_OP_DECOMP: return decomp_ws(M, K).total;
+    case Q8_OP_DECOMP: return decomp_ws(M, N, K).total;
     case Q8_OP_FP8: return fp8_ws(M, K).total;
     case Q8_OP_STATIC: return static_ws(M, K).total;
     case Q8_OP_GROUPED: return grouped_ws(M, K).total;
@@ -344,7 +348,7 @@ q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_
   Q8_TRY(check_mnk(M, N, K));
   if (!wq || !w_scale || !w_zp || (M > 0 && (!x || !y))) return Q8_ERR_NULL_PTR;
   if (std::isnan(threshold)) return Q8_ERR_BAD_ARG;
-  const DecompWs ws = decomp_ws(M, K);
+  const DecompWs ws = decomp_ws(M, N, K);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return Q8_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_zp) || !aligned16(y) ||
       !aligned16(workspace) || (bias && !aligned16(bias)) || (acc_out && !aligned16(acc_out)) ||
@@ -358,7 +362,7 @@ q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_
     // by the quantizer's compaction workgroup alone (no flags, no rows)
     if (n_outliers)
       return launched(q8::launch_quant_act_f16_outliers(nullptr, 0, K, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                                        n_outliers, nullptr, nullptr, st));
+                                                        n_outliers, nullptr, nullptr, q8::OutlierPanels{}, st));
     return Q8_OK;
   }
 
@@ -369,13 +373,17 @@ q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_
   uint8_t* flags = reinterpret_cast<uint8_t*>(base + ws.flags);
   int32_t* idx = reinterpret_cast<int32_t*>(base + ws.idx);
   int32_t* cnt = reinterpret_cast<int32_t*>(base + ws.cnt);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(base + ws.xp);
+  uint16_t* wp = reinterpret_cast<uint16_t*>(base + ws.wp);
   const uint16_t* xh = static_cast<const uint16_t*>(x);
 
   // threshold <= 0: no outlier columns (the decomposition is off)
   const bool on = threshold > 0.0f;
   if (on) Q8_TRY(launched(q8::launch_outlier_flags(xh, M, K, threshold, flags, st)));
+  // the panels are needed only when there can be outlier columns
+  const q8::OutlierPanels pan{wq, w_scale, w_zp, N, on ? xp : nullptr, wp};
   Q8_TRY(launched(q8::launch_quant_act_f16_outliers(xh, M, K, on ? flags : nullptr, xq, xs, rs, idx, cnt,
-                                                    outlier_idx, n_outliers, st)));
+                                                    outlier_idx, n_outliers, pan, st)));
   q8::GemmArgs g{};
   g.a = reinterpret_cast<const uint8_t*>(xq);
   g.b = reinterpret_cast<const uint8_t*>(wq);
@@ -392,6 +400,8 @@ q8_status q8_linear_int8_decomp(const void* x, int64_t M, int64_t K, const int8_
   g.x_f16 = xh;
   g.out_idx = idx;
   g.out_cnt = cnt;
+  g.x_panel = xp;
+  g.w_panel = wp;
   return launched(q8::launch_gemm(q8::GEMM_INT8_DECOMP, g, Q8_F16, st));
 }
 

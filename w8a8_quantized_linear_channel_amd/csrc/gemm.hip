@@ -56,19 +56,6 @@ constexpr int kMaxGroupsDev = 1024;   // groups (experts) of one grouped call
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-// Outlier weight of the LLM.int8 flow: fp16(fp32(S (q - Z))), the product
-// rounded to fp32 before the conversion to fp16, as the dequantized fp32
-// weights are cast to fp16.  Left alone, the compiler fuses the multiply and
-// the conversion into one v_fma_mixlo_f16 (even with contraction off), which
-// rounds the exact product to fp16 once and differs from the two roundings
-// next to a tie of fp16; the empty asm makes the fp32 product a value of its
-// own.
-__device__ __forceinline__ _Float16 outlier_weight_f16(float s, int q, float z) {
-  float p = s * ((float)q - z);
-  asm volatile("" : "+v"(p));
-  return (_Float16)p;
-}
-
 // One MFMA shape.  A fragment row is (base multiple of 32) + lane % 32, so
 // ((row >> 2) & 3) == ((lane >> 2) & 3) and the swizzled byte offset of the
 // lane's operand inside its LDS row is lane_off(lane) XOR a per-k-step constant.
@@ -284,14 +271,28 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
     if constexpr (KIND != GEMM_FP8) pf_zi = (int)g.b_zp[n];
     pf_bb = g.bias ? g.bias[n] : 0.0f;
   }
-  // LLM.int8: the outlier count and the first 16 outlier columns, requested
-  // now (the list holds K entries, K >= 16), so that the epilogue's outlier
-  // flow does not begin with two dependent round trips (count, then list)
-  int pf_cnt = 0, pf_col[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // LLM.int8: the outlier count and this lane's 16 bytes of the panels of
+  // the first kPanelCols outlier columns (fragment rows m and n, 8-column
+  // group lane / 32), requested now so that the epilogue's outlier flow does
+  // not begin with a round trip.  Rows past M or N read the last row; their
+  // outputs are not stored.
+  int pf_cnt = 0;
+  v4i pf_xo[TL::FM], pf_wo[TL::FN];
   if constexpr (KIND == GEMM_INT8_DECOMP) {
     pf_cnt = *g.out_cnt;
+    const int kg0 = lane >> 5, lm0 = lane & 31;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pf_col[e] = g.out_idx[(lane >> 5) * 8 + e];
+    for (int i = 0; i < TL::FM; ++i) {
+      const int m = m0 + wm * TL::TM + i * 32 + lm0;
+      const int mc = m < M ? m : M - 1;
+      pf_xo[i] = *(const v4i*)(g.x_panel + (size_t)mc * kPanelCols + kg0 * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) {
+      const int n = n0 + wn * TL::TN + j * 32 + lm0;
+      const int ncl = n < N ? n : N - 1;
+      pf_wo[j] = *(const v4i*)(g.w_panel + (size_t)ncl * kPanelCols + kg0 * 8);
+    }
   }
 
   // ---- DMA loader.  One wave instruction fills 1 KB = 16 LDS rows; lane l
@@ -542,19 +543,44 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
           acc[i][j][r] = __float_as_int((sx * f_sb[nl]) * (float)(a - f_zi[nl] * rs));
         }
     }
-    // the prefetched count and columns are first used here (the empty asm
+    // the prefetched count and panels are first used here (the empty asm
     // keeps their uses from being hoisted next to their loads)
     asm volatile("" : "+v"(pf_cnt));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(pf_col[e]));
     const int cnt = pf_cnt;
+    static_assert(kPanelCols == 16, "one v_mfma_f32_32x32x16_f16 step per panel");
     const int kg = lane >> 5;                          // 8-column group of the 16-column step
-    for (int kc = 0; kc < cnt; kc += 16) {
+    auto outlier_mfmas = [&](const v8h* xo, const v8h* wo) {
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) {
+          v16f c = __builtin_bit_cast(v16f, acc[i][j]);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[j], xo[i], c, 0, 0, 0);
+          acc[i][j] = __builtin_bit_cast(v16i, c);
+        }
+    };
+    if (cnt > 0) {
+      // the first kPanelCols outlier columns, from the quantizer's panels
+      // (zeros past the count)
+      v8h xo[TL::FM], wo[TL::FN];
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i) {
+        asm volatile("" : "+v"(pf_xo[i]));
+        xo[i] = __builtin_bit_cast(v8h, pf_xo[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) {
+        asm volatile("" : "+v"(pf_wo[j]));
+        wo[j] = __builtin_bit_cast(v8h, pf_wo[j]);
+      }
+      outlier_mfmas(xo, wo);
+    }
+    for (int kc = kPanelCols; kc < cnt; kc += 16) {
       int col[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int jj = kc + kg * 8 + e;
-        col[e] = jj < cnt ? (kc == 0 ? pf_col[e] : g.out_idx[jj]) : -1;
+        col[e] = jj < cnt ? g.out_idx[jj] : -1;
       }
       // Every load is issued unconditionally, at a clamped address, and all
       // of them before any is used; each value is zeroed afterwards where its
@@ -604,14 +630,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
           wo[j][e] = (col[e] >= 0 && nok) ? w : (_Float16)0.0f;
         }
       }
-#pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::FN; ++j) {
-          v16f c = __builtin_bit_cast(v16f, acc[i][j]);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[j], xo[i], c, 0, 0, 0);
-          acc[i][j] = __builtin_bit_cast(v16i, c);
-        }
+      outlier_mfmas(xo, wo);
     }
   }
 

@@ -214,6 +214,19 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)p;
 }
 
+// Outlier weight of the LLM.int8 flow: fp16(fp32(S (q - Z))), the product
+// rounded to fp32 before the conversion to fp16, as the dequantized fp32
+// weights are cast to fp16.  Left alone, the compiler fuses the multiply and
+// the conversion into one v_fma_mixlo_f16 (even with contraction off), which
+// rounds the exact product to fp16 once and differs from the two roundings
+// next to a tie of fp16; the empty asm makes the fp32 product a value of its
+// own.
+__device__ __forceinline__ _Float16 outlier_weight_f16(float s, int q, float z) {
+  float p = s * ((float)q - z);
+  asm volatile("" : "+v"(p));
+  return (_Float16)p;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
          ((uint32_t)(d & 0xff) << 24);

@@ -16,13 +16,27 @@ hipError_t launch_quant_act_i8_static(const void* x, int dt, int64_t M, int64_t 
                                       float* x_scale, int32_t* x_rowsum, hipStream_t st);
 hipError_t launch_quant_act_i8(const void* x, int dt, int64_t M, int64_t K, int8_t* xq, float* x_scale,
                                int32_t* x_rowsum, hipStream_t st);
+// LLM.int8: the first kPanelCols outlier columns in compact form for the
+// GEMM's outlier flow, row-major with kPanelCols fp16 values per row and
+// zeros past the outlier count: x_panel [M] rows hold X[m, O_j], w_panel [N]
+// rows hold fp16(fp32(S_w[n] (wq[n, O_j] - Z_w[n]))).
+constexpr int kPanelCols = 16;
+struct OutlierPanels {
+  const int8_t* wq;         // [N, K] weight codes
+  const float* w_scale;     // [N]
+  const float* w_zp;        // [N]
+  int64_t N;
+  uint16_t* x_panel;        // [M, kPanelCols] or null (no panels)
+  uint16_t* w_panel;        // [N, kPanelCols]
+};
 // fp16 activations of the LLM.int8 step: columns with flags[k] != 0 read as 0
 // (flags may be null: none); also writes the ascending outlier list idx[] and
-// its count cnt[0] (and copies to user_idx / user_cnt when not null).
+// its count cnt[0] (and copies to user_idx / user_cnt when not null), and the
+// panels when p.x_panel is not null.
 hipError_t launch_quant_act_f16_outliers(const uint16_t* x, int64_t M, int64_t K, const uint8_t* flags,
                                          int8_t* xq, float* x_scale, int32_t* x_rowsum, int32_t* idx,
                                          int32_t* cnt, int32_t* user_idx, int32_t* user_cnt,
-                                         hipStream_t st);
+                                         const OutlierPanels& p, hipStream_t st);
 
 // Operands and epilogue inputs of the MFMA GEMM (gemm.hip).
 struct GemmArgs {
@@ -40,6 +54,8 @@ struct GemmArgs {
   const uint16_t* x_f16;    // [M, K] fp16 activations
   const int32_t* out_idx;   // ascending outlier columns
   const int32_t* out_cnt;   // [1] number of outlier columns (device)
+  const uint16_t* x_panel;  // [M, kPanelCols] the first outlier columns of X (fp16)
+  const uint16_t* w_panel;  // [N, kPanelCols] their fp16 weights
   // INT8 output (ydt DT_I8): 1 / S_y of the static output scale
   double y_inv;
   // grouped problems (experts): groups > 0 and the device row offsets [groups+1]

@@ -127,29 +127,37 @@ constexpr int kRowCache = 8;   // chunks per thread held in registers: 16-bit ro
 // chunks that no lane of the wave flags skip the masking.  One extra
 // workgroup (the last) compacts the flags into the ascending list of outlier
 // columns and its count (for the GEMM's outlier flow and the caller) while
-// the others quantize; flags == NULL means no outlier columns.
+// the others quantize; flags == NULL means no outlier columns.  When
+// pan.x_panel is set, the first workgroups of the grid write the panels of
+// the first kPanelCols outlier columns, 16 rows each (one value per thread,
+// so that the scattered reads spread over many CUs): ceil(R / 16) for X, then
+// ceil(N / 16) for the weights; each finds those columns with the same scan
+// of the flags.
 // At least 4 waves per SIMD (<= 128 VGPRs): several rows per CU keep loads in flight.
 template <int MODE, int DT>
 __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
     const void* __restrict__ x, int64_t R, int64_t K, const uint8_t* __restrict__ flags, float bound,
     uint8_t* __restrict__ xq, float* __restrict__ x_scale, int32_t* __restrict__ x_rowsum,
     int32_t* __restrict__ idx, int32_t* __restrict__ cnt, int32_t* __restrict__ user_idx,
-    int32_t* __restrict__ user_cnt, int32_t* __restrict__ gsum, int glanes) {
+    int32_t* __restrict__ user_cnt, int32_t* __restrict__ gsum, int glanes, const OutlierPanels pan) {
   constexpr int E = Chunk<DT>::kElems;
   __shared__ float redf[kWaves];
   __shared__ int redi[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  int64_t bid = blockIdx.x;
   if constexpr (MODE == RM_I8_OUTLIER) {
-    if (blockIdx.x == gridDim.x - 1) {
-      // Thread t owns the run [t*per, (t+1)*per) of 16-byte flag blocks (K is
-      // a multiple of 16); a block prefix sum of the runs' counts places every
-      // flagged column in ascending order.
-      int total = 0;
+    constexpr int kPanelRows = kThreads / kPanelCols;
+    const int64_t nxp = pan.x_panel != nullptr ? (R + kPanelRows - 1) / kPanelRows : 0;
+    const int64_t npan = pan.x_panel != nullptr ? nxp + (pan.N + kPanelRows - 1) / kPanelRows : 0;
+    if (bid < npan || bid == npan + R) {
+      // Thread t owns the run [c0, c0 + per) of 16-byte flag blocks (K is a
+      // multiple of 16); a block prefix sum of the runs' counts gives every
+      // flagged column its rank in ascending order.
+      const int per = 16 * (int)((K + 16 * kThreads - 1) / (16 * kThreads));
+      const int c0 = tid * per;
+      int mine = 0, before = 0, total = 0;
       if (flags != nullptr) {
-        const int per = 16 * (int)((K + 16 * kThreads - 1) / (16 * kThreads));
-        const int c0 = tid * per;
-        int mine = 0;
         for (int c = c0; c < c0 + per && c < (int)K; c += 16) {
           const v4i f = *(const v4i*)(flags + c);
 #pragma unroll
@@ -163,35 +171,66 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
         }
         if (lane == 63) redi[wave] = incl;
         __syncthreads();
-        int before = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           if (w < wave) before += redi[w];
           total += redi[w];
         }
-        int pos = before + incl - mine;
-        if (mine > 0) {
-          for (int c = c0; c < c0 + per && c < (int)K; c += 16) {
-            const v4i f = *(const v4i*)(flags + c);
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (((uint32_t)f[e >> 2] >> (8 * (e & 3))) & 0xffu) {
-                idx[pos] = c + e;
-                if (user_idx) user_idx[pos] = c + e;
-                ++pos;
-              }
-          }
-        }
+        before += incl - mine;
       }
-      if (tid == 0) {
-        *cnt = total;
-        if (user_cnt) *user_cnt = total;
+      // this thread's flagged columns, ascending, with their ranks
+      auto each_flagged = [&](auto fn) {
+        int pos = before;
+        for (int c = c0; c < c0 + per && c < (int)K; c += 16) {
+          const v4i f = *(const v4i*)(flags + c);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (((uint32_t)f[e >> 2] >> (8 * (e & 3))) & 0xffu) fn(pos++, c + e);
+        }
+      };
+      if (bid == npan + R) {
+        if (mine > 0)
+          each_flagged([&](int pos, int col) {
+            idx[pos] = col;
+            if (user_idx) user_idx[pos] = col;
+          });
+        if (tid == 0) {
+          *cnt = total;
+          if (user_cnt) *user_cnt = total;
+        }
+        return;
+      }
+      // panel workgroups: the first kPanelCols outlier columns, then one
+      // value of a panel per thread (zeros past the outlier count)
+      __shared__ int pcol[kPanelCols];
+      if (mine > 0 && before < kPanelCols)
+        each_flagged([&](int pos, int col) {
+          if (pos < kPanelCols) pcol[pos] = col;
+        });
+      __syncthreads();
+      const int np = total < kPanelCols ? total : kPanelCols;
+      const int j = tid % kPanelCols;
+      const int cj = j < np ? pcol[j] : 0;
+      if (bid < nxp) {
+        const int64_t r = bid * kPanelRows + tid / kPanelCols;
+        if (r < R) {
+          const uint16_t v = ((const uint16_t*)x)[r * K + cj];
+          pan.x_panel[r * kPanelCols + j] = j < np ? v : (uint16_t)0;
+        }
+      } else {
+        const int64_t n = (bid - nxp) * kPanelRows + tid / kPanelCols;
+        if (n < pan.N) {
+          const float s = pan.w_scale[n], z = (float)(int)pan.w_zp[n];
+          const uint16_t v = __builtin_bit_cast(uint16_t, outlier_weight_f16(s, pan.wq[n * K + cj], z));
+          pan.w_panel[n * kPanelCols + j] = j < np ? v : (uint16_t)0;
+        }
       }
       return;
     }
+    bid -= npan;
   }
 
-  const int64_t m = blockIdx.x;
+  const int64_t m = bid;
   const int nch = (int)(K / E);
   const int64_t row = m * K;
   const bool masked = MODE == RM_I8_OUTLIER && flags != nullptr;
@@ -312,18 +351,19 @@ template <int MODE>
 void launch_rows(const void* x, int dt, int64_t R, int64_t K, const uint8_t* flags, float bound, uint8_t* xq,
                  float* x_scale, int32_t* x_rowsum, int32_t* idx, int32_t* cnt, int32_t* user_idx,
                  int32_t* user_cnt, unsigned grid, hipStream_t st, int32_t* gsum = nullptr, int glanes = 0) {
+  const OutlierPanels none{};
   switch (dt) {
     case DT_F32:
       k_quant_rows<MODE, DT_F32><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                            cnt, user_idx, user_cnt, gsum, glanes);
+                                                            cnt, user_idx, user_cnt, gsum, glanes, none);
       break;
     case DT_F16:
       k_quant_rows<MODE, DT_F16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                            cnt, user_idx, user_cnt, gsum, glanes);
+                                                            cnt, user_idx, user_cnt, gsum, glanes, none);
       break;
     default:
       k_quant_rows<MODE, DT_BF16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                             cnt, user_idx, user_cnt, gsum, glanes);
+                                                             cnt, user_idx, user_cnt, gsum, glanes, none);
       break;
   }
 }
@@ -373,10 +413,14 @@ hipError_t launch_quant_act_i8_groups(const void* x, int dt, int64_t M, int64_t 
 hipError_t launch_quant_act_f16_outliers(const uint16_t* x, int64_t M, int64_t K, const uint8_t* flags,
                                          int8_t* xq, float* x_scale, int32_t* x_rowsum, int32_t* idx,
                                          int32_t* cnt, int32_t* user_idx, int32_t* user_cnt,
-                                         hipStream_t st) {
-  // one workgroup per row, plus the compaction workgroup
-  k_quant_rows<RM_I8_OUTLIER, DT_F16><<<(unsigned)(M + 1), kThreads, 0, st>>>(
-      x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, nullptr, 0);
+                                         const OutlierPanels& p, hipStream_t st) {
+  // the panel workgroups (16 rows each), one workgroup per row, then the
+  // compaction workgroup
+  constexpr int kPanelRows = kThreads / kPanelCols;
+  const int64_t panels =
+      p.x_panel != nullptr ? (M + kPanelRows - 1) / kPanelRows + (p.N + kPanelRows - 1) / kPanelRows : 0;
+  k_quant_rows<RM_I8_OUTLIER, DT_F16><<<(unsigned)(M + 1 + panels), kThreads, 0, st>>>(
+      x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, nullptr, 0, p);
   return hipGetLastError();
 }
 
