@@ -48,16 +48,27 @@ static_assert(DT_I8 == kOutInt8, "INT8 output code");
 namespace {
 
 
-constexpr int kBK = 64;             // bytes of K per stage
+// Bytes of K per stage: 64 for the 256 x 256 tile (four stages of 32 KB),
+// kSmallBK for the smaller tiles, whose four stages fit at 128 bytes
+// (whole 128-byte lines per DMA lane group)
+constexpr int kSmallBK = 128;
+constexpr int bk_for(int bm) { return bm == 256 ? 64 : kSmallBK; }
 constexpr int kStages = 4;          // LDS buffers (prefetch distance kStages - 1)
 constexpr int kGroupM = 4;          // tile-rows per L2 group
 constexpr int kXcds = 8;
 constexpr int kMaxGroupsDev = 1024;   // groups (experts) of one grouped call
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// LDS row swizzle: 16-byte chunk c of row r sits at physical chunk
+// c ^ sw(r).  With 64-byte rows four rows share a 256-byte bank row, with
+// 128-byte rows two; either way the 16 rows that one 16-lane group of a
+// fragment read touches cover all 64 banks once.
+template <int BK>
+__device__ __forceinline__ int swz_key(int row) { return BK == 64 ? (row >> 2) & 3 : (row >> 1) & 7; }
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key<BK>(row)) << 4); }
 
 // One MFMA shape.  A fragment row is (base multiple of 32) + lane % 32, so
-// ((row >> 2) & 3) == ((lane >> 2) & 3) and the swizzled byte offset of the
+// swz_key(row) == swz_key(lane % 32) and the swizzled byte offset of the
 // lane's operand inside its LDS row is lane_off(lane) XOR a per-k-step constant.
 // A and B fragments use the same lane -> k mapping, so each instruction sums
 // over exactly the k bytes of its step whatever order the hardware uses.
@@ -66,7 +77,8 @@ struct MmaI8 {                       // v_mfma_i32_32x32x32_i8
   using Op = v4i;
   using Acc = v16i;
   // lane l: 16-byte logical chunk 2*ks + l/32 of its row
-  __device__ static int lane_off(int lane) { return ((lane >> 5) ^ ((lane >> 2) & 3)) << 4; }
+  template <int BK>
+  __device__ static int lane_off(int lane) { return ((lane >> 5) ^ swz_key<BK>(lane & 31)) << 4; }
   __device__ static Op load(const uint8_t* row, int off, int ks) {
     return *(const v4i*)(row + (off ^ (ks << 5)));
   }
@@ -79,7 +91,8 @@ struct MmaF8 {                       // v_mfma_f32_32x32x64_f8f6f4, both operand
   using Op = v8i;
   using Acc = v16f;
   // lane l: logical chunks 4*ks + 2*(l/32) + {0, 1} of its row
-  __device__ static int lane_off(int lane) { return ((2 * (lane >> 5)) ^ ((lane >> 2) & 3)) << 4; }
+  template <int BK>
+  __device__ static int lane_off(int lane) { return ((2 * (lane >> 5)) ^ swz_key<BK>(lane & 31)) << 4; }
   __device__ static Op load(const uint8_t* row, int off, int ks) {
     const v4i lo = *(const v4i*)(row + (off ^ (ks << 6)));
     const v4i hi = *(const v4i*)(row + ((off ^ 16) ^ (ks << 6)));
@@ -99,14 +112,14 @@ __device__ __forceinline__ int raw32(float x) { return __float_as_int(x); }
 // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 __device__ __forceinline__ int out_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-template <int BM, int BN, int NW>
+template <int BM, int BN, int NW, int BK>
 struct Tile {
   static constexpr int NT = 64 * NW;                        // threads
   static constexpr int WN = NW == 8 ? 4 : 2, WM = NW / WN;  // wave grid
   static constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;          // 32x32 fragments per wave
-  static constexpr int ALOADS = BM * (kBK / 16) / NT;   // 16-byte chunks per thread
-  static constexpr int BLOADS = BN * (kBK / 16) / NT;
+  static constexpr int ALOADS = BM * (BK / 16) / NT;   // 16-byte chunks per thread
+  static constexpr int BLOADS = BN * (BK / 16) / NT;
   static constexpr int LOADS = ALOADS + BLOADS;               // DMA instructions per wave per stage
   static_assert(ALOADS >= 1 && BLOADS >= 1 && FM >= 1 && FN >= 1, "tile too small");
 };
@@ -221,7 +234,8 @@ __device__ __forceinline__ bool group_tile(GemmArgs& g, int& tm, int& tn, int* l
 template <int BM, int BN, int KIND, int YDT, int NW, bool GROUPED = false>
 __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   using MM = typename std::conditional<KIND == GEMM_FP8, MmaF8, MmaI8>::type;
-  using TL = Tile<BM, BN, NW>;
+  constexpr int kBK = bk_for(BM);
+  using TL = Tile<BM, BN, NW, kBK>;
   constexpr int kThreads = TL::NT;
   using Acc = typename MM::Acc;
   constexpr int NR = MM::NR;
@@ -295,25 +309,28 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
     }
   }
 
-  // ---- DMA loader.  One wave instruction fills 1 KB = 16 LDS rows; lane l
-  // lands at row l/4, physical chunk l%4, which holds logical chunk
-  // (l%4) ^ ((row >> 2) & 3).  Rows past M (or N) re-read the last row: they
-  // only feed outputs that are never stored.
-  constexpr int kRowsPerDma = 64 * 16 / kBK;     // 16
-  const int lrow = lane >> 2;
-  const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  // ---- DMA loader.  One wave instruction fills 1 KB = 1024 / kBK LDS rows;
+  // lane l lands at row l / (kBK/16) of them, physical chunk l % (kBK/16),
+  // which holds logical chunk (l % (kBK/16)) ^ swz_key(row).  Rows past M (or
+  // N) re-read the last row: they only feed outputs that are never stored.
+  constexpr int kRowsPerDma = 64 * 16 / kBK;     // 16 or 8
+  constexpr int kChunks = kBK / 16;
+  const int lrow = lane / kChunks;
+  const int pchunk = lane % kChunks;
   uint32_t aoff[TL::ALOADS], boff[TL::BLOADS];
 #pragma unroll
   for (int j = 0; j < TL::ALOADS; ++j) {
-    int gm = m0 + (j * (kThreads / 64) + wave) * kRowsPerDma + lrow;
+    const int r = (j * (kThreads / 64) + wave) * kRowsPerDma + lrow;   // LDS row in the stage
+    int gm = m0 + r;
     gm = gm < M ? gm : M - 1;
-    aoff[j] = (uint32_t)(gm * K + lchunk * 16);
+    aoff[j] = (uint32_t)(gm * K + (pchunk ^ swz_key<kBK>(r)) * 16);
   }
 #pragma unroll
   for (int j = 0; j < TL::BLOADS; ++j) {
-    int gn = n0 + (j * (kThreads / 64) + wave) * kRowsPerDma + lrow;
+    const int r = (j * (kThreads / 64) + wave) * kRowsPerDma + lrow;
+    int gn = n0 + r;
     gn = gn < N ? gn : N - 1;
-    boff[j] = (uint32_t)(gn * K + lchunk * 16);
+    boff[j] = (uint32_t)(gn * K + (pchunk ^ swz_key<kBK>(r)) * 16);
   }
   const int swave = __builtin_amdgcn_readfirstlane(wave);
   auto dma = [&](uint8_t* sa, uint8_t* sb, int k0) {
@@ -338,17 +355,17 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   auto tail = [&](uint8_t* sa, uint8_t* sb, int k0) {
 #pragma unroll
     for (int j = 0; j < TL::ALOADS; ++j) {
-      const int i = tid + j * kThreads, row = i >> 2, c = i & 3;
+      const int i = tid + j * kThreads, row = i / kChunks, c = i % kChunks;
       const int gm = (m0 + row) < M ? (m0 + row) : M - 1;
       const int gk = k0 + c * 16;
-      *(v4i*)(sa + swz(row, c)) = gk < K ? *(const v4i*)(g.a + gm * K + gk) : v4i{0, 0, 0, 0};
+      *(v4i*)(sa + swz<kBK>(row, c)) = gk < K ? *(const v4i*)(g.a + gm * K + gk) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < TL::BLOADS; ++j) {
-      const int i = tid + j * kThreads, row = i >> 2, c = i & 3;
+      const int i = tid + j * kThreads, row = i / kChunks, c = i % kChunks;
       const int gn = (n0 + row) < N ? (n0 + row) : N - 1;
       const int gk = k0 + c * 16;
-      *(v4i*)(sb + swz(row, c)) = gk < K ? *(const v4i*)(g.b + gn * K + gk) : v4i{0, 0, 0, 0};
+      *(v4i*)(sb + swz<kBK>(row, c)) = gk < K ? *(const v4i*)(g.b + gn * K + gk) : v4i{0, 0, 0, 0};
     }
   };
   const int nfull = K / kBK;                 // stages filled by DMA
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
   // chunk inside the row.
   const int arow = (wm * TL::TM + (lane & 31)) * kBK;
   const int brow = (wn * TL::TN + (lane & 31)) * kBK;
-  const int loff = MM::lane_off(lane);
+  const int loff = MM::template lane_off<kBK>(lane);
   // Fragments live in two register sets: while the MFMAs of one k-step run,
   // the LDS reads of the next k-step (or, across a stage boundary, of the
   // next stage's first k-step) go to the other set.
