@@ -50,13 +50,13 @@ METRIC = "q8_linear int8 TOPS (prefill) + GB/s (decode) and % of MI355X roofline
 # runs of `bench.py --only prefill --steps 3 --warmup 1 --warm-ms 0
 # --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
 # scaled by what the same counter reads for a plain 256 MiB device copy
-# (`bench.py --only copy`): FETCH_SIZE reads 131086 KiB for 262144 KiB moved
+# (`bench.py --only copy`): FETCH_SIZE reads 131087 KiB for 262144 KiB moved
 # (x 2.0), WRITE_SIZE 262144 KiB (x 1.0).  Valid for the GEMM sources whose
 # hash is recorded here; after any change to them the figure is withheld.
 GEMM_TRAFFIC = {
-    "sources_sha256": "4344cf02c74b19cc60a23274ab058d50bd83bf7cf5cdd60d9e0af94b9e1bddc3",
-    "fetch_kib": 90436.42, "fetch_scale": 262144.0 / 131085.62,
-    "write_kib": 57373.93, "write_scale": 262144.0 / 262144.00,
+    "sources_sha256": "ef6db2febf0fef58642228f518fd16c5616917cd655b39ec6b25e600d2f4ff00",
+    "fetch_kib": 90433.59, "fetch_scale": 262144.0 / 131086.90,
+    "write_kib": 57359.80, "write_scale": 262144.0 / 262144.00,
 }
 
 
