@@ -274,13 +274,18 @@ def bench_decomp(dev, steps, warmup):
     def step(i, pair):
         q8.q8_linear_int8_decomp(x, wq, ws, wz, 6.0, out=y, workspace=wsp)
 
-    # no per-step events: at ~30 us a step, an event pair per step is a
+    # no per-step events: at ~20 us a step, an event pair per step is a
     # visible share of it
     ms, _, _ = timed_steps(step, steps, warmup, None)
+    # the same step replayed from a HIP graph of 20 steps, reported beside
+    # the eager figure (the graph's node gaps make it the slower of the two)
+    graph_ms = graph_us(lambda: q8.q8_linear_int8_decomp(x, wq, ws, wz, 6.0, out=y, workspace=wsp),
+                        20, max(4, steps // 2)) * 1e-3
     ops = 2.0 * M * N * K
     nbytes = N * K + 8 * N + M * K * 2 + M * N * 2
     t_ideal = max(ops / (PEAK_INT8_TOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
-    return {"M": M, "N": N, "K": K, "ms_per_step": ms, "tops": ops / (ms * 1e-3) / 1e12,
+    return {"M": M, "N": N, "K": K, "ms_per_step": ms, "graph_ms_per_step": graph_ms,
+            "tops": ops / (ms * 1e-3) / 1e12,
             "roofline": {"bound": "ridge", "ideal_us": t_ideal * 1e6, "frac": t_ideal / (ms * 1e-3)}}
 
 
@@ -571,7 +576,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
                     help="host seconds per workload for the oracle's cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "grouped", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "static", "grouped", "copy"], default=None,
                     help="run one workload (for profiling); 'copy' runs a plain 256 MiB device copy, "
                          "the known-size kernel that scales the HBM byte counters")
     ap.add_argument("--warm-ms", type=float, default=WARM_MS,
@@ -643,7 +648,8 @@ def main():
         d = bench_decomp(dev, args.steps, args.warmup)
         progress("llm_int8")
         out["llm_int8"] = {"workload": "LLM.int8 decomposition 512x4096x4096 fp16, 6 outlier columns",
-                           "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
+                           "ms_per_step": round(d["ms_per_step"], 5),
+                           "graph_ms_per_step": round(d["graph_ms_per_step"], 5), "TOPS": round(d["tops"], 1),
                            "roofline": {k: round(v, 4) if isinstance(v, float) else v
                                         for k, v in d["roofline"].items()}}
     if args.only in (None, "fp8"):
@@ -662,12 +668,14 @@ def main():
                                       f"{d['tokens_per_expert']}, N = K = {N}, bf16 out, ub 1200",
                           "ms_per_step": round(d["ms_per_step"], 5), "TFLOPS": round(d["tflops"], 1),
                           "frac_of_fp8_peak": round(d["tflops"] / PEAK_FP8_TFLOPS, 4)}
+    if args.only in (None, "static"):
         d = bench_static(dev, args.steps, args.warmup)
         progress("static_int8_out")
         out["static_int8_out"] = {"workload": "prefill FFN-up 2048x14336x4096, static activation scale, INT8 output "
                                               "(q8_linear_static: static quantization + int8 GEMM, float64 requantize)",
                                   "ms_per_step": round(d["ms_per_step"], 5), "TOPS": round(d["tops"], 1),
                                   "frac_of_int8_peak": round(d["tops"] / PEAK_INT8_TOPS, 4)}
+    if args.only is None:
         out["ceilings"] = bench_ceilings(dev, args.steps)
         progress("ceilings")
     if args.only in (None, "grouped"):
