@@ -120,6 +120,10 @@ enum RowMode : int {
   RM_I8_GROUPS = 4,  // as RM_I8, plus the code sum of every group of glanes consecutive chunks
 };
 constexpr int kRowCache = 8;   // chunks per thread held in registers: 16-bit rows up to 16384 values
+// Rows of up to 2 kThreads chunks (16-bit rows of up to 4096 values) use a
+// cache of two chunks: ~50 instead of ~86 registers, so eight row workgroups
+// fit on a CU instead of five and a 2048-row activation runs in one round.
+constexpr int kSmallCache = 2;
 
 // RM_I8_OUTLIER: the outlier columns (flags[k] != 0) are left out of the row
 // absmax and get code 0 (their product goes through the fp16 outlier flow);
@@ -134,7 +138,7 @@ constexpr int kRowCache = 8;   // chunks per thread held in registers: 16-bit ro
 // ceil(N / 16) for the weights; each finds those columns with the same scan
 // of the flags.
 // At least 4 waves per SIMD (<= 128 VGPRs): several rows per CU keep loads in flight.
-template <int MODE, int DT>
+template <int MODE, int DT, int CACHE = kRowCache>
 __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
     const void* __restrict__ x, int64_t R, int64_t K, const uint8_t* __restrict__ flags, float bound,
     uint8_t* __restrict__ xq, float* __restrict__ x_scale, int32_t* __restrict__ x_rowsum,
@@ -249,10 +253,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
     }
   };
 
-  v4i d[kRowCache];
-  uint64_t fw[kRowCache];
+  v4i d[CACHE];
+  uint64_t fw[CACHE];
 #pragma unroll
-  for (int j = 0; j < kRowCache; ++j) {
+  for (int j = 0; j < CACHE; ++j) {
     const int c = tid + kThreads * j;
     if (c < nch) {
       d[j] = load_chunk<DT>(x, row, c);
@@ -268,9 +272,9 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
   };
   if constexpr (MODE != RM_I8_STATIC) {
 #pragma unroll
-    for (int j = 0; j < kRowCache; ++j)
+    for (int j = 0; j < CACHE; ++j)
       if (tid + kThreads * j < nch) take_max(d[j], fw[j]);
-    for (int c = tid + kThreads * kRowCache; c < nch; c += kThreads) take_max(load_chunk<DT>(x, row, c), flag_word(c));
+    for (int c = tid + kThreads * CACHE; c < nch; c += kThreads) take_max(load_chunk<DT>(x, row, c), flag_word(c));
     amax = block_max<kWaves>(amax, redf);
   }
 
@@ -335,11 +339,11 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
     }
   };
 #pragma unroll
-  for (int j = 0; j < kRowCache; ++j) {
+  for (int j = 0; j < CACHE; ++j) {
     const int c = tid + kThreads * j;
     if (c < nch) emit(d[j], fw[j], c);
   }
-  for (int c = tid + kThreads * kRowCache; c < nch; c += kThreads) emit(load_chunk<DT>(x, row, c), flag_word(c), c);
+  for (int c = tid + kThreads * CACHE; c < nch; c += kThreads) emit(load_chunk<DT>(x, row, c), flag_word(c), c);
   if constexpr (MODE != RM_FP8) qsum = block_sum<kWaves>(qsum, redi);
   if (tid == 0) {
     if (x_scale) x_scale[m] = s;
@@ -352,18 +356,27 @@ void launch_rows(const void* x, int dt, int64_t R, int64_t K, const uint8_t* fla
                  float* x_scale, int32_t* x_rowsum, int32_t* idx, int32_t* cnt, int32_t* user_idx,
                  int32_t* user_cnt, unsigned grid, hipStream_t st, int32_t* gsum = nullptr, int glanes = 0) {
   const OutlierPanels none{};
+  const bool small = K <= 8 * kSmallCache * kThreads;   // 16-bit rows: at most kSmallCache chunks per thread
   switch (dt) {
     case DT_F32:
       k_quant_rows<MODE, DT_F32><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
                                                             cnt, user_idx, user_cnt, gsum, glanes, none);
       break;
     case DT_F16:
-      k_quant_rows<MODE, DT_F16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                            cnt, user_idx, user_cnt, gsum, glanes, none);
+      if (small)
+        k_quant_rows<MODE, DT_F16, kSmallCache><<<grid, kThreads, 0, st>>>(
+            x, R, K, flags, bound, xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, gsum, glanes, none);
+      else
+        k_quant_rows<MODE, DT_F16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
+                                                              cnt, user_idx, user_cnt, gsum, glanes, none);
       break;
     default:
-      k_quant_rows<MODE, DT_BF16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
-                                                             cnt, user_idx, user_cnt, gsum, glanes, none);
+      if (small)
+        k_quant_rows<MODE, DT_BF16, kSmallCache><<<grid, kThreads, 0, st>>>(
+            x, R, K, flags, bound, xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, gsum, glanes, none);
+      else
+        k_quant_rows<MODE, DT_BF16><<<grid, kThreads, 0, st>>>(x, R, K, flags, bound, xq, x_scale, x_rowsum, idx,
+                                                               cnt, user_idx, user_cnt, gsum, glanes, none);
       break;
   }
 }
@@ -419,8 +432,12 @@ hipError_t launch_quant_act_f16_outliers(const uint16_t* x, int64_t M, int64_t K
   constexpr int kPanelRows = kThreads / kPanelCols;
   const int64_t panels =
       p.x_panel != nullptr ? (M + kPanelRows - 1) / kPanelRows + (p.N + kPanelRows - 1) / kPanelRows : 0;
-  k_quant_rows<RM_I8_OUTLIER, DT_F16><<<(unsigned)(M + 1 + panels), kThreads, 0, st>>>(
-      x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, nullptr, 0, p);
+  if (K <= 8 * kSmallCache * kThreads)
+    k_quant_rows<RM_I8_OUTLIER, DT_F16, kSmallCache><<<(unsigned)(M + 1 + panels), kThreads, 0, st>>>(
+        x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, nullptr, 0, p);
+  else
+    k_quant_rows<RM_I8_OUTLIER, DT_F16><<<(unsigned)(M + 1 + panels), kThreads, 0, st>>>(
+        x, M, K, flags, 0.0f, (uint8_t*)xq, x_scale, x_rowsum, idx, cnt, user_idx, user_cnt, nullptr, 0, p);
   return hipGetLastError();
 }
 
