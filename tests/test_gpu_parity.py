@@ -152,6 +152,11 @@ ACT_CASES = [
     ("prefill_2048x4096_bf16", 2048, 4096, torch.bfloat16, 12),
     ("overflow_row_5x20032_bf16", 5, 20032, torch.bfloat16, 13),
     ("f32_overflow_3x8208", 3, 8208, torch.float32, 14),
+    # 16-bit rows of up to 4096 values run a two-chunk register cache, longer
+    # ones the eight-chunk one: both sides of that boundary
+    ("cache_edge_9x4096_f16", 9, 4096, torch.float16, 15),
+    ("cache_edge_7x4112_bf16", 7, 4112, torch.bfloat16, 16),
+    ("cache_edge_6x4112_f16", 6, 4112, torch.float16, 17),
 ]
 
 
@@ -405,6 +410,15 @@ def test_decomp_whole_accumulator(tile, M, N, K, seed):
     assert_equal(host(acc), acc_ref.astype(np.int64).astype(np.int32), "whole INT32 accumulator")
 
 
+@pytest.mark.parametrize("K", [4096, 4112])
+def test_decomp_row_cache_edge(K):
+    # the masked quantizer keeps rows of up to 4096 values in a two-chunk
+    # register cache and longer ones in the eight-chunk one
+    log(f"[decomp] row cache edge K={K}")
+    wl = inputs.llm_int8_outliers(M=40, K=K, N=200, n_outlier_cols=5)
+    run_decomp_case(wl.x, wl.w, 6.0, what=f"K={K}")
+
+
 @pytest.mark.parametrize("tau", [6.0, 0.0, -1.0, 1e-30])
 def test_decomp_thresholds(tau):
     log(f"[decomp] threshold {tau}")
@@ -553,7 +567,8 @@ def test_w8a16_one_signed_rows_and_bias():
 # ---------------------------------------------------------------- static scales, INT8 output
 @pytest.mark.parametrize("name,M,K,dt,scale", [("bf16_2048x4096", 2048, 4096, torch.bfloat16, 0.021),
                                                ("f32_37x272_saturating", 37, 272, torch.float32, 0.004),
-                                               ("f16_5x1040", 5, 1040, torch.float16, 0.0371)])
+                                               ("f16_5x1040", 5, 1040, torch.float16, 0.0371),
+                                               ("bf16_4x4112_cache_edge", 4, 4112, torch.bfloat16, 0.019)])
 def test_quantize_act_static_codes(name, M, K, dt, scale):
     log(f"[act static] {name} S={scale}")
     x = inputs.random_matrix(140 + M, (M, K), 1.0, dt)
