@@ -576,7 +576,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=5.0,
                     help="host seconds per workload for the oracle's cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "static", "grouped", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "decomp", "fp8", "moe", "static", "grouped", "copy"], default=None,
                     help="run one workload (for profiling); 'copy' runs a plain 256 MiB device copy, "
                          "the known-size kernel that scales the HBM byte counters")
     ap.add_argument("--warm-ms", type=float, default=WARM_MS,
@@ -660,7 +660,7 @@ def main():
                       "gemm_us": round(d["gemm_us"], 2),
                       "roofline": {k: round(v, 4) if isinstance(v, float) else v
                                    for k, v in d["roofline"].items()}}
-    if args.only is None:
+    if args.only in (None, "moe"):
         d = bench_moe_fp8(dev, args.steps, args.warmup)
         progress("moe_fp8")
         T, N, K, E = d["shape"]

@@ -657,9 +657,11 @@ def test_fp8_grouped_moe_full_size():
 
 
 @pytest.mark.parametrize("counts,N,K", [([0, 130, 0, 7, 300, 0], 200, 528),     # empty experts, 64x128 tiles
-                                        ([513], 256, 256),                       # one expert, 256x256 tiles
+                                        ([513], 256, 256),                       # one expert, 128x128 tiles (mean 513)
                                         ([1, 1, 1, 1], 96, 64),                  # one token each
-                                        ([150, 0, 400, 100], 1000, 1040)])       # 128x128 tiles (mean 162)
+                                        ([150, 0, 400, 100], 1000, 1040),        # 128x128 tiles (mean 162)
+                                        ([900, 0, 411, 300], 520, 576),          # 128x128 tiles (mean 402), N tail
+                                        ([1600, 7], 300, 320)])                  # 256x256 tiles (mean 803)
 def test_fp8_grouped_ragged(counts, N, K):
     log(f"[fp8 experts] counts={counts} N={N} K={K}")
     E = len(counts)
