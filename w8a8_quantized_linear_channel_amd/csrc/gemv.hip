@@ -20,9 +20,11 @@
 //     region, so no barrier is needed between coding and the MFMAs.
 // Rows are processed in run-time loops: the kernel runs once per call, so
 // every instruction is fetched cold, and compact code is what keeps the
-// activation work short.  The four partial INT32 tiles and the per-row code
-// sums meet in LDS and wave 0 applies y = S_x S_w (acc - Z_w sum_k q_x)
-// (+ bias) with the per-row factors it loaded at the start.
+// activation work short.  Each k-step also runs an MFMA of all-ones weights
+// against the codes, which gives sum_k q_x in the accumulator's own layout;
+// the four partial INT32 tiles and code sums meet in LDS and wave 0 applies
+// y = S_x S_w (acc - Z_w sum_k q_x) (+ bias) with the per-row factors it
+// loaded at the start.
 //
 // Code columns past K are zero, so the clamped weight loads there add
 // nothing.  Code rows m >= M hold stale bytes: they only feed MFMA output
@@ -61,13 +63,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
                                                          const float* __restrict__ bias, void* __restrict__ y,
                                                          int32_t* __restrict__ acc_out) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves][kRows * kArea];
-  // Per-thread partials of every row (absmax in pass 1, then code sums in
-  // pass 2): no reduction inside the row loops; one block-wide pass per
-  // quantity reduces all rows at once.
+  // Per-thread partial absmax of every row: no reduction inside the row
+  // loop; one block-wide pass reduces all rows at once.
   __shared__ __attribute__((aligned(16))) float lred[kRows][kThreads];
   __shared__ float rscale[kRows];
-  __shared__ int rsum[kRows];
   __shared__ v4i part[kWaves][64];
+  __shared__ v4i psum[kWaves][64];     // the code sums' partial tiles
   // per-channel factors of the 16 columns, one 1 KB DMA by wave 0: scales at
   // [0, 16), zero points at [16, 32), biases at [32, 48); the rest unused
   __shared__ __attribute__((aligned(16))) float fac[256];
@@ -203,10 +204,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
     return dpp_row_reduce(r, op);
   };
   auto fmax_bits = [](int a, int b) __attribute__((always_inline)) { return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b))); };
-  auto add_int = [](int a, int b) __attribute__((always_inline)) { return a + b; };
   auto row_scale = [&](int m) __attribute__((always_inline)) { return rscale[m]; };
   v4i acc = {0, 0, 0, 0};
-  // per-group weights: the group code sums and the fp32 sum over groups
+  // the code sums (per-group weights: of the current group), from the
+  // all-ones MFMA; and, per-group, the fp32 sum over groups
   v4i accs = {0, 0, 0, 0};
   v4f fsum = {0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int NG = GS > 0 ? kKW / GS : 1;   // groups in a wave's share of a segment
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
       const float s = __int_as_float(r) / 127.0f;
       rscale[tid >> 4] = s < kEps ? kEps : s;
     }
-    __syncthreads();   // the scales are in LDS; lred is free for the code sums
+    __syncthreads();   // the scales are in LDS
   };
   // ---- pass 2 over one segment: codes, then the MFMAs on them.  reload:
   // X (and, past the first segment, W) must be fetched again.
@@ -319,21 +320,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
         }
         words[g] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
       }
-      int q = 0;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) q = sum_i8x4(words[g], q);
       // the row's X values have all been read (same wave, in order) before
       // their codes overwrite the start of the area
       uint8_t* area = xw + m * kArea;
       *(v2i*)(area + 8 * lane) = v2i{(int)words[0], (int)words[1]};
       *(v2i*)(area + 512 + 8 * lane) = v2i{(int)words[2], (int)words[3]};
-      ((int*)lred[m])[tid] = sg == 0 ? q : ((int*)lred[m])[tid] + q;
     }
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     if constexpr (GS == 0) {
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         const v4i xv = *(const v4i*)(xw + lr * kArea + s * 64 + lg * 16);
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[s], xv, acc, 0, 0, 0);
+        accs = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, xv, accs, 0, 0, 0);
       }
     } else {
       if (sg > 0) load_groups(k0);   // pass 1 loaded segment 0's groups
@@ -352,7 +351,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
             }
         }
       }
-      const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         const v4i xv = *(const v4i*)(xw + lr * kArea + s * 64 + lg * 16);
@@ -416,11 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
   }
   // ---- partial tiles and code sums meet in LDS; wave 0 applies the epilogue
   part[wave][lane] = acc;
-  __syncthreads();
-  {
-    const int r = reduce_rows(add_int);
-    if ((tid & 15) == 0) rsum[tid >> 4] = r;
-  }
+  psum[wave][lane] = accs;
   __syncthreads();
   if (wave == 0) {
     if (fac_dma) {
@@ -432,13 +426,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_i8(const void* __restrict_
         fbi[r] = fac[32 + 4 * lg + r];
       }
     }
-    v4i t = part[0][lane];
+    v4i t = part[0][lane], ts = psum[0][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) t += part[w][lane];
+    for (int w = 1; w < kWaves; ++w) {
+      t += part[w][lane];
+      ts += psum[w][lane];
+    }
     const int m = lr;
     if (m < M) {
       const float s_m = row_scale(m);
-      const int r_m = rsum[m];
+      const int r_m = ts[0];   // sum_k q_x[m, k]: every column of the all-ones product
       // The factors are first used here: the empty asm keeps their uses
       // (the zero point's conversion would otherwise be hoisted next to its
       // load, making the weight stream wait for the factor loads).
