@@ -578,6 +578,33 @@ def test_quantize_act_static_codes(name, M, K, dt, scale):
     assert_equal(host(rs), rr, "static row sums")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("K", [1024, 4112])
+def test_quantize_act_static_every_value(dt, K):
+    # Every finite 16-bit value in [-64, 64] against scales that put x / S on
+    # half-integers (0.25, 0.5), next to them (0.1, 1/3, 0.0371, 7), far past
+    # the clamp (1e-3, 1.5e-38: x / S overflows), and with a reciprocal below
+    # the normal range (1e38): the kernel decides most codes from x * RN(1/S)
+    # and the ones next to a half-integer by the division; all must equal the
+    # binary32 division's codes.
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    if dt == torch.bfloat16:
+        vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    else:
+        vals = bits.view(np.float16).astype(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 64.0)]
+    M = (vals.size + K - 1) // K
+    flat = np.zeros(M * K, dtype=np.float32)
+    flat[:vals.size] = vals
+    x = torch.tensor(flat.reshape(M, K)).to(dt)
+    for scale in (0.25, 0.5, 0.1, 1.0 / 3.0, 0.0371, 7.0, 1e-3, 1.5e-38, 1e38):
+        log(f"[act static] every {dt} value, K={K}, S={scale}")
+        xq, rs = q8.q8_quantize_act_static(g(x), scale)
+        rq, rr = O.quantize_act_int8_static(x, scale)
+        assert_equal(host(xq), rq, f"static codes S={scale}")
+        assert_equal(host(rs), rr, f"static row sums S={scale}")
+
+
 def run_static_case(x, w, x_scale, rows=None, bias=None, clip_frac=0.2, what=""):
     """GPU q8_linear_static on the full problem; oracle O12 on `rows` (all if
     None).  The output scale is set from the oracle's float64 values so that

@@ -293,6 +293,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
   }
   if constexpr (MODE != RM_I8_STATIC) s = s < kEps ? kEps : s;
   const float r = 1.0f / s;
+  // the product path of a static scale needs r to carry its full precision
+  const bool r_normal = __builtin_isnormal(r);
   int qsum = 0;
   auto emit = [&](const v4i& ch, uint64_t f, int c) {
     float v[E];
@@ -315,12 +317,40 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
         // scale needs the clamp (clamping before rounding to even is the same
         // for the integer bounds +-127)
         uint32_t b[4];
+        if constexpr (MODE == RM_I8_STATIC) {
+          // A static scale: the code of RN(x / s) from one product t = RN(x r),
+          // r = RN(1 / s).  |t - x/s| <= 2^-23 |x/s| (< 2^-16 below 128) and
+          // RN(x/s) is within half an ulp (<= 2^-18) of x/s, so where t lies
+          // more than 2^-14 from every half-integer both round to the same
+          // integer, and the clamp to +-127 keeps them equal; from |t| >= 128
+          // on, |x/s| > 127.5 too and both saturate (t = +-inf gives a NaN
+          // distance, hence no tie).  The few values next to a half-integer
+          // (and every value when r is not a normal number) take the division
+          // itself.
+          float y[4];
+          bool near[4];
+          bool any_near = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xv = v[4 * g + e];
-          float y = fast ? quot_fma(xv, s, r) : xv / s;
-          if constexpr (MODE == RM_I8_STATIC) y = fminf(fmaxf(y, -127.0f), 127.0f);
-          b[e] = rne_int8_bits(y);
+          for (int e = 0; e < 4; ++e) {
+            const float t = v[4 * g + e] * r;
+            const float d = fabsf(t - __builtin_rintf(t)) - 0.5f;
+            near[e] = !r_normal || fabsf(d) <= 0x1p-14f;
+            any_near |= near[e];
+            y[e] = fminf(fmaxf(t, -127.0f), 127.0f);
+          }
+          if (__any(any_near)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (near[e]) y[e] = fminf(fmaxf(v[4 * g + e] / s, -127.0f), 127.0f);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = rne_int8_bits(y[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float xv = v[4 * g + e];
+            b[e] = rne_int8_bits(fast ? quot_fma(xv, s, r) : xv / s);
+          }
         }
         words[g] = pack_lo_bytes(b[0], b[1], b[2], b[3]);
         qsum = sum_i8x4(words[g], qsum);
