@@ -358,13 +358,20 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
     }
     store_codes<E>(xq, row + (int64_t)c * E, words);
     if constexpr (MODE == RM_I8_GROUPS) {
-      // chunk c belongs to group c / glanes; its glanes chunks sit in glanes
-      // consecutive lanes of one wave (chunk c is thread c % 256), all active
-      // together since K is a multiple of the group size
+      // chunk c belongs to group c / glanes; its glanes chunks (8, 16 or 32:
+      // groups of 64 or 128 values) sit in glanes consecutive lanes of one
+      // wave (chunk c is thread c % 256), all active together since K is a
+      // multiple of the group size.  The sum runs on DPP moves inside the
+      // 16-lane rows (quad swaps, then the half-row and row mirrors); one
+      // lane permute joins two rows for 32 lanes.
       int cs = 0;
 #pragma unroll
       for (int g = 0; g < E / 4; ++g) cs = sum_i8x4(words[g], cs);
-      for (int o = 1; o < glanes; o <<= 1) cs += __shfl_xor(cs, o, 64);
+      cs += __builtin_amdgcn_update_dpp(0, cs, 0xB1, 0xF, 0xF, false);
+      cs += __builtin_amdgcn_update_dpp(0, cs, 0x4E, 0xF, 0xF, false);
+      cs += __builtin_amdgcn_update_dpp(0, cs, 0x141, 0xF, 0xF, false);
+      if (glanes >= 16) cs += __builtin_amdgcn_update_dpp(0, cs, 0x140, 0xF, 0xF, false);
+      if (glanes >= 32) cs += __shfl_xor(cs, 16, 64);
       if ((c & (glanes - 1)) == 0) gsum[(int64_t)(c / glanes) * R + m] = cs;
     }
   };
