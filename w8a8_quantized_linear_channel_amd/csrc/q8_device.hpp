@@ -123,6 +123,19 @@ __device__ __forceinline__ float wave_min(float v) {
   const float d = __int_as_float(__builtin_amdgcn_readlane(r, 48));
   return fminf(fminf(a, b), fminf(c, d));
 }
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active): row
+// shifts by 1, 2, 4 and 8 inside each 16-lane row, then lane 15's total of
+// rows 0 and 2 into rows 1 and 3, then lane 31's total of rows 0-1 into rows
+// 2 and 3.  Lanes with no source lane keep the 0 passed as the old value.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return v;
+}
 __device__ __forceinline__ int wave_sum(int v) {
   const int r = dpp_row_reduce(v, [](int a, int b) { return a + b; });
   return __builtin_amdgcn_readlane(r, 0) + __builtin_amdgcn_readlane(r, 16) +

@@ -167,12 +167,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant_rows(
 #pragma unroll
           for (int i = 0; i < 4; ++i) mine = sum_i8x4((uint32_t)f[i], mine);   // bytes are 0 or 1
         }
-        int incl = mine;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int t = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += t;
-        }
+        const int incl = wave_incl_scan(mine);
         if (lane == 63) redi[wave] = incl;
         __syncthreads();
 #pragma unroll
