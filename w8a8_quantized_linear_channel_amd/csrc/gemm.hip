@@ -787,7 +787,7 @@ hipError_t launch_tiles(const GemmArgs& g, int ydt, hipStream_t st) {
   // 256 x 256 int8 tiles run 8 waves (two per SIMD, 128 x 64 each), so one
   // wave's stalls on the DMA issue are covered by the other's MFMAs; the fp8
   // operands are twice as wide and would spill at that register budget
-  constexpr int NW = BM == 256 && BN == 256 && KIND != GEMM_FP8 ? 8 : 4;
+  constexpr int NW = (BM == 256 && BN == 256 && KIND != GEMM_FP8) || (BM == 64 && BN == 128 && KIND != GEMM_FP8) ? 8 : 4;
   const int64_t ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   dim3 grid((unsigned)(ntm * ntn)), block(64 * NW);
   if constexpr (KIND == GEMM_INT8) {
