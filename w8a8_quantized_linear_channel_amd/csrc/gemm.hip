@@ -13,9 +13,10 @@
 //                     accumulation, y = S_a[m] S_b[n] acc (+ bias)
 //
 // Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile; each wave
-// owns (BM/2) x (BN/2) built from 32 x 32 MFMA fragments.  The 256 x 256 int8
-// tile uses 8 waves (2 x 4, two per SIMD), each 128 x 64.  K advances 64
-// bytes per stage.  Four LDS buffers hold four stages, filled by
+// owns (BM/2) x (BN/2) built from 32 x 32 MFMA fragments.  The int8 tiles of
+// 256 x 256, 128 x 128 and 64 x 128 use 8 waves (2 x 4, two per SIMD), each
+// (BM/2) x (BN/4).  K advances 64 bytes per stage on 256 x 256 tiles, 128 on
+// the smaller ones.  Four LDS buffers hold four stages, filled by
 // global_load_lds_dwordx4 (global -> LDS without registers) three stages
 // ahead of the MFMAs, so a stage's loads have three stages of compute to
 // arrive.  Fragments are double buffered in registers: the LDS reads of the
@@ -784,10 +785,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(const GemmArgs g0) {
 // decomposition's output is fp16); fp8 bf16.
 template <int BM, int BN, int KIND>
 hipError_t launch_tiles(const GemmArgs& g, int ydt, hipStream_t st) {
-  // 256 x 256 int8 tiles run 8 waves (two per SIMD, 128 x 64 each), so one
-  // wave's stalls on the DMA issue are covered by the other's MFMAs; the fp8
-  // operands are twice as wide and would spill at that register budget
-  constexpr int NW = (BM == 256 && BN == 256 && KIND != GEMM_FP8) || (BM == 64 && BN == 128 && KIND != GEMM_FP8) ? 8 : 4;
+  // The int8 tiles of 256 x 256, 128 x 128 and 64 x 128 run 8 waves (two per
+  // SIMD: 128 x 64, 64 x 32 and 32 x 32 each), so one wave's stalls on the DMA
+  // issue and its fragment reads are covered by the other's MFMAs; the fp8
+  // operands are twice as wide and spill at that register budget on 256 x 256
+  // (on 128 x 128 eight fp8 waves measured no faster)
+  constexpr int NW = KIND != GEMM_FP8 && ((BM == 256 && BN == 256) || (BM == 64 && BN == 128) || (BM == 128 && BN == 128))
+                         ? 8 : 4;
   const int64_t ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   dim3 grid((unsigned)(ntm * ntn)), block(64 * NW);
   if constexpr (KIND == GEMM_INT8) {
