@@ -212,6 +212,22 @@ def test_quantize_act_fp8_scale_ub(ub):
     assert_equal(f32_bits(host(xs)), f32_bits(rs), "scale bits")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("K", [4096, 4112])
+def test_quantize_act_fp8_row_cache_edge(dt, K):
+    # 16-bit rows of up to 4096 values run the two-chunk register cache,
+    # longer ones the eight-chunk one; rows with the bound binding and not
+    log(f"[act fp8] row cache edge K={K} {dt}")
+    x = inputs.random_matrix(23, (7, K), 2.0, torch.float32).numpy().copy()
+    x[2, K - 1] = 3000.0       # the bound binds on this row
+    x[4, :] = 0.0
+    xt = torch.from_numpy(x).to(dt)
+    xq, xs, _ = q8.q8_quantize_act(g(xt), "fp8_e4m3", scale_ub=1200.0)
+    rq, rs = O.quantize_fp8_rowwise(xt, 1200.0)
+    assert_equal(host(xq), rq, "e4m3 codes")
+    assert_equal(f32_bits(host(xs)), f32_bits(rs), "scale bits")
+
+
 def test_quantize_fp8_full_size():
     log("[fp8 quant] 4096x14336 activations and weights, every row")
     wl = inputs.fp8_rowwise()
